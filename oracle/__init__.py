@@ -1,0 +1,12 @@
+"""fp64 CPU oracle of the GPT-2 Pre-LN forward (test infrastructure only).
+
+This package is the checker, not the product.  Only the test suite, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the HIP
+library never calls into it, and nothing here calls the HIP library.
+
+See ``oracle.gpt2`` for the functions and the passages each one follows.
+"""
+from .gpt2 import (  # noqa: F401
+    bf16_round, layer_norm, gelu_new, causal_attention, block_forward,
+    embed, forward_hidden, forward, decode_logits, prepare_params, TRACE_POINTS,
+)

@@ -1,0 +1,233 @@
+"""Plain fp64 reference of the GPT-2 Pre-LN forward pass -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  It shares no code with the HIP path.
+
+Every value is carried in float64.  Matrix products use numpy's ``@`` (a
+library primitive); nothing is blocked, fused or reordered beyond the plain
+definitions below.  Each function names the page passage it follows; the
+pages are cited by title and section:
+
+  [Hidden]  russellluo.com, "从零学大模型：Hidden State 如何流过 GPT-2 Block？"
+  [HFsrc]   pwwt.cn, "逐行拆GPT-2源码：GPT2LMHeadModel到Attention"
+  [Anatomy] bbs.huaweicloud.com blog 476445 (GPT-2 parameter anatomy)
+  [Stack]   nano-ai.tech, "从零手写大模型 · 推理篇 12 - Transformer Stack"
+  [llmc]    dpshk.com news 6064214 (llm.c study notes on attention, LN, MLP)
+
+Readings taken where the pages leave a point open (each also listed in the
+design notes of the repository):
+  * LayerNorm variance is the biased (divide by D) variance, eps = 1e-5 added
+    to the variance inside the square root ([llmc] 3.2; [HFsrc] GPT2Config).
+  * The causal mask removes keys j > i entirely (weight exactly 0); the row
+    maximum is subtracted before exp ([HFsrc] GPT2Attention ``_attn``; [llmc]
+    2.3 and 5.3).
+  * Attention scores are divided by sqrt(head_dim); no per-layer scaling
+    ([HFsrc] GPT2Config, scale_attn_by_inverse_layer_idx = false).
+  * The lm_head is tied to wte and has no bias ([HFsrc] GPT2LMHeadModel).
+  * Dropout is the identity (inference; [Hidden] Pre-Norm section).
+  * "bf16 weights": matrices and wte/wpe are rounded fp32 -> bf16
+    (round-to-nearest-even) once; biases and LayerNorm parameters stay fp32.
+    After that rounding, every operation is fp64 -- the oracle never rounds
+    activations.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TRACE_POINTS = ("attn_norm", "ffn_inp", "ffn_norm", "ffn_out", "l_out")
+
+# --------------------------------------------------------------------------
+# bf16 rounding of the stored weights
+# --------------------------------------------------------------------------
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), returned as float32 values.
+
+    bf16 keeps the upper 16 bits of an IEEE binary32.  Rounding adds half an
+    ulp of the kept part (0x7FFF) plus the kept part's lowest bit (for ties to
+    even), then truncates.  NaNs stay NaN (quiet).
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    r = r.astype(np.uint32)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = (u[nan].astype(np.uint32) | 0x00400000) & 0xFFFF0000
+    return r.view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Building blocks
+# --------------------------------------------------------------------------
+
+
+def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float = 1e-5) -> np.ndarray:
+    """LN(x) = gamma * (x - mu) / sqrt(var + eps) + beta over the last axis.
+
+    [Hidden] section Pre-Norm (the LN formula, eps inside the root);
+    [llmc] 3.2 (two passes: mean, then variance; eps added to the variance).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    mu = x.sum(axis=-1, keepdims=True) / d
+    xc = x - mu
+    var = (xc * xc).sum(axis=-1, keepdims=True) / d
+    return xc / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def gelu_new(x: np.ndarray) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+
+    [HFsrc] section GPT2MLP (NewGELUActivation); [llmc] 4.2 (x^3 as x*x*x).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * (x * x * x))))
+
+
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_offset: int = 0,
+                     return_probs: bool = False):
+    """softmax(q k^T / sqrt(hs), keys j <= i) v, per head.
+
+    q: [H, Tq, hs] at absolute positions q_offset .. q_offset+Tq-1;
+    k, v: [H, Tk, hs] at positions 0 .. Tk-1.
+    [HFsrc] GPT2Attention ``_attn`` (scores, scale by sqrt of the head size,
+    lower-triangular mask sliced to the last Tq rows, softmax, weights @ v);
+    [llmc] 2.2 (scale), 2.3 (mask before softmax), 5.3 (max subtraction).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    H, Tq, hs = q.shape
+    Tk = k.shape[1]
+    i = np.arange(Tq)[:, None] + q_offset
+    j = np.arange(Tk)[None, :]
+    allowed = j <= i                                   # [Tq, Tk]
+    out = np.empty((H, Tq, v.shape[2]), dtype=np.float64)
+    probs = np.empty((H, Tq, Tk), dtype=np.float64) if return_probs else None
+    for h in range(H):
+        s = (q[h] @ k[h].T) / np.sqrt(float(hs))
+        s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.where(allowed, np.exp(s), 0.0)
+        p = e / e.sum(axis=-1, keepdims=True)
+        out[h] = p @ v[h]
+        if return_probs:
+            probs[h] = p
+    return (out, probs) if return_probs else out
+
+
+# --------------------------------------------------------------------------
+# Parameters
+# --------------------------------------------------------------------------
+
+
+def prepare_params(blob: np.ndarray, shape, dtype: str) -> dict:
+    """fp64 views of the parameter blob, keyed as in the safetensors list.
+
+    dtype "bf16": matrices and wte/wpe are first rounded to bf16 (see module
+    notes); "f32": values used as stored.
+    """
+    from workloads import unpack  # layout only (offsets of each key)
+    raw = unpack(np.asarray(blob, np.float32), shape)
+    out = {}
+    for key, arr in raw.items():
+        is_matrix = key in ("wte", "wpe") or key.endswith("c_attn.w") or key.endswith("c_proj.w") \
+            or key.endswith("c_fc.w")
+        a = bf16_round(arr) if (dtype == "bf16" and is_matrix) else arr
+        out[key] = a.astype(np.float64)
+    out["_shape"] = shape
+    return out
+
+
+# --------------------------------------------------------------------------
+# The stack
+# --------------------------------------------------------------------------
+
+
+def embed(P: dict, ids: np.ndarray, pos0: int = 0) -> np.ndarray:
+    """x_t = wte[id_t] + wpe[pos0 + t]  ([HFsrc] GPT2Model; [Stack] GPT.forward)."""
+    ids = np.asarray(ids)
+    T = ids.shape[-1]
+    return P["wte"][ids] + P["wpe"][pos0:pos0 + T]
+
+
+def block_forward(x: np.ndarray, P: dict, l: int, trace: dict | None = None) -> np.ndarray:
+    """One Pre-LN block on one sequence x [T, D].
+
+    H = X + Attn(LN_1(X)),  X' = H + MLP(LN_2(H))
+    [Hidden] section "GPT-2 Block" (the four-line data flow);
+    [HFsrc] GPT2Block.forward (ln_1 -> attn -> residual -> ln_2 -> mlp ->
+    residual), GPT2Attention (fused c_attn, split into thirds q|k|v, heads as
+    consecutive head_dim-wide column blocks, merge heads, c_proj), GPT2MLP
+    (c_fc -> gelu_new -> c_proj).
+    """
+    s = P["_shape"]
+    D, H = s.d_model, s.n_head
+    hs = D // H
+    T = x.shape[0]
+    pre = f"h.{l}."
+    h = layer_norm(x, P[pre + "ln_1.w"], P[pre + "ln_1.b"], s.ln_eps)
+    qkv = h @ P[pre + "attn.c_attn.w"] + P[pre + "attn.c_attn.b"]
+    q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+    split = lambda t: t.reshape(T, H, hs).transpose(1, 0, 2)   # [H, T, hs]
+    a = causal_attention(split(q), split(k), split(v))
+    a = a.transpose(1, 0, 2).reshape(T, D)                      # merge heads in order
+    x_h = x + (a @ P[pre + "attn.c_proj.w"] + P[pre + "attn.c_proj.b"])
+    h2 = layer_norm(x_h, P[pre + "ln_2.w"], P[pre + "ln_2.b"], s.ln_eps)
+    u = gelu_new(h2 @ P[pre + "mlp.c_fc.w"] + P[pre + "mlp.c_fc.b"])
+    m = u @ P[pre + "mlp.c_proj.w"] + P[pre + "mlp.c_proj.b"]
+    x_out = x_h + m
+    if trace is not None:
+        trace.setdefault("attn_norm", []).append(h)
+        trace.setdefault("ffn_inp", []).append(x_h)
+        trace.setdefault("ffn_norm", []).append(h2)
+        trace.setdefault("ffn_out", []).append(m)
+        trace.setdefault("l_out", []).append(x_out)
+    return x_out
+
+
+def forward_hidden(P: dict, ids: np.ndarray, n_layers: int | None = None,
+                   trace: dict | None = None) -> np.ndarray:
+    """ln_f output h_f [T, D] of one sequence ids [T] ([HFsrc] GPT2Model; [Stack])."""
+    s = P["_shape"]
+    x = embed(P, ids)
+    L = s.n_layer if n_layers is None else n_layers
+    for l in range(L):
+        x = block_forward(x, P, l, trace)
+    return layer_norm(x, P["ln_f.w"], P["ln_f.b"], s.ln_eps)
+
+
+def forward(P: dict, ids: np.ndarray, positions=None, trace: dict | None = None) -> np.ndarray:
+    """Logits [B, T, V] (or [B, len(positions), V]) for ids [B, T].
+
+    logits = ln_f(X_L) @ wte^T, the tied head without bias ([HFsrc]
+    GPT2LMHeadModel; [Anatomy] LM head; [Stack] final LayerNorm + head).
+    ``positions`` selects which rows of every sequence get logits (all when
+    None); rows are independent once h_f is known.
+    """
+    ids = np.atleast_2d(np.asarray(ids))
+    outs = []
+    for b in range(ids.shape[0]):
+        hf = forward_hidden(P, ids[b], trace=trace)
+        if positions is not None:
+            hf = hf[np.asarray(positions)]
+        outs.append(hf @ P["wte"].T)
+    return np.stack(outs)
+
+
+def decode_logits(P: dict, prefix: np.ndarray, new_ids: np.ndarray) -> np.ndarray:
+    """Logits [B, V] of one new token per sequence after a cached prefix.
+
+    A KV cache only avoids recomputing the prefix's keys and values; the new
+    token sits at position len(prefix) ([HFsrc] GPT2Model position_ids from
+    past_length; GPT2Attention KV-cache concatenation).  So the result is the
+    last row of the plain forward over prefix ++ [new].
+    """
+    prefix = np.atleast_2d(np.asarray(prefix))
+    new_ids = np.asarray(new_ids).reshape(-1)
+    full = np.concatenate([prefix, new_ids[:, None]], axis=1)
+    T = full.shape[1]
+    return forward(P, full, positions=[T - 1])[:, 0, :]

@@ -1,0 +1,385 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+No GPU.  Each test checks the oracle against something other than itself:
+page values (tests/golden), closed forms, invariants, library routines
+(torch fp64), or brute-force scalar loops on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tiny_shape(n_head=4, d=64, L=2, vocab=512, npos=64, ff=None):
+    return W.ModelShape(vocab=vocab, n_positions=npos, d_model=d, n_head=n_head, n_layer=L,
+                        d_ff=ff or 4 * d)
+
+
+def _random_params(shape, seed, dtype="f32", init=None):
+    init = init or W.Init(w_std=0.2, proj_std=0.2, bias_std=0.1, gamma=(1.0, 0.3), beta=(0.0, 0.3))
+    blob = W.make_params(shape, init, seed)
+    return blob, oracle.prepare_params(blob, shape, dtype)
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+
+def test_layernorm_moments_closed_form():
+    """gamma=1, beta=0: each row has mean 0 and variance var/(var+eps)."""
+    rng = np.random.default_rng(1)
+    x = rng.normal(3.0, 2.0, size=(64, 768)) * rng.uniform(0.001, 10, size=(64, 1))
+    y = oracle.layer_norm(x, np.ones(768), np.zeros(768), 1e-5)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+
+
+def test_layernorm_eps_inside_sqrt():
+    """A constant row has variance 0: output must be beta exactly (eps keeps it finite);
+    a row [a, -a] has |out| = a/sqrt(a^2+eps), which distinguishes sqrt(var+eps) from
+    sqrt(var)+eps."""
+    y = oracle.layer_norm(np.full((1, 8), 5.0), np.ones(8), np.full(8, 0.25), 1e-5)
+    assert np.all(y == 0.25)
+    a = 0.01
+    y = oracle.layer_norm(np.array([[a, -a]]), np.ones(2), np.zeros(2), 1e-5)
+    np.testing.assert_allclose(y[0], [a / math.sqrt(a * a + 1e-5), -a / math.sqrt(a * a + 1e-5)],
+                               rtol=1e-14)
+
+
+def test_layernorm_worked_example_page():
+    g = _golden("ln_worked_example.json")
+    x = np.array([g["input"]])
+    y = oracle.layer_norm(x, np.ones(4), np.zeros(4), 1e-5)[0]
+    assert abs(x.mean() - g["printed_mean"]) < 1e-3
+    np.testing.assert_allclose(y, g["printed_output"], atol=0.06)
+    assert list(np.sign(y)) == list(np.sign(g["printed_output"]))
+
+
+def test_layernorm_vs_torch_fp64():
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(33, 1600)) * 4 + 1
+    gm, bt = rng.normal(1, 0.1, 1600), rng.normal(0, 0.1, 1600)
+    ref = F.layer_norm(torch.from_numpy(x), (1600,), torch.from_numpy(gm), torch.from_numpy(bt), 1e-5)
+    np.testing.assert_allclose(oracle.layer_norm(x, gm, bt), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- GELU
+
+
+def test_gelu_identities_and_torch():
+    x = np.linspace(-8, 8, 4001)
+    y = oracle.gelu_new(x)
+    assert oracle.gelu_new(np.array([0.0]))[0] == 0.0
+    # tanh is odd: gelu(x) - gelu(-x) = x
+    np.testing.assert_allclose(y - oracle.gelu_new(-x), x, atol=1e-14)
+    ref = F.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-15)
+    # and it is the tanh form, not the erf form (they differ by up to ~5e-4)
+    erf = F.gelu(torch.from_numpy(x)).numpy()
+    assert 1e-4 < np.abs(y - erf).max() < 1e-3
+
+
+# ---------------------------------------------------------------- attention
+
+
+def _rand_qkv(rng, H, T, hs, scale=1.0):
+    return [rng.normal(size=(H, T, hs)) * scale for _ in range(3)]
+
+
+def test_softmax_rows_sum_to_one_and_causal_zero_mass():
+    rng = np.random.default_rng(3)
+    q, k, v = _rand_qkv(rng, 3, 37, 16, 3.0)
+    _, p = oracle.causal_attention(q, k, v, return_probs=True)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-13)
+    i, j = np.triu_indices(37, 1)
+    assert np.all(p[:, i, j] == 0.0)
+    assert np.all(p[:, np.arange(37), np.arange(37)] > 0)
+
+
+def test_attention_single_token_returns_v():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand_qkv(rng, 2, 1, 8, 5.0)
+    np.testing.assert_array_equal(oracle.causal_attention(q, k, v), v)
+
+
+def test_attention_zero_query_is_prefix_mean():
+    """q = 0 makes every allowed score equal, so a_i = mean of v_0..v_i."""
+    rng = np.random.default_rng(5)
+    _, k, v = _rand_qkv(rng, 2, 19, 8)
+    q = np.zeros_like(k)
+    a = oracle.causal_attention(q, k, v)
+    expect = np.cumsum(v, axis=1) / np.arange(1, 20)[None, :, None]
+    np.testing.assert_allclose(a, expect, rtol=1e-13, atol=1e-14)
+
+
+def test_attention_scale_is_inverse_sqrt_head_dim():
+    """Two keys with scores 0 and (q.k1)/sqrt(hs): weights follow a logistic in 2a."""
+    hs, a = 4, 0.7
+    q = np.zeros((1, 2, hs)); q[0, 1] = a            # row 1 sees keys 0 and 1
+    k = np.zeros((1, 2, hs)); k[0, 1] = 1.0          # score(1,0) = 0, score(1,1) = 4a/2 = 2a
+    v = np.zeros((1, 2, 1)); v[0, 1, 0] = 1.0
+    out = oracle.causal_attention(q, k, v)
+    w1 = math.exp(2 * a) / (1 + math.exp(2 * a))
+    assert abs(out[0, 1, 0] - w1) < 1e-15
+
+
+def test_attention_vs_torch_sdpa_fp64():
+    rng = np.random.default_rng(6)
+    q, k, v = _rand_qkv(rng, 4, 50, 16, 2.0)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                         torch.from_numpy(v)[None], is_causal=True)[0].numpy()
+    np.testing.assert_allclose(oracle.causal_attention(q, k, v), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_query_offset_matches_suffix():
+    """Queries at positions p.. see keys 0..p+i: equal to the last rows of the full call."""
+    rng = np.random.default_rng(7)
+    q, k, v = _rand_qkv(rng, 2, 12, 8)
+    full = oracle.causal_attention(q, k, v)
+    part = oracle.causal_attention(q[:, 9:], k, v, q_offset=9)
+    np.testing.assert_allclose(part, full[:, 9:], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+
+def test_bf16_round_hand_values_and_torch():
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -20), 3.0e38,
+                     -0.0, 1e-40, np.inf, -np.inf], dtype=np.float32)
+    r = oracle.bf16_round(vals)
+    assert r[0] == 1.0
+    assert r[1] == 1.0                       # tie -> even (mantissa 0)
+    assert r[2] == 1 + 2 ** -6               # tie -> even (mantissa 2)
+    assert r[3] == -(1 + 2 ** -7)            # above the tie -> away
+    assert np.isinf(r[7]) and np.isinf(r[8])
+    rng = np.random.default_rng(8)
+    x = (rng.normal(size=100000) * np.exp(rng.uniform(-30, 30, 100000))).astype(np.float32)
+    x = np.concatenate([x, vals])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(oracle.bf16_round(x), ref)
+
+
+# ---------------------------------------------------------------- parameter layout
+
+
+def test_param_counts_page_table():
+    g = _golden("gpt2_small_param_table.json")
+    s = W.SMALL
+    specs = dict(W.param_specs(s))
+    n = lambda k: int(np.prod(specs[k]))
+    assert n("wte") == g["token_embedding"]
+    assert n("wpe") == g["position_embedding"]
+    attn = sum(n(f"h.{l}.attn.{t}") for l in range(12) for t in ("c_attn.w", "c_attn.b", "c_proj.w", "c_proj.b"))
+    ffn = sum(n(f"h.{l}.mlp.{t}") for l in range(12) for t in ("c_fc.w", "c_fc.b", "c_proj.w", "c_proj.b"))
+    ln = sum(n(f"h.{l}.{t}") for l in range(12) for t in ("ln_1.w", "ln_1.b", "ln_2.w", "ln_2.b")) \
+        + n("ln_f.w") + n("ln_f.b")
+    assert attn == g["attention_12_layers"]
+    assert ffn == g["ffn_12_layers"]
+    assert ln == g["layernorm_and_other"]
+    assert W.param_count(s) == sum(g[k] for k in ("token_embedding", "position_embedding",
+                                                 "attention_12_layers", "ffn_12_layers",
+                                                 "layernorm_and_other"))
+    per = g["per_layer"]
+    assert n("h.0.attn.c_attn.w") == per["qkv"]
+    assert n("h.0.attn.c_proj.w") == per["out_proj"]
+    assert n("h.0.mlp.c_fc.w") == per["ffn_w1"] == n("h.0.mlp.c_proj.w") == per["ffn_w2"]
+    assert n("h.0.mlp.c_fc.b") + n("h.0.mlp.c_proj.b") == per["ffn_biases"]
+    assert sum(1 for k in specs if k.startswith("h.0.")) == g["tensors_per_block"]
+
+
+def test_param_counts_other_shapes():
+    assert W.param_count(W.TINY) == 136960
+    assert W.param_count(W.MEDIUM) == 354823168
+    assert W.param_count(W.XL) == 1557611200
+
+
+# ---------------------------------------------------------------- whole stack
+
+
+def _torch_reference_forward(P, ids):
+    """Independent fp64 forward built from torch.nn.functional library routines."""
+    s = P["_shape"]
+    D, H = s.d_model, s.n_head
+    t = lambda key: torch.from_numpy(P[key])
+    ids_t = torch.from_numpy(np.asarray(ids, np.int64))
+    B, T = ids_t.shape
+    x = F.embedding(ids_t, t("wte")) + t("wpe")[:T]
+    for l in range(s.n_layer):
+        p = lambda k: t(f"h.{l}.{k}")
+        h = F.layer_norm(x, (D,), p("ln_1.w"), p("ln_1.b"), s.ln_eps)
+        qkv = F.linear(h, p("attn.c_attn.w").T, p("attn.c_attn.b"))
+        q, k, v = qkv.split(D, dim=2)
+        heads = lambda z: z.view(B, T, H, D // H).permute(0, 2, 1, 3)
+        a = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True)
+        a = a.permute(0, 2, 1, 3).reshape(B, T, D)
+        x = x + F.linear(a, p("attn.c_proj.w").T, p("attn.c_proj.b"))
+        h = F.layer_norm(x, (D,), p("ln_2.w"), p("ln_2.b"), s.ln_eps)
+        u = F.gelu(F.linear(h, p("mlp.c_fc.w").T, p("mlp.c_fc.b")), approximate="tanh")
+        x = x + F.linear(u, p("mlp.c_proj.w").T, p("mlp.c_proj.b"))
+    x = F.layer_norm(x, (D,), t("ln_f.w"), t("ln_f.b"), s.ln_eps)
+    return F.linear(x, t("wte")).numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_vs_torch_library_fp64(dtype):
+    s = _tiny_shape(n_head=4, d=64, L=3, vocab=97, npos=40)
+    _, P = _random_params(s, 11, dtype)
+    ids = np.random.default_rng(12).integers(0, 97, size=(2, 29))
+    np.testing.assert_allclose(oracle.forward(P, ids), _torch_reference_forward(P, ids),
+                               rtol=1e-11, atol=1e-11)
+
+
+def test_block_identity_when_projections_zero():
+    """Zero attn/mlp c_proj weights and biases: every block returns its input, so
+    logits = LN_f(wte[id] + wpe[t]) @ wte^T."""
+    s = _tiny_shape(L=3)
+    blob, P = _random_params(s, 13)
+    for l in range(s.n_layer):
+        for k in ("attn.c_proj.w", "attn.c_proj.b", "mlp.c_proj.w", "mlp.c_proj.b"):
+            P[f"h.{l}.{k}"] = np.zeros_like(P[f"h.{l}.{k}"])
+    ids = np.random.default_rng(14).integers(0, s.vocab, size=(1, 21))
+    x0 = P["wte"][ids[0]] + P["wpe"][:21]
+    np.testing.assert_array_equal(oracle.block_forward(x0, P, 0), x0)
+    expect = oracle.layer_norm(x0, P["ln_f.w"], P["ln_f.b"]) @ P["wte"].T
+    np.testing.assert_allclose(oracle.forward(P, ids)[0], expect, rtol=1e-13, atol=1e-14)
+
+
+def test_causality_perturbation_bitwise():
+    s = _tiny_shape(L=2)
+    _, P = _random_params(s, 15)
+    ids = np.random.default_rng(16).integers(0, s.vocab, size=(1, 24))
+    base = oracle.forward(P, ids)
+    for t in (0, 7, 22):
+        ids2 = ids.copy()
+        ids2[0, t + 1] = (ids2[0, t + 1] + 1 + t) % s.vocab
+        out = oracle.forward(P, ids2)
+        np.testing.assert_array_equal(out[0, :t + 1], base[0, :t + 1])
+        assert not np.array_equal(out[0, t + 1], base[0, t + 1])
+
+
+def test_batch_independence_permutation():
+    s = _tiny_shape(L=2)
+    _, P = _random_params(s, 17)
+    ids = np.random.default_rng(18).integers(0, s.vocab, size=(4, 10))
+    base = oracle.forward(P, ids)
+    perm = [2, 0, 3, 1]
+    np.testing.assert_array_equal(oracle.forward(P, ids[perm]), base[perm])
+
+
+def test_decode_uses_next_position():
+    """The new token's embedding uses position len(prefix): with zero projections
+    the decode logits reduce to LN_f(wte[new] + wpe[P]) @ wte^T."""
+    s = _tiny_shape(L=1)
+    _, P = _random_params(s, 19)
+    for k in ("attn.c_proj.w", "attn.c_proj.b", "mlp.c_proj.w", "mlp.c_proj.b"):
+        P[f"h.0.{k}"] = np.zeros_like(P[f"h.0.{k}"])
+    prefix = np.random.default_rng(20).integers(0, s.vocab, size=(2, 9))
+    new = np.array([3, 5])
+    got = oracle.decode_logits(P, prefix, new)
+    x = P["wte"][new] + P["wpe"][9]
+    np.testing.assert_allclose(got, oracle.layer_norm(x, P["ln_f.w"], P["ln_f.b"]) @ P["wte"].T,
+                               rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------- brute force: d=4, T=3, 2 layers
+
+
+def _bf_layernorm(v, g, b, eps):
+    n = len(v)
+    mu = sum(v) / n
+    var = sum((vi - mu) ** 2 for vi in v) / n
+    return [(v[i] - mu) / math.sqrt(var + eps) * g[i] + b[i] for i in range(n)]
+
+
+def _bf_matvec(v, Wm, bias):
+    """y_j = sum_i v_i W[i][j] + b_j (W stored [in][out])."""
+    return [sum(v[i] * Wm[i][j] for i in range(len(v))) + bias[j] for j in range(len(bias))]
+
+
+def _bf_forward(P, ids):
+    """Scalar-loop forward, written independently of the oracle's array code."""
+    s = P["_shape"]
+    D, H, L = s.d_model, s.n_head, s.n_layer
+    hs = D // H
+    T = len(ids)
+    L_ = lambda a: a.tolist()
+    X = [[P["wte"][ids[t]][d] + P["wpe"][t][d] for d in range(D)] for t in range(T)]
+    for l in range(L):
+        g = lambda k: L_(P[f"h.{l}.{k}"])
+        hn = [_bf_layernorm(X[t], g("ln_1.w"), g("ln_1.b"), s.ln_eps) for t in range(T)]
+        qkv = [_bf_matvec(hn[t], g("attn.c_attn.w"), g("attn.c_attn.b")) for t in range(T)]
+        att = [[0.0] * D for _ in range(T)]
+        for h in range(H):
+            for i in range(T):
+                qi = qkv[i][h * hs:(h + 1) * hs]
+                sc = []
+                for j in range(i + 1):
+                    kj = qkv[j][D + h * hs:D + (h + 1) * hs]
+                    sc.append(sum(qi[c] * kj[c] for c in range(hs)) / math.sqrt(hs))
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = sum(e)
+                for c in range(hs):
+                    att[i][h * hs + c] = sum(e[j] / z * qkv[j][2 * D + h * hs + c] for j in range(i + 1))
+        proj = [_bf_matvec(att[t], g("attn.c_proj.w"), g("attn.c_proj.b")) for t in range(T)]
+        Hs = [[X[t][d] + proj[t][d] for d in range(D)] for t in range(T)]
+        h2 = [_bf_layernorm(Hs[t], g("ln_2.w"), g("ln_2.b"), s.ln_eps) for t in range(T)]
+        fc = [_bf_matvec(h2[t], g("mlp.c_fc.w"), g("mlp.c_fc.b")) for t in range(T)]
+        u = [[0.5 * x * (1 + math.tanh(math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3))) for x in r]
+             for r in fc]
+        mo = [_bf_matvec(u[t], g("mlp.c_proj.w"), g("mlp.c_proj.b")) for t in range(T)]
+        X = [[Hs[t][d] + mo[t][d] for d in range(D)] for t in range(T)]
+    hf = [_bf_layernorm(X[t], L_(P["ln_f.w"]), L_(P["ln_f.b"]), s.ln_eps) for t in range(T)]
+    wte = L_(P["wte"])
+    return [[sum(hf[t][d] * wte[v][d] for d in range(D)) for v in range(s.vocab)] for t in range(T)]
+
+
+@pytest.mark.parametrize("n_head", [1, 2])
+def test_brute_force_d4_t3_two_layers(n_head):
+    """The hand-walk toy of the Transformer Stack page: d_model 4, 3 tokens, 2 layers."""
+    s = W.ModelShape(vocab=8, n_positions=3, d_model=4, n_head=n_head, n_layer=2, d_ff=16)
+    _, P = _random_params(s, 21 + n_head)
+    ids = np.array([5, 1, 7])
+    got = oracle.forward(P, ids[None])[0]
+    ref = np.array(_bf_forward(P, ids))
+    assert got.shape == (3, 8)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_brute_force_dyadic_hand_values():
+    """A d=4 row [1,-1,1,-1] has mean 0 and variance 1: LN gives +-1/sqrt(1+eps)."""
+    y = oracle.layer_norm(np.array([[1.0, -1.0, 1.0, -1.0]]), np.ones(4), np.zeros(4), 1e-5)[0]
+    c = 1 / math.sqrt(1 + 1e-5)
+    np.testing.assert_allclose(y, [c, -c, c, -c], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- page shapes
+
+
+def test_page_shapes_small_model():
+    g = _golden("shapes.json")
+    s = W.ModelShape(vocab=50257, n_positions=1024, d_model=768, n_head=12, n_layer=12, d_ff=3072)
+    w = W.WORKLOADS["gpt2-small-b8t1024"]
+    blob = W.make_params(w)
+    P = oracle.prepare_params(blob, s, "bf16")
+    ids3 = np.array([[464, 3797, 25365]])
+    assert list(oracle.forward(P, ids3).shape) == g["forward_logits"]["shape"]
+    trace = {}
+    oracle.forward_hidden(P, np.array([2437, 389]), trace=trace)
+    for name in oracle.TRACE_POINTS:
+        assert len(trace[name]) == 12
+        assert all(list(t.shape) == g["hidden_trace"]["shape"] for t in trace[name])
