@@ -1,0 +1,416 @@
+// Causal attention on gfx950 (see attention.h for what is computed).
+//
+// Prefill kernel (flash-style):
+//   * one block = 4 waves = 128 queries of one (b, h); blocks of the longest
+//     query tiles are launched first (causal work grows with the tile index).
+//   * key tiles of 64 keys are staged in LDS (K as [key][d], V transposed as
+//     [d][key]) through a double-buffered ring; the next tile's global loads
+//     are in flight while the current one is on the matrix cores.
+//   * each wave computes S^T = K Q^T with MFMA (lane l ends with 4 keys of one
+//     query), keeps a running max and sum per query (online softmax, fp32,
+//     the running max subtracted before exp as the llm.c notes advise), then
+//     O^T += V^T P^T with MFMA.  Everything per query stays in the lane that
+//     holds that query, so rescaling needs no cross-lane traffic.
+//   * key tiles that lie entirely after a wave's last query are skipped; only
+//     tiles that straddle the diagonal evaluate the mask.
+//   * keys past the last valid position are clamped on load (K) or zeroed in
+//     LDS (V), so uninitialised cache rows never reach the arithmetic.
+#include "attention.h"
+
+namespace gpt2 {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int CH>
+__device__ __forceinline__ int swz_ch(int row, int c) {
+  return c ^ (row & ((CH < 8 ? CH : 8) - 1));
+}
+
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__ q,
+                                                            const T* __restrict__ k,
+                                                            const T* __restrict__ vt,
+                                                            T* __restrict__ out, int BH, int H,
+                                                            int Tq, int kvT, int n_qtiles) {
+  constexpr int QW = 32, NW = 4, BQ = QW * NW, BKEYS = 64;
+  constexpr int ESZ = (int)sizeof(T);
+  constexpr int KROWB = HS * ESZ, KCH = KROWB / 16;     // K tile rows (keys)
+  constexpr int VROWB = BKEYS * ESZ, VCH = VROWB / 16;  // V^T tile rows (d)
+  constexpr int NSLAB = KROWB / 64;
+  constexpr int KF = BKEYS / 16, DF = HS / 16, QF = QW / 16;
+  constexpr int KPS = Mma<T>::kPerSlab;      // keys per PV matrix step
+  constexpr int KFPS = KPS / 16;             // key fragments per PV step (2 bf16, 1 fp32)
+  constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
+  constexpr int K_CHUNKS = BKEYS * KCH, V_CHUNKS = HS * VCH;
+  constexpr int LK = (K_CHUNKS + 255) / 256, LV = (V_CHUNKS + 255) / 256;
+  static_assert(NSLAB >= 1 && KROWB % 64 == 0, "head_dim bytes must be a multiple of 64");
+
+  __shared__ u32x4_t sK[2][K_CHUNKS];
+  __shared__ u32x4_t sV[2][V_CHUNKS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int bh = blockIdx.x % BH;
+  const int qt = n_qtiles - 1 - blockIdx.x / BH;
+  const int b = bh / H, h = bh - b * H;
+  const int D = H * HS;
+
+  const int q_blk = qt * BQ;
+  const int q0w = q_blk + wave * QW;
+  const int q_end = min(q_blk + BQ, Tq);        // exclusive, block's last query + 1
+  const int n_kt = (q_end + BKEYS - 1) / BKEYS;  // key tiles this block needs
+  const int nkeys = Tq;                           // valid key positions
+
+  const T* qb = q + (size_t)bh * Tq * HS;
+  const T* kb = k + (size_t)bh * kvT * HS;
+  const T* vb = vt + (size_t)bh * HS * kvT;
+
+  // Query fragments stay in registers: lane (lr, lg) holds query q0w+qf*16+lr,
+  // bytes slab*64 + lg*16 .. +16 of its row.
+  u32x4_t qfrag[QF][NSLAB];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    int row = min(q0w + qf * 16 + lr, Tq - 1);
+    const char* p = reinterpret_cast<const char*>(qb + (size_t)row * HS);
+#pragma unroll
+    for (int s = 0; s < NSLAB; ++s) qfrag[qf][s] = *reinterpret_cast<const u32x4_t*>(p + s * 64 + lg * 16);
+  }
+
+  u32x4_t rk[LK], rv[LV];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      int idx = tid + i * 256;
+      if (idx < K_CHUNKS) {
+        int row = idx / KCH, c = idx % KCH;
+        int key = min(kt * BKEYS + row, nkeys - 1);
+        rk[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(kb + (size_t)key * HS) + c * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      int idx = tid + i * 256;
+      if (idx < V_CHUNKS) {
+        int d = idx / VCH, c = idx % VCH;
+        int key0 = kt * BKEYS + c * EPC;
+        const T* src = vb + (size_t)d * kvT + key0;
+        if (key0 + EPC <= nkeys) {
+          rv[i] = *reinterpret_cast<const u32x4_t*>(src);
+        } else {
+          // partial chunk at the end of the sequence: zero the invalid keys
+          u32x4_t w = {0u, 0u, 0u, 0u};
+          if (key0 < nkeys) {
+            const u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(src);
+            const int valid_bytes = (nkeys - key0) * ESZ;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              int lo = j * 4;
+              if (lo + 4 <= valid_bytes) w[j] = t4[j];
+              else if (lo < valid_bytes) w[j] = t4[j] & 0xFFFFu;  // only bf16 can split a word
+            }
+          }
+          rv[i] = w;
+        }
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      int idx = tid + i * 256;
+      if (idx < K_CHUNKS) {
+        int row = idx / KCH, c = idx % KCH;
+        sK[buf][row * KCH + swz_ch<KCH>(row, c)] = rk[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      int idx = tid + i * 256;
+      if (idx < V_CHUNKS) {
+        int d = idx / VCH, c = idx % VCH;
+        sV[buf][d * VCH + swz_ch<VCH>(d, c)] = rv[i];
+      }
+    }
+  };
+
+  f32x4_t o[DF][QF];
+  float m_run[QF], l_run[QF];
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    m_run[qf] = -INFINITY;
+    l_run[qf] = 0.f;
+#pragma unroll
+    for (int df = 0; df < DF; ++df) o[df][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if (kt + 1 < n_kt) gload(kt + 1);
+    const int buf = kt & 1;
+    const int key0 = kt * BKEYS;
+    if (key0 <= q0w + QW - 1) {  // wave-uniform: otherwise the whole tile is masked for this wave
+      f32x4_t s[KF][QF];
+#pragma unroll
+      for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+        for (int qf = 0; qf < QF; ++qf) s[kf][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < NSLAB; ++sl) {
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf) {
+          int row = kf * 16 + lr;
+          u32x4_t kfr = sK[buf][row * KCH + swz_ch<KCH>(row, sl * 4 + lg)];
+#pragma unroll
+          for (int qf = 0; qf < QF; ++qf) Mma<T>::run(s[kf][qf], kfr, qfrag[qf][sl]);
+        }
+      }
+      // lane holds S^T[key = key0 + kf*16 + 4*lg + e][query = q0w + qf*16 + lr]
+      const bool diag = key0 + BKEYS - 1 > q0w;
+#pragma unroll
+      for (int qf = 0; qf < QF; ++qf) {
+        const int qi = q0w + qf * 16 + lr;
+        if (diag) {
+#pragma unroll
+          for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (key0 + kf * 16 + 4 * lg + e > qi) s[kf][qf][e] = -INFINITY;
+        }
+        float mx = s[0][qf][0];
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kf][qf][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[qf], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[qf] - m_new) * kLog2e);
+        m_run[qf] = m_new;
+        const float mb = m_new * kLog2e;
+        float ls = 0.f;
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float p = __builtin_amdgcn_exp2f(s[kf][qf][e] * kLog2e - mb);
+            s[kf][qf][e] = p;
+            ls += p;
+          }
+        l_run[qf] = l_run[qf] * alpha + ls;
+#pragma unroll
+        for (int df = 0; df < DF; ++df) {
+          o[df][qf][0] *= alpha;
+          o[df][qf][1] *= alpha;
+          o[df][qf][2] *= alpha;
+          o[df][qf][3] *= alpha;
+        }
+      }
+      // O^T += V^T P^T, KPS keys per matrix step
+#pragma unroll
+      for (int st = 0; st < BKEYS / KPS; ++st) {
+        u32x4_t pf[QF];
+#pragma unroll
+        for (int qf = 0; qf < QF; ++qf) {
+          if constexpr (ESZ == 2) {
+            const f32x4_t& p0 = s[st * 2][qf];
+            const f32x4_t& p1 = s[st * 2 + 1][qf];
+            pf[qf] = u32x4_t{pack2_bf16(p0[0], p0[1]), pack2_bf16(p0[2], p0[3]), pack2_bf16(p1[0], p1[1]),
+                             pack2_bf16(p1[2], p1[3])};
+          } else {
+            const f32x4_t& p0 = s[st][qf];
+            pf[qf] = __builtin_bit_cast(u32x4_t, p0);
+          }
+        }
+#pragma unroll
+        for (int df = 0; df < DF; ++df) {
+          const int d = df * 16 + lr;
+          u32x4_t vf;
+          if constexpr (ESZ == 2) {
+            // keys st*32 + 4*lg + 0..3 and st*32 + 16 + 4*lg + 0..3 (8 bytes each)
+            const int c0 = st * 4 + (lg >> 1), c1 = c0 + 2, half = lg & 1;
+            const u32x2_t* row = reinterpret_cast<const u32x2_t*>(&sV[buf][d * VCH]);
+            const u32x2_t a0 = row[swz_ch<VCH>(d, c0) * 2 + half];
+            const u32x2_t a1 = row[swz_ch<VCH>(d, c1) * 2 + half];
+            vf = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+          } else {
+            // keys st*16 + 4*lg + 0..3 (16 bytes)
+            vf = sV[buf][d * VCH + swz_ch<VCH>(d, st * 4 + lg)];
+          }
+#pragma unroll
+          for (int qf = 0; qf < QF; ++qf) Mma<T>::run(o[df][qf], vf, pf[qf]);
+        }
+      }
+      (void)KFPS;
+    }
+    if (kt + 1 < n_kt) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // Normalise and merge heads: lane holds O^T[d = df*16 + 4*lg + e][query = q0w + qf*16 + lr]
+#pragma unroll
+  for (int qf = 0; qf < QF; ++qf) {
+    float l = l_run[qf];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int qi = q0w + qf * 16 + lr;
+    if (qi < Tq) {
+      T* dst = out + ((size_t)b * Tq + qi) * D + h * HS;
+#pragma unroll
+      for (int df = 0; df < DF; ++df)
+        Elem<T>::store4(dst + df * 16 + 4 * lg, o[df][qf][0] * inv, o[df][qf][1] * inv, o[df][qf][2] * inv,
+                        o[df][qf][3] * inv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode
+
+constexpr int kDecKeys = 256;  // keys per split block
+
+// One block per (bh, split): scores for up to 256 keys, block softmax,
+// partial output o[d] = sum_j p_j v_j with its (max, sum).
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q,
+                                                                 const T* __restrict__ k,
+                                                                 const T* __restrict__ vt,
+                                                                 float* __restrict__ part, int n_keys,
+                                                                 int kvT, int nsplit) {
+  __shared__ float sq[HS];
+  __shared__ float sp[kDecKeys];
+  __shared__ float sred[8];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+  const int j0 = split * kDecKeys;
+  const int nj = min(kDecKeys, n_keys - j0);
+  if (tid < HS) sq[tid] = Elem<T>::to_f32(q[(size_t)bh * HS + tid]);
+  __syncthreads();
+
+  // scores: one key per thread
+  float s = -INFINITY;
+  if (tid < nj) {
+    const T* kr = k + ((size_t)bh * kvT + j0 + tid) * HS;
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < HS; d += 4) {
+      float4 kv4 = Elem<T>::load4(kr + d);
+      acc += sq[d] * kv4.x + sq[d + 1] * kv4.y + sq[d + 2] * kv4.z + sq[d + 3] * kv4.w;
+    }
+    s = acc;
+  }
+  float mx = wave_max(s);
+  if ((tid & 63) == 0) sred[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+  const float p = tid < nj ? __builtin_amdgcn_exp2f((s - mx) * kLog2e) : 0.f;
+  sp[tid] = p;
+  float ls = wave_sum(p);
+  __syncthreads();
+  if ((tid & 63) == 0) sred[4 + (tid >> 6)] = ls;
+  __syncthreads();
+  ls = sred[4] + sred[5] + sred[6] + sred[7];
+
+  // o[d] = sum_j p_j V^T[d][j0 + j]: 4 threads per d, each a quarter of the keys
+  constexpr int TPD = 256 / HS;           // threads per d
+  constexpr int KPT = kDecKeys / TPD;     // keys per thread
+  const int d = tid / TPD, part_i = tid % TPD;
+  const T* vr = vt + ((size_t)bh * HS + d) * kvT + j0 + part_i * KPT;
+  float acc = 0.f;
+  const int jbeg = part_i * KPT;
+#pragma unroll 4
+  for (int j = 0; j < KPT; j += 4) {
+    if (jbeg + j < nj) {
+      float4 v4 = Elem<T>::load4(vr + j);
+      // keys past nj have p == 0; their cache entries may be unwritten: guard each
+      float v[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (jbeg + j + e < nj) acc += sp[jbeg + j + e] * v[e];
+    }
+  }
+#pragma unroll
+  for (int o = TPD / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  float* dst = part + ((size_t)bh * nsplit + split) * (HS + 2);
+  if (part_i == 0) dst[d] = acc;
+  if (tid == 0) {
+    dst[HS] = mx;
+    dst[HS + 1] = ls;
+  }
+}
+
+// Merge the splits of one (b, h): out = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s.
+template <typename T, int HS>
+__global__ __launch_bounds__(64) void attn_decode_merge_kernel(const float* __restrict__ part,
+                                                                T* __restrict__ out, int H,
+                                                                int nsplit) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* pb = part + (size_t)bh * nsplit * (HS + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pb[s * (HS + 2) + HS]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = __builtin_amdgcn_exp2f((pb[s * (HS + 2) + HS] - M) * kLog2e);
+    den += w * pb[s * (HS + 2) + HS + 1];
+    if (d < HS) num += w * pb[s * (HS + 2) + d];
+  }
+  const int b = bh / H, h = bh - b * H;
+  if (d < HS) out[(size_t)b * H * HS + h * HS + d] = Elem<T>::from_f32(num / den);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out, int B, int H, int Tq,
+                                    int kvT, int hs, hipStream_t stream) {
+  const int n_qtiles = (Tq + 127) / 128;
+  dim3 grid(B * H * n_qtiles), block(256);
+  if (hs == 64) {
+    hipLaunchKernelGGL((attn_prefill_kernel<T, 64>), grid, block, 0, stream, q, k, vt, out, B * H, H, Tq, kvT,
+                       n_qtiles);
+  } else if (hs == 16 && sizeof(T) == 4) {
+    hipLaunchKernelGGL((attn_prefill_kernel<T, (sizeof(T) == 4 ? 16 : 64)>), grid, block, 0, stream, q, k,
+                       vt, out, B * H, H, Tq, kvT, n_qtiles);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t decode_partials_floats(int B, int H, int hs) {
+  const int max_split = (4096 + kDecKeys - 1) / kDecKeys;
+  return (size_t)B * H * max_split * (hs + 2);
+}
+
+template <typename T>
+hipError_t launch_attention_decode(const T* q, const T* k, const T* vt, T* out, float* part, int B, int H,
+                                   int n_keys, int kvT, int hs, hipStream_t stream) {
+  const int nsplit = (n_keys + kDecKeys - 1) / kDecKeys;
+  if (hs == 64) {
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, 64>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
+                       part, n_keys, kvT, nsplit);
+    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 64>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
+  } else if (hs == 16) {
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, 16>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
+                       part, n_keys, kvT, nsplit);
+    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 16>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_attention_prefill<float>(const float*, const float*, const float*, float*, int, int,
+                                                    int, int, int, hipStream_t);
+template hipError_t launch_attention_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*, int,
+                                                     int, int, int, int, hipStream_t);
+template hipError_t launch_attention_decode<float>(const float*, const float*, const float*, float*, float*, int,
+                                                   int, int, int, int, hipStream_t);
+template hipError_t launch_attention_decode<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*,
+                                                    float*, int, int, int, int, int, hipStream_t);
+
+}  // namespace gpt2

@@ -1,0 +1,125 @@
+// Shared device-side helpers of the gfx950 kernels: element types, bf16
+// conversion, 16-byte fragments and the MFMA wrappers used by the GEMM and
+// attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt2 {
+
+// bf16 is stored as raw 16-bit patterns; arithmetic is always fp32.
+struct bf16_t {
+  uint16_t bits;
+};
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+// 16-byte fragment as a native clang vector (element access compiles to plain
+// register moves; HIP's uint4 is a union wrapper and is not used for fragments).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+// Round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two floats -> packed pair of bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element traits: loading/storing groups of 4 elements as fp32.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float to_f32(float v) { return v; }
+  __device__ static __forceinline__ float from_f32(float v) { return v; }
+  __device__ static __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+  __device__ static __forceinline__ float4 load4(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+};
+
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v.bits); }
+  __device__ static __forceinline__ bf16_t from_f32(float v) { return bf16_t{f32_to_bf16(v)}; }
+  __device__ static __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack2_bf16(a, b), pack2_bf16(c, d)};
+  }
+  __device__ static __forceinline__ float4 load4(const bf16_t* p) {
+    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p);
+    return make_float4(bf16_to_f32(u[0] & 0xFFFF), bf16_to_f32(u[0] >> 16), bf16_to_f32(u[1] & 0xFFFF),
+                       bf16_to_f32(u[1] >> 16));
+  }
+};
+
+// Matrix-core step on one 16-byte fragment per lane.
+//
+// Fragment convention (both operands): lane l owns matrix row (l % 16) and a
+// 16-byte run along k that starts at byte 16*(l / 16) of a 64-byte k-slab.
+// Both operands use the same (lane group, element) -> k assignment, so the
+// k-sum is complete whatever order the hardware pairs the elements in.
+//   bf16: one v_mfma_f32_16x16x32_bf16 covers the 32 k of a slab.
+//   f32:  four v_mfma_f32_16x16x4_f32 cover its 16 k (element j of every lane
+//         in step j).
+// Result (16x16, fp32): lane l holds rows 4*(l/16)+0..3 of column l%16 of
+// A_rows x B_rows^T, where A_rows is the matrix whose rows the first operand
+// supplies.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  static constexpr int kPerSlab = 32;
+  __device__ static __forceinline__ void run(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int kPerSlab = 16;
+  __device__ static __forceinline__ void run(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    const f32x4_t fa = __builtin_bit_cast(f32x4_t, a);
+    const f32x4_t fb = __builtin_bit_cast(f32x4_t, b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[0], fb[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[1], fb[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[2], fb[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[3], fb[3], acc, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_via_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// gelu_new(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
+// tanh(y) = 1 - 2 / (exp(2y) + 1), which saturates to +-1 without NaN.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float y = k0 * (x + 0.044715f * (x * x * x));
+  float e = exp_via_exp2(2.0f * y);
+  float t = 1.0f - 2.0f / (e + 1.0f);
+  return 0.5f * x * (1.0f + t);
+}
+
+}  // namespace gpt2

@@ -1,0 +1,125 @@
+// Matrix-core GEMM with fused epilogues for the projections of the GPT-2 block
+// and the tied lm_head:  C[m, n] = sum_k A[m, k] * B[n, k]   (both K-contiguous)
+//
+//   c_attn  (pwwt.cn "逐行拆GPT-2源码", GPT2Attention: one fused projection to
+//            3*d_model, split into thirds q|k|v, heads = consecutive head_dim
+//            column blocks)                        -> EpiQKV (bias, head scatter)
+//   c_proj  (GPT2Attention c_proj, then the first residual of GPT2Block.forward)
+//                                                   -> EpiResidual (bias, x += .)
+//   c_fc    (GPT2MLP c_fc followed by gelu_new)     -> EpiGelu
+//   mlp.c_proj (GPT2MLP c_proj, second residual)    -> EpiResidual
+//   lm_head (GPT2LMHeadModel: tied to wte, no bias) -> EpiLogits
+//
+// Design (gfx950):
+//   * block tile BM x BN, k staged 128 bytes per step (64 bf16 / 32 fp32)
+//     through a double-buffered LDS ring, one barrier per k step; global loads
+//     of step k+1 are in flight while step k runs on the matrix cores.
+//   * WGM x WGN waves; each wave owns a (BM/WGM) x (BN/WGN) sub-tile built from
+//     16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16, or 16x16x4_f32 for fp32).
+//   * operands are swapped in the MFMA (B rows first) so that every lane ends
+//     with 4 consecutive output columns of one row: epilogue stores are
+//     8- or 16-byte vectors.
+//   * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r lives at
+//     slot c ^ (r & 7) so the 16 rows read by a lane group fall in distinct
+//     bank groups.
+//   * blocks are remapped so that each XCD (blockIdx % 8 on MI355X) walks a
+//     contiguous range of tiles, grouped GROUP_M tile-rows at a time, which
+//     keeps the A row-panels and B column-panels in that XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace gpt2 {
+
+template <typename T>
+struct EpiQKV {
+  const float* bias;  // [3D]
+  T* q;               // [B][H][Tq][hs], scaled by q_scale
+  T* k;               // [B][H][kvT][hs], rows t0 + t
+  T* vt;              // [B][H][hs][kvT], columns t0 + t
+  int Tq;             // tokens per sequence in this call (rows m = b*Tq + t)
+  int t0;             // absolute position of row t = 0 (past length)
+  int kvT;            // allocated positions per sequence in k / vt
+  int H, hs, D;
+  float q_scale;
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
+    float4 b = *reinterpret_cast<const float4*>(bias + n);
+    float v0 = acc[0] + b.x, v1 = acc[1] + b.y, v2 = acc[2] + b.z, v3 = acc[3] + b.w;
+    int which = n / D;
+    int hd = n - which * D;
+    int head = hd / hs;
+    int d = hd - head * hs;
+    int bb = m / Tq;
+    int t = m - bb * Tq;
+    size_t bh = (size_t)bb * H + head;
+    if (which == 0) {
+      Elem<T>::store4(q + (bh * Tq + t) * hs + d, v0 * q_scale, v1 * q_scale, v2 * q_scale, v3 * q_scale);
+    } else if (which == 1) {
+      Elem<T>::store4(k + (bh * kvT + t0 + t) * hs + d, v0, v1, v2, v3);
+    } else {
+      T* p = vt + (bh * hs + d) * kvT + t0 + t;
+      p[0] = Elem<T>::from_f32(v0);
+      p[kvT] = Elem<T>::from_f32(v1);
+      p[2 * (size_t)kvT] = Elem<T>::from_f32(v2);
+      p[3 * (size_t)kvT] = Elem<T>::from_f32(v3);
+    }
+  }
+};
+
+struct EpiResidual {
+  const float* bias;  // [N]
+  float* x;           // [M][ldx] fp32 residual stream, updated in place
+  int ldx;
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
+    float4 b = *reinterpret_cast<const float4*>(bias + n);
+    float4* p = reinterpret_cast<float4*>(x + (size_t)m * ldx + n);
+    float4 r = *p;
+    r.x += acc[0] + b.x;
+    r.y += acc[1] + b.y;
+    r.z += acc[2] + b.z;
+    r.w += acc[3] + b.w;
+    *p = r;
+  }
+};
+
+template <typename T>
+struct EpiGelu {
+  const float* bias;  // [N]
+  T* u;               // [M][ldu]
+  int ldu;
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
+    float4 b = *reinterpret_cast<const float4*>(bias + n);
+    Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(acc[0] + b.x), gelu_tanh(acc[1] + b.y),
+                    gelu_tanh(acc[2] + b.z), gelu_tanh(acc[3] + b.w));
+  }
+};
+
+struct EpiLogits {
+  float* out;   // [M][ldo], only columns n < n_valid are written
+  int ldo;
+  int n_valid;
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
+    float* p = out + (size_t)m * ldo + n;
+    if (n + 3 < n_valid) {
+      p[0] = acc[0];
+      p[1] = acc[1];
+      p[2] = acc[2];
+      p[3] = acc[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < n_valid) p[e] = acc[e];
+    }
+  }
+};
+
+// Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),
+// K % (128 / sizeof(T)) == 0, N % 4 == 0.  `tile` picks the tile shape
+// (see gemm.hip); returns hipSuccess or the launch error.
+enum GemmTile { kTile128x128 = 0, kTile256x128 = 1, kTile64x64 = 2, kTile32x64 = 3 };
+
+template <typename T, class Epi>
+hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,
+                       const Epi& epi, hipStream_t stream);
+
+}  // namespace gpt2

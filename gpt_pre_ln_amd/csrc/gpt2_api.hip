@@ -1,0 +1,529 @@
+// C ABI of the GPT-2 Pre-LN forward library (declarations and contract in
+// include/gpt2.h).  Host side only: argument checks, the device layouts of
+// parameters / workspace / KV cache, and the launch sequence of one forward or
+// decode step.  Every step of the computation runs in the kernels of
+// rowops.hip, gemm.hip and attention.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "attention.h"
+#include "gemm.h"
+#include "rowops.h"
+
+using namespace gpt2;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+inline int round_up_int(int v, int a) { return (v + a - 1) / a * a; }
+
+gpt2_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return GPT2_ERR_HIP;
+}
+
+#define GPT2_HIP(call, what)                   \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// ------------------------------------------------------------------ config
+
+gpt2_status check_config(const gpt2_config* c) {
+  if (!c) return GPT2_ERR_INVALID_ARG;
+  if (c->vocab_size < 1 || c->n_positions < 1 || c->d_model < 1 || c->n_head < 1 || c->n_layer < 1 ||
+      c->d_ff < 1)
+    return GPT2_ERR_SHAPE;
+  if (c->dtype != GPT2_F32 && c->dtype != GPT2_BF16) return GPT2_ERR_UNSUPPORTED;
+  if (!(c->ln_eps >= 0.f) || !std::isfinite(c->ln_eps)) return GPT2_ERR_INVALID_ARG;
+  if (c->d_model % c->n_head != 0) return GPT2_ERR_SHAPE;
+  const int hs = c->d_model / c->n_head;
+  if (!(hs == 64 || (hs == 16 && c->dtype == GPT2_F32))) return GPT2_ERR_UNSUPPORTED;
+  if (c->d_model % 64 != 0 || c->d_ff % 64 != 0) return GPT2_ERR_UNSUPPORTED;
+  if (c->d_model > 2048) return GPT2_ERR_UNSUPPORTED;
+  if (c->n_positions > 4096) return GPT2_ERR_UNSUPPORTED;
+  if (c->vocab_size > (1 << 24)) return GPT2_ERR_UNSUPPORTED;
+  return GPT2_OK;
+}
+
+inline size_t esize(const gpt2_config& c) { return c.dtype == GPT2_BF16 ? 2 : 4; }
+inline int vocab_pad(const gpt2_config& c) { return round_up_int(c.vocab_size, 256); }
+inline int kv_stride(int max_T) { return round_up_int(max_T, 64); }
+
+struct LayerOff {
+  size_t ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_fc, b_fc, w_pr, b_pr;
+};
+
+struct ParamLayout {
+  size_t wte = 0, wpe = 0, lnf_g = 0, lnf_b = 0, total = 0;
+  std::vector<LayerOff> layers;
+};
+
+ParamLayout param_layout(const gpt2_config& c) {
+  ParamLayout L;
+  const size_t es = esize(c), D = c.d_model, F = c.d_ff;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.wte = take((size_t)vocab_pad(c) * D * es);
+  L.wpe = take((size_t)c.n_positions * D * es);
+  for (int l = 0; l < c.n_layer; ++l) {
+    LayerOff o;
+    o.ln1_g = take(D * 4);
+    o.ln1_b = take(D * 4);
+    o.w_qkv = take(3 * D * D * es);
+    o.b_qkv = take(3 * D * 4);
+    o.w_o = take(D * D * es);
+    o.b_o = take(D * 4);
+    o.ln2_g = take(D * 4);
+    o.ln2_b = take(D * 4);
+    o.w_fc = take(F * D * es);
+    o.b_fc = take(F * 4);
+    o.w_pr = take(D * F * es);
+    o.b_pr = take(D * 4);
+    L.layers.push_back(o);
+  }
+  L.lnf_g = take(D * 4);
+  L.lnf_b = take(D * 4);
+  L.total = off;
+  return L;
+}
+
+size_t blob_floats(const gpt2_config& c) {
+  const size_t V = c.vocab_size, P = c.n_positions, D = c.d_model, F = c.d_ff;
+  const size_t per_layer = 2 * D + (3 * D * D + 3 * D) + (D * D + D) + 2 * D + (D * F + F) + (F * D + D);
+  return V * D + P * D + per_layer * c.n_layer + 2 * D;
+}
+
+struct WsLayout {
+  size_t x, h, q, k, vt, a, u, part, total;
+};
+
+WsLayout ws_layout(const gpt2_config& c, int B, int T) {
+  WsLayout W;
+  const size_t es = esize(c), D = c.d_model, F = c.d_ff, M = (size_t)B * T;
+  const size_t Tp = kv_stride(T);
+  const int hs = c.d_model / c.n_head;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  W.x = take(M * D * 4);
+  W.h = take(M * D * es);
+  W.q = take(M * D * es);
+  W.k = take((size_t)B * Tp * D * es);
+  W.vt = take((size_t)B * Tp * D * es);
+  W.a = take(M * D * es);
+  W.u = take(M * F * es);
+  W.part = take(decode_partials_floats(B, c.n_head, hs) * 4);
+  W.total = off;
+  return W;
+}
+
+size_t kv_layer_bytes(const gpt2_config& c, int B, int max_T) {
+  return 2 * (size_t)B * kv_stride(max_T) * c.d_model * esize(c);
+}
+
+// ------------------------------------------------------------------ timing
+
+enum KernelClass { kEmbed = 0, kLN = 1, kQKV = 2, kAttn = 3, kOProj = 4, kFC = 5, kMLPProj = 6, kLMHead = 7 };
+constexpr int kMaxTimed = 4096;
+
+}  // namespace
+
+struct gpt2_model {
+  gpt2_config cfg;
+  char* params;
+  size_t param_bytes;
+  char* ws;
+  size_t ws_bytes;
+  ParamLayout lay;
+  float* trace = nullptr;
+  size_t trace_floats = 0;
+  bool timing_on = false;
+  int timing_class = -1;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  int n_timed = 0;
+  bool timing_overflow = false;
+};
+
+namespace {
+
+struct TimedScope {
+  gpt2_model* m;
+  hipStream_t s;
+  bool active;
+  TimedScope(gpt2_model* m_, int cls, hipStream_t s_) : m(m_), s(s_), active(false) {
+    if (m->timing_on && m->timing_class == cls) {
+      if (m->n_timed < kMaxTimed) {
+        active = true;
+        hipEventRecord(m->ev[2 * m->n_timed], s);
+      } else {
+        m->timing_overflow = true;
+      }
+    }
+  }
+  ~TimedScope() {
+    if (active) {
+      hipEventRecord(m->ev[2 * m->n_timed + 1], s);
+      ++m->n_timed;
+    }
+  }
+};
+
+template <typename T>
+const T* pp(const gpt2_model* m, size_t off) {
+  return reinterpret_cast<const T*>(m->params + off);
+}
+const float* pf(const gpt2_model* m, size_t off) { return reinterpret_cast<const float*>(m->params + off); }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+GemmTile pick_tile(int M, int N) {
+  if (M <= 32) return kTile32x64;
+  if (M <= 64) return kTile64x64;
+  (void)N;
+  return kTile128x128;
+}
+
+// ------------------------------------------------------------------ forward
+
+template <typename T>
+gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, float* logits, float* hidden,
+                        gpt2_kv_view* kv, hipStream_t st) {
+  const gpt2_config& c = m->cfg;
+  const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
+  const int M = B * T_seq;
+  const WsLayout W = ws_layout(c, B, T_seq);
+  float* x = reinterpret_cast<float*>(m->ws + W.x);
+  T* h = reinterpret_cast<T*>(m->ws + W.h);
+  T* q = reinterpret_cast<T*>(m->ws + W.q);
+  T* a = reinterpret_cast<T*>(m->ws + W.a);
+  T* u = reinterpret_cast<T*>(m->ws + W.u);
+  const int kvT = kv ? kv_stride(kv->max_T) : kv_stride(T_seq);
+  const float q_scale = 1.0f / std::sqrt((float)hs);
+
+  {
+    TimedScope ts(m, kEmbed, st);
+    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, st), "embed");
+  }
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& o = m->lay.layers[l];
+    T* kl;
+    T* vtl;
+    if (kv) {
+      char* base = reinterpret_cast<char*>(kv->d_kv) + (size_t)l * kv_layer_bytes(c, kv->B, kv->max_T);
+      kl = reinterpret_cast<T*>(base);
+      vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, kv->B, kv->max_T) / 2);
+    } else {
+      kl = reinterpret_cast<T*>(m->ws + W.k);
+      vtl = reinterpret_cast<T*>(m->ws + W.vt);
+    }
+    {
+      TimedScope ts(m, kLN, st);
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
+    }
+    {
+      TimedScope ts(m, kQKV, st);
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, T_seq, 0, kvT, H, hs, D, q_scale};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D), h, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "c_attn");
+    }
+    {
+      TimedScope ts(m, kAttn, st);
+      GPT2_HIP(launch_attention_prefill<T>(q, kl, vtl, a, B, H, T_seq, kvT, hs, st), "attention");
+    }
+    {
+      TimedScope ts(m, kOProj, st);
+      EpiResidual e{pf(m, o.b_o), x, D};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, D), a, pp<T>(m, o.w_o), M, D, D, D, D, e, st), "attn.c_proj");
+    }
+    {
+      TimedScope ts(m, kLN, st);
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st), "ln_2");
+    }
+    {
+      TimedScope ts(m, kFC, st);
+      EpiGelu<T> e{pf(m, o.b_fc), u, F};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, F), h, pp<T>(m, o.w_fc), M, F, D, D, D, e, st), "c_fc");
+    }
+    {
+      TimedScope ts(m, kMLPProj, st);
+      EpiResidual e{pf(m, o.b_pr), x, D};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, D), u, pp<T>(m, o.w_pr), M, D, F, F, F, e, st), "mlp.c_proj");
+    }
+    if (m->trace && (size_t)(l + 1) * M * D <= m->trace_floats) {
+      GPT2_HIP(hipMemcpyAsync(m->trace + (size_t)l * M * D, x, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st),
+               "trace copy");
+    }
+  }
+  {
+    TimedScope ts(m, kLN, st);
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, hidden, M, D, c.ln_eps, st), "ln_f");
+  }
+  if (logits) {
+    TimedScope ts(m, kLMHead, st);
+    EpiLogits e{logits, V, V};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
+             "lm_head");
+  }
+  if (kv) kv->past_len = T_seq;
+  return GPT2_OK;
+}
+
+template <typename T>
+gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, float* logits, hipStream_t st) {
+  const gpt2_config& c = m->cfg;
+  const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
+  const int B = kv->B, M = B, pos = kv->past_len;
+  const WsLayout W = ws_layout(c, B, 1);
+  float* x = reinterpret_cast<float*>(m->ws + W.x);
+  T* h = reinterpret_cast<T*>(m->ws + W.h);
+  T* q = reinterpret_cast<T*>(m->ws + W.q);
+  T* a = reinterpret_cast<T*>(m->ws + W.a);
+  T* u = reinterpret_cast<T*>(m->ws + W.u);
+  float* part = reinterpret_cast<float*>(m->ws + W.part);
+  const int kvT = kv_stride(kv->max_T);
+  const float q_scale = 1.0f / std::sqrt((float)hs);
+
+  GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, st), "embed");
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& o = m->lay.layers[l];
+    char* base = reinterpret_cast<char*>(kv->d_kv) + (size_t)l * kv_layer_bytes(c, B, kv->max_T);
+    T* kl = reinterpret_cast<T*>(base);
+    T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
+    {
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, 1, pos, kvT, H, hs, D, q_scale};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D), h, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "c_attn");
+    }
+    GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
+    {
+      EpiResidual e{pf(m, o.b_o), x, D};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, D), a, pp<T>(m, o.w_o), M, D, D, D, D, e, st), "attn.c_proj");
+    }
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st), "ln_2");
+    {
+      EpiGelu<T> e{pf(m, o.b_fc), u, F};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, F), h, pp<T>(m, o.w_fc), M, F, D, D, D, e, st), "c_fc");
+    }
+    {
+      EpiResidual e{pf(m, o.b_pr), x, D};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, D), u, pp<T>(m, o.w_pr), M, D, F, F, F, e, st), "mlp.c_proj");
+    }
+  }
+  GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st), "ln_f");
+  {
+    EpiLogits e{logits, V, V};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
+             "lm_head");
+  }
+  kv->past_len = pos + 1;
+  return GPT2_OK;
+}
+
+template <typename T>
+gpt2_status run_init(gpt2_model* m, const float* blob, hipStream_t st) {
+  const gpt2_config& c = m->cfg;
+  const size_t V = c.vocab_size, P = c.n_positions, D = c.d_model, F = c.d_ff;
+  size_t src = 0;  // float offset into the blob
+  auto mat = [&](size_t dst_off, size_t K, size_t N) -> gpt2_status {  // blob [K][N] -> device [N][K]
+    GPT2_HIP(launch_transpose_convert<T>(blob + src, reinterpret_cast<T*>(m->params + dst_off), (int)K, (int)N,
+                                         (int)N, st),
+             "init transpose");
+    src += K * N;
+    return GPT2_OK;
+  };
+  auto vec = [&](size_t dst_off, size_t n) -> gpt2_status {
+    GPT2_HIP(hipMemcpyAsync(m->params + dst_off, blob + src, n * 4, hipMemcpyDeviceToDevice, st), "init copy");
+    src += n;
+    return GPT2_OK;
+  };
+  gpt2_status s;
+  GPT2_HIP(launch_convert<T>(blob + src, reinterpret_cast<T*>(m->params + m->lay.wte), V * D,
+                             (size_t)vocab_pad(c) * D, st),
+           "init wte");
+  src += V * D;
+  GPT2_HIP(launch_convert<T>(blob + src, reinterpret_cast<T*>(m->params + m->lay.wpe), P * D, P * D, st),
+           "init wpe");
+  src += P * D;
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& o = m->lay.layers[l];
+    if ((s = vec(o.ln1_g, D)) || (s = vec(o.ln1_b, D)) || (s = mat(o.w_qkv, D, 3 * D)) || (s = vec(o.b_qkv, 3 * D)) ||
+        (s = mat(o.w_o, D, D)) || (s = vec(o.b_o, D)) || (s = vec(o.ln2_g, D)) || (s = vec(o.ln2_b, D)) ||
+        (s = mat(o.w_fc, D, F)) || (s = vec(o.b_fc, F)) || (s = mat(o.w_pr, F, D)) || (s = vec(o.b_pr, D)))
+      return s;
+  }
+  if ((s = vec(m->lay.lnf_g, D)) || (s = vec(m->lay.lnf_b, D))) return s;
+  return GPT2_OK;
+}
+
+}  // namespace
+
+// ======================================================================= C ABI
+
+extern "C" {
+
+const char* gpt2_status_string(gpt2_status s) {
+  switch (s) {
+    case GPT2_OK: return "ok";
+    case GPT2_ERR_INVALID_ARG: return "invalid argument";
+    case GPT2_ERR_SHAPE: return "shape out of range";
+    case GPT2_ERR_CAPACITY: return "kv cache capacity exceeded";
+    case GPT2_ERR_WORKSPACE: return "workspace or parameter region too small";
+    case GPT2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GPT2_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gpt2_last_error(void) { return g_last_error.c_str(); }
+
+gpt2_status gpt2_param_blob_floats(const gpt2_config* cfg, size_t* n) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!n) return GPT2_ERR_INVALID_ARG;
+  *n = blob_floats(*cfg);
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_param_bytes(const gpt2_config* cfg, size_t* bytes) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return GPT2_ERR_INVALID_ARG;
+  *bytes = param_layout(*cfg).total;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, int32_t B, int32_t T, size_t* bytes) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || T > cfg->n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
+  *bytes = ws_layout(*cfg, B, T).total;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_kv_cache_bytes(const gpt2_config* cfg, int32_t B, int32_t max_T, size_t* bytes) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || max_T < 1 || max_T > cfg->n_positions) return GPT2_ERR_SHAPE;
+  *bytes = (size_t)cfg->n_layer * kv_layer_bytes(*cfg, B, max_T);
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_create(const gpt2_config* cfg, void* d_params, size_t param_bytes, void* d_workspace,
+                        size_t ws_bytes, gpt2_model** out) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!out || !d_params || !d_workspace) return GPT2_ERR_INVALID_ARG;
+  if (!aligned(d_params, kAlign) || !aligned(d_workspace, kAlign)) return GPT2_ERR_INVALID_ARG;
+  ParamLayout lay = param_layout(*cfg);
+  if (param_bytes < lay.total) return GPT2_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(*cfg, 1, 1).total) return GPT2_ERR_WORKSPACE;
+  gpt2_model* m = new gpt2_model();
+  m->cfg = *cfg;
+  m->params = static_cast<char*>(d_params);
+  m->param_bytes = param_bytes;
+  m->ws = static_cast<char*>(d_workspace);
+  m->ws_bytes = ws_bytes;
+  m->lay = std::move(lay);
+  *out = m;
+  return GPT2_OK;
+}
+
+void gpt2_destroy(gpt2_model* m) {
+  if (!m) return;
+  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  delete m;
+}
+
+gpt2_status gpt2_init_params(gpt2_model* m, const float* d_blob, size_t n, void* stream) {
+  if (!m || !d_blob) return GPT2_ERR_INVALID_ARG;
+  if (!aligned(d_blob, 4)) return GPT2_ERR_INVALID_ARG;
+  if (n != blob_floats(m->cfg)) return GPT2_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return m->cfg.dtype == GPT2_BF16 ? run_init<bf16_t>(m, d_blob, st) : run_init<float>(m, d_blob, st);
+}
+
+gpt2_status gpt2_forward(gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits, float* hidden,
+                         gpt2_kv_view* kv, void* stream) {
+  if (!m || !tokens) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || T > m->cfg.n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
+  if (!aligned(tokens, 4) || (logits && !aligned(logits, 4)) || (hidden && !aligned(hidden, 16)))
+    return GPT2_ERR_INVALID_ARG;
+  if (ws_layout(m->cfg, B, T).total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
+  if (kv) {
+    if (!kv->d_kv || !aligned(kv->d_kv, kAlign)) return GPT2_ERR_INVALID_ARG;
+    if (kv->B != B) return GPT2_ERR_SHAPE;
+    if (kv->max_T < T || kv->max_T > m->cfg.n_positions) return GPT2_ERR_CAPACITY;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return m->cfg.dtype == GPT2_BF16 ? run_forward<bf16_t>(m, tokens, B, T, logits, hidden, kv, st)
+                                   : run_forward<float>(m, tokens, B, T, logits, hidden, kv, st);
+}
+
+gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, float* logits, void* stream) {
+  if (!m || !kv || !tokens || !logits || !kv->d_kv) return GPT2_ERR_INVALID_ARG;
+  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(logits, 4)) return GPT2_ERR_INVALID_ARG;
+  if (kv->B < 1 || kv->max_T < 1 || kv->max_T > m->cfg.n_positions) return GPT2_ERR_SHAPE;
+  if (kv->past_len < 0) return GPT2_ERR_SHAPE;
+  if (kv->past_len >= kv->max_T) return GPT2_ERR_CAPACITY;
+  if (ws_layout(m->cfg, kv->B, 1).total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, tokens, logits, st)
+                                   : run_decode<float>(m, kv, tokens, logits, st);
+}
+
+gpt2_status gpt2_set_trace(gpt2_model* m, float* d_trace, size_t n) {
+  if (!m) return GPT2_ERR_INVALID_ARG;
+  if (d_trace && !aligned(d_trace, 4)) return GPT2_ERR_INVALID_ARG;
+  m->trace = d_trace;
+  m->trace_floats = d_trace ? n : 0;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_timing_enable(gpt2_model* m, int32_t which, int32_t on) {
+  if (!m || which < 0 || which > kLMHead) return GPT2_ERR_INVALID_ARG;
+  if (on && m->ev.empty()) {
+    m->ev.resize(2 * kMaxTimed);
+    for (auto& e : m->ev) GPT2_HIP(hipEventCreate(&e), "hipEventCreate");
+  }
+  m->timing_on = on != 0;
+  m->timing_class = which;
+  m->n_timed = 0;
+  m->timing_overflow = false;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_timing_read(gpt2_model* m, double* total_ms, int32_t* launches) {
+  if (!m || !total_ms || !launches) return GPT2_ERR_INVALID_ARG;
+  double tot = 0.0;
+  for (int i = 0; i < m->n_timed; ++i) {
+    GPT2_HIP(hipEventSynchronize(m->ev[2 * i + 1]), "hipEventSynchronize");
+    float ms = 0.f;
+    GPT2_HIP(hipEventElapsedTime(&ms, m->ev[2 * i], m->ev[2 * i + 1]), "hipEventElapsedTime");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = m->n_timed;
+  m->n_timed = 0;
+  m->timing_overflow = false;
+  return GPT2_OK;
+}
+
+}  // extern "C"

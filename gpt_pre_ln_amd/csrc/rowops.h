@@ -1,0 +1,31 @@
+// Row-wise HBM-bound kernels: token + position embedding, LayerNorm, and the
+// one-time parameter conversion.
+#pragma once
+
+#include "common.h"
+
+namespace gpt2 {
+
+// x[m, :] = wte[ids[m], :] + wpe[pos0 + m % T, :] (fp32 out).
+// pwwt.cn "逐行拆GPT-2源码", GPT2Model (wte + wpe, positions from past_length).
+template <typename T>
+hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq,
+                        int pos0, int D, hipStream_t stream);
+
+// y[m, :] = gamma * (x - mean) / sqrt(var + eps) + beta over D (biased
+// variance, two passes over the row held in registers); optional fp32 copy.
+// russellluo.com "Hidden State 如何流过 GPT-2 Block", Pre-Norm; dpshk.com 3.2.
+template <typename T>
+hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32,
+                            int M, int D, float eps, hipStream_t stream);
+
+// dst[n][k] = convert(src[k][n]) for a [K][N] fp32 source (Conv1D [in, out]
+// -> [out, in]); dst rows N..N_pad-1 are zero-filled.
+template <typename T>
+hipError_t launch_transpose_convert(const float* src, T* dst, int K, int N, int N_pad, hipStream_t stream);
+
+// dst[i] = convert(src[i]) for i < n; dst[n .. n_pad) = 0.
+template <typename T>
+hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipStream_t stream);
+
+}  // namespace gpt2

@@ -1,0 +1,147 @@
+// Row-wise kernels (see rowops.h).  One wavefront per row: D <= 2048 floats
+// fit in registers (at most 8 float4 per lane), the row statistics are two
+// wavefront reductions (mean, then the centred sum of squares) with no LDS.
+#include "rowops.h"
+
+namespace gpt2 {
+
+namespace {
+
+constexpr int kMaxV4 = 8;  // float4 per lane -> D <= 2048
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ wte,
+                                                     const T* __restrict__ wpe, float* __restrict__ x, int M,
+                                                     int T_seq, int pos0, int D) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int id = ids[row];
+  const int pos = pos0 + row % T_seq;
+  const T* we = wte + (size_t)id * D;
+  const T* pe = wpe + (size_t)pos * D;
+  float* xr = x + (size_t)row * D;
+  for (int c = lane * 4; c < D; c += 256) {
+    float4 a = Elem<T>::load4(we + c);
+    float4 b = Elem<T>::load4(pe + c);
+    *reinterpret_cast<float4*>(xr + c) = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                         const float* __restrict__ beta, T* __restrict__ y,
+                                                         float* __restrict__ y32, int M, int D, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const float* xr = x + (size_t)row * D;
+  float4 v[kMaxV4];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxV4; ++i) {
+    const int c = lane * 4 + i * 256;
+    if (c < D) {
+      v[i] = *reinterpret_cast<const float4*>(xr + c);
+      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float mean = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxV4; ++i) {
+    const int c = lane * 4 + i * 256;
+    if (c < D) {
+      v[i].x -= mean;
+      v[i].y -= mean;
+      v[i].z -= mean;
+      v[i].w -= mean;
+      sq += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
+    }
+  }
+  const float var = wave_sum(sq) / (float)D;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int i = 0; i < kMaxV4; ++i) {
+    const int c = lane * 4 + i * 256;
+    if (c < D) {
+      const float4 g = *reinterpret_cast<const float4*>(gamma + c);
+      const float4 b = *reinterpret_cast<const float4*>(beta + c);
+      const float o0 = v[i].x * rstd * g.x + b.x, o1 = v[i].y * rstd * g.y + b.y;
+      const float o2 = v[i].z * rstd * g.z + b.z, o3 = v[i].w * rstd * g.w + b.w;
+      Elem<T>::store4(y + (size_t)row * D + c, o0, o1, o2, o3);
+      if (y32) *reinterpret_cast<float4*>(y32 + (size_t)row * D + c) = make_float4(o0, o1, o2, o3);
+    }
+  }
+}
+
+// 32x32 tile transpose through LDS; 256 threads = 32 x 8.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_convert_kernel(const float* __restrict__ src, T* __restrict__ dst,
+                                                                 int K, int N, int N_pad) {
+  __shared__ float tile[32][33];
+  const int n0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) {
+    const int kk = k0 + r, nn = n0 + tx;
+    tile[r][tx] = (kk < K && nn < N) ? src[(size_t)kk * N + nn] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int nn = n0 + r, kk = k0 + tx;
+    if (nn < N_pad && kk < K) dst[(size_t)nn * K + kk] = Elem<T>::from_f32(tile[tx][r]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ src, T* __restrict__ dst, size_t n,
+                                                       size_t n_pad) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_pad; i += (size_t)gridDim.x * 256)
+    dst[i] = Elem<T>::from_f32(i < n ? src[i] : 0.f);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq, int pos0, int D,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(embed_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32, int M, int D,
+                            float eps, hipStream_t stream) {
+  if (D > 256 * kMaxV4 || D % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(layernorm_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, x, gamma, beta, y, y32, M, D,
+                     eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_transpose_convert(const float* src, T* dst, int K, int N, int N_pad, hipStream_t stream) {
+  dim3 grid((N_pad + 31) / 32, (K + 31) / 32);
+  hipLaunchKernelGGL(transpose_convert_kernel<T>, grid, dim3(256), 0, stream, src, dst, K, N, N_pad);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipStream_t stream) {
+  size_t blocks = (n_pad + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, n, n_pad);
+  return hipGetLastError();
+}
+
+#define GPT2_ROWOPS(T)                                                                                          \
+  template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, hipStream_t); \
+  template hipError_t launch_layernorm<T>(const float*, const float*, const float*, T*, float*, int, int, float,    \
+                                          hipStream_t);                                                             \
+  template hipError_t launch_transpose_convert<T>(const float*, T*, int, int, int, hipStream_t);                   \
+  template hipError_t launch_convert<T>(const float*, T*, size_t, size_t, hipStream_t);
+
+GPT2_ROWOPS(float)
+GPT2_ROWOPS(bf16_t)
+
+}  // namespace gpt2

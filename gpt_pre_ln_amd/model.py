@@ -1,0 +1,98 @@
+"""Device-buffer owner around the C ABI.
+
+PyTorch allocates the parameter region, workspace, KV caches and outputs and
+supplies the stream; every computation is a call into libgpt2.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class KVCache:
+    """A key/value cache in a torch-owned device buffer plus its C view."""
+
+    def __init__(self, cfg, batch: int, max_T: int, device):
+        nbytes = B.gpt2_kv_cache_bytes(cfg, batch, max_T)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.view = B.gpt2_kv_view(self.buf.data_ptr(), batch, max_T, 0)
+
+    @property
+    def past_len(self) -> int:
+        return self.view.past_len
+
+
+class GPT2:
+    def __init__(self, vocab_size, n_positions, d_model, n_head, n_layer, d_ff, dtype="bf16",
+                 max_batch=1, max_seq=None, ln_eps=1e-5, device="cuda:0"):
+        self.device = torch.device(device)
+        self.cfg = B.make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dtype)
+        self.dtype = dtype
+        max_seq = max_seq or n_positions
+        self.param_bytes = B.gpt2_param_bytes(self.cfg)
+        self.ws_bytes = max(B.gpt2_workspace_bytes(self.cfg, max_batch, max_seq),
+                            B.gpt2_workspace_bytes(self.cfg, max_batch, 1))
+        self.params = torch.empty(self.param_bytes, dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.handle = B.gpt2_create(self.cfg, self.params.data_ptr(), self.param_bytes,
+                                    self.ws.data_ptr(), self.ws_bytes)
+
+    @classmethod
+    def from_shape(cls, shape, dtype, **kw):
+        return cls(shape.vocab, shape.n_positions, shape.d_model, shape.n_head, shape.n_layer,
+                   shape.d_ff, dtype=dtype, ln_eps=shape.ln_eps, **kw)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None:
+            B.gpt2_destroy(h)
+            self.handle = None
+
+    @property
+    def stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def load_blob(self, blob) -> None:
+        """Convert an fp32 parameter blob (numpy or torch) into the device layout."""
+        n = B.gpt2_param_blob_floats(self.cfg)
+        if isinstance(blob, np.ndarray):
+            d_blob = torch.from_numpy(np.ascontiguousarray(blob, dtype=np.float32)).to(self.device)
+        else:
+            d_blob = blob.to(self.device, torch.float32).contiguous()
+        if d_blob.numel() != n:
+            raise ValueError(f"blob has {d_blob.numel()} floats, the config needs {n}")
+        B.gpt2_init_params(self.handle, d_blob.data_ptr(), n, self.stream)
+        torch.cuda.current_stream(self.device).synchronize()
+        del d_blob
+
+    def forward(self, ids: torch.Tensor, logits: bool = True, hidden: bool = False, kv: KVCache | None = None,
+                out_logits: torch.Tensor | None = None):
+        """ids: int32 [B, T] on the device. Returns (logits [B,T,V] fp32 | None, hidden [B,T,D] | None)."""
+        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.device == self.device
+        Bsz, T = ids.shape
+        lg = None
+        if logits:
+            lg = out_logits if out_logits is not None else torch.empty(
+                (Bsz, T, self.cfg.vocab_size), dtype=torch.float32, device=self.device)
+        hd = torch.empty((Bsz, T, self.cfg.d_model), dtype=torch.float32, device=self.device) if hidden else None
+        B.gpt2_forward(self.handle, ids.data_ptr(), Bsz, T, lg.data_ptr() if lg is not None else None,
+                       hd.data_ptr() if hd is not None else None, kv.view if kv is not None else None,
+                       self.stream)
+        return lg, hd
+
+    def new_kv_cache(self, batch: int, max_T: int) -> KVCache:
+        return KVCache(self.cfg, batch, max_T, self.device)
+
+    def decode_step(self, kv: KVCache, new_ids: torch.Tensor, out_logits: torch.Tensor | None = None):
+        """new_ids: int32 [B] on the device. Returns logits [B, V] fp32."""
+        assert new_ids.dtype == torch.int32 and new_ids.is_contiguous()
+        lg = out_logits if out_logits is not None else torch.empty(
+            (kv.view.B, self.cfg.vocab_size), dtype=torch.float32, device=self.device)
+        B.gpt2_decode_step(self.handle, kv.view, new_ids.data_ptr(), lg.data_ptr(), self.stream)
+        return lg
+
+    def set_trace(self, trace: torch.Tensor | None):
+        B.gpt2_set_trace(self.handle, trace.data_ptr() if trace is not None else None,
+                         trace.numel() if trace is not None else 0)

@@ -1,0 +1,159 @@
+/*
+ * gpt2.h -- C ABI of the MI355X (gfx950) GPT-2 Pre-LN forward library.
+ *
+ * What the library computes (pages cited by title and section):
+ *   x_0   = wte[id_t] + wpe[t]                       (pwwt.cn "逐行拆GPT-2源码", GPT2Model)
+ *   H_l   = X_l + CausalMHA(LN_1(X_l))               (russellluo.com "Hidden State 如何流过
+ *   X_l+1 = H_l + MLP(LN_2(H_l))                      GPT-2 Block", section GPT-2 Block)
+ *   logits = LN_f(X_L) @ wte^T   (tied, no bias)     (pwwt.cn, GPT2LMHeadModel)
+ * with LN(x) = gamma*(x-mu)/sqrt(var+eps)+beta (biased variance), attention
+ * softmax(q k^T / sqrt(head_dim)) over keys j <= i, MLP = c_proj(gelu_new(c_fc(x)))
+ * with gelu_new the tanh approximation (pwwt.cn, GPT2Attention and GPT2MLP).
+ * Incremental decode with a key/value cache places the new token at position
+ * past_len (pwwt.cn, GPT2Model position_ids and the KV-cache lines of
+ * GPT2Attention).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer named d_* is DEVICE memory owned by the caller; the library
+ *     never allocates or frees device memory and keeps only the pointers it is
+ *     given at gpt2_create.  The gpt2_model handle owns host memory only.
+ *   - Every call that launches work is asynchronous on `stream` (a hipStream_t,
+ *     NULL = the default stream) and never synchronises.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - All argument checks happen on the host before anything is launched; on
+ *     any error nothing is launched and nothing is written.
+ *   - One handle must not be used concurrently from two streams: the forward
+ *     and decode calls share its workspace.
+ *   - Token ids must lie in [0, vocab_size); this precondition is not checked
+ *     on the device.
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT2_OK = 0,
+  GPT2_ERR_INVALID_ARG = 1, /* null pointer, bad alignment, non-positive size */
+  GPT2_ERR_SHAPE = 2,       /* T outside [1, n_positions], B < 1, blob size mismatch, ... */
+  GPT2_ERR_CAPACITY = 3,    /* KV cache full or too small for the request */
+  GPT2_ERR_WORKSPACE = 4,   /* workspace / parameter region smaller than required */
+  GPT2_ERR_UNSUPPORTED = 5, /* configuration the kernels do not cover (see gpt2_config) */
+  GPT2_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} gpt2_status;
+
+typedef enum { GPT2_F32 = 0, GPT2_BF16 = 1 } gpt2_dtype;
+
+/* Model hyper-parameters, the GPT2Config fields of pwwt.cn section GPT2Config.
+ * Supported: d_model % 64 == 0, d_model % n_head == 0, head_dim = d_model/n_head
+ * in {16, 32, 64} (16 and 32 with GPT2_F32 only), d_ff % 64 == 0,
+ * n_positions <= 4096.
+ * dtype GPT2_F32: every kernel computes and stores in fp32.
+ * dtype GPT2_BF16: matrices, wte and wpe are held in bf16 (round to nearest
+ * even from the fp32 blob), biases and LayerNorm parameters in fp32; matrix
+ * products take bf16 operands with fp32 accumulation; the residual stream,
+ * LayerNorm statistics, softmax and GELU are fp32; logits are fp32. */
+typedef struct {
+  int32_t vocab_size;
+  int32_t n_positions;
+  int32_t d_model;
+  int32_t n_head;
+  int32_t n_layer;
+  int32_t d_ff;
+  float ln_eps;
+  int32_t dtype; /* gpt2_dtype */
+} gpt2_config;
+
+typedef struct gpt2_model gpt2_model;
+
+/* A key/value cache in caller-owned device memory (gpt2_kv_cache_bytes bytes).
+ * Layout per layer l: K as [B][n_head][max_T][head_dim] and V transposed as
+ * [B][n_head][head_dim][max_T], element type as the model dtype.  past_len
+ * counts the cached positions; gpt2_forward with a view sets it to T and
+ * gpt2_decode_step increments it. */
+typedef struct {
+  void* d_kv;
+  int32_t B;
+  int32_t max_T;
+  int32_t past_len;
+} gpt2_kv_view;
+
+/* Number of floats in the host parameter blob: wte[V,D], wpe[P,D], per layer
+ * ln_1.{w,b}, attn.c_attn.{w[D,3D],b}, attn.c_proj.{w[D,D],b}, ln_2.{w,b},
+ * mlp.c_fc.{w[D,F],b}, mlp.c_proj.{w[F,D],b}, then ln_f.{w,b} -- the order of
+ * the safetensors key list (pwwt.cn, section on weights and architecture),
+ * matrices [in, out] as Conv1D stores them. */
+gpt2_status gpt2_param_blob_floats(const gpt2_config* cfg, size_t* n_floats);
+
+/* Bytes of the device parameter region (converted layout, see gpt2_init_params). */
+gpt2_status gpt2_param_bytes(const gpt2_config* cfg, size_t* bytes);
+
+/* Bytes of device workspace needed for gpt2_forward at batch B, length T, and
+ * for gpt2_decode_step at batch B (T = 1). */
+gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, int32_t B, int32_t T, size_t* bytes);
+
+/* Bytes of a KV cache for B sequences of up to max_T positions (max_T <= n_positions). */
+gpt2_status gpt2_kv_cache_bytes(const gpt2_config* cfg, int32_t B, int32_t max_T, size_t* bytes);
+
+/* Create a handle.  d_params: gpt2_param_bytes bytes; d_workspace: ws_bytes
+ * bytes (the largest forward the handle will run decides the size).  Both must
+ * be 256-byte aligned and stay valid until gpt2_destroy.  No HIP call is made. */
+gpt2_status gpt2_create(const gpt2_config* cfg, void* d_params, size_t param_bytes,
+                        void* d_workspace, size_t ws_bytes, gpt2_model** out);
+
+void gpt2_destroy(gpt2_model* model);
+
+/* Convert the fp32 parameter blob (DEVICE memory, n_floats floats in the
+ * gpt2_param_blob_floats order) into the device parameter region: matrices are
+ * transposed to [out, in] and, for GPT2_BF16, rounded to bf16 (nearest even);
+ * wte is zero-padded to a multiple of 256 rows.  The blob is only read and may
+ * be freed once the stream has passed this call. */
+gpt2_status gpt2_init_params(gpt2_model* model, const float* d_blob, size_t n_floats, void* stream);
+
+/* Full forward of B sequences of T tokens (1 <= T <= n_positions).
+ *   d_tokens: int32 [B, T] token ids.
+ *   d_logits: fp32 [B, T, vocab_size] or NULL (skip the lm_head).
+ *   d_hidden: fp32 [B, T, d_model] output of the final LayerNorm, or NULL.
+ *   kv:       NULL, or a cache view with kv->B == B and kv->max_T >= T: keys and
+ *             values of positions [0, T) are written into it and kv->past_len
+ *             is set to T (prefill).
+ * The workspace must hold gpt2_workspace_bytes(cfg, B, T). */
+gpt2_status gpt2_forward(gpt2_model* model, const int32_t* d_tokens, int32_t B, int32_t T,
+                         float* d_logits, float* d_hidden, gpt2_kv_view* kv, void* stream);
+
+/* One decode step: one new token per sequence at position kv->past_len.
+ *   d_new_tokens: int32 [kv->B]; d_logits: fp32 [kv->B, vocab_size].
+ * Requires kv->past_len < kv->max_T (else GPT2_ERR_CAPACITY).  Appends the new
+ * keys/values to the cache and increments kv->past_len (host side, at enqueue). */
+gpt2_status gpt2_decode_step(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_new_tokens,
+                             float* d_logits, void* stream);
+
+/* Optional per-layer trace for debugging: when d_trace is non-NULL, the next
+ * gpt2_forward calls copy the residual stream after every block (X_{l+1},
+ * fp32 [n_layer][B*T][d_model]) into d_trace, which must hold that many floats.
+ * NULL turns tracing off. */
+gpt2_status gpt2_set_trace(gpt2_model* model, float* d_trace, size_t n_floats);
+
+/* Kernel timing for measurement: when enabled, gpt2_forward records a pair of
+ * HIP events (on the call's stream) around every launch of the kernel class
+ * `which` (0 embed, 1 layernorm, 2 qkv gemm, 3 attention, 4 attn c_proj gemm,
+ * 5 c_fc gemm, 6 mlp c_proj gemm, 7 lm_head gemm).  gpt2_timing_read waits for
+ * the recorded events, returns the summed milliseconds and launch count since
+ * the last read, and resets them.  At most 4096 launches are kept per read. */
+gpt2_status gpt2_timing_enable(gpt2_model* model, int32_t which, int32_t on);
+gpt2_status gpt2_timing_read(gpt2_model* model, double* total_ms, int32_t* launches);
+
+const char* gpt2_status_string(gpt2_status s);
+
+/* Text of the last HIP error seen by this thread inside the library ("" if none). */
+const char* gpt2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_H */

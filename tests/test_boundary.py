@@ -1,0 +1,163 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side checks reject bad arguments before any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gpt2.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from gpt_pre_ln_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from gpt_pre_ln_amd.build import build
+        build(verbose=False)
+    binding.load()
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(B):
+    names = _declared_functions()
+    assert len(names) >= 12
+    lib = B.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gpt2_\w+)", out))
+    assert set(names) <= exported
+    # the binding wraps every declared entry point under the same name
+    for n in names:
+        if n not in ("gpt2_status_string", "gpt2_last_error"):
+            assert hasattr(B, n), f"binding lacks {n}"
+
+
+def _cfg(B, shape, dtype):
+    return B.make_config(shape.vocab, shape.n_positions, shape.d_model, shape.n_head, shape.n_layer,
+                         shape.d_ff, shape.ln_eps, dtype)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_blob_size_matches_layout(B, name):
+    w = W.WORKLOADS[name]
+    cfg = _cfg(B, w.shape, w.dtype)
+    assert B.gpt2_param_blob_floats(cfg) == W.param_count(w.shape)
+    es = 2 if w.dtype == "bf16" else 4
+    # device region: matrices at es bytes, wte padded to 256 rows, vectors fp32
+    assert B.gpt2_param_bytes(cfg) >= W.param_count(w.shape) * es
+
+
+def test_kv_cache_bytes(B):
+    s = W.SMALL
+    cfg = _cfg(B, s, "bf16")
+    # [L][K, V^T][B][H][round_up(max_T, 64)][hs] bf16
+    assert B.gpt2_kv_cache_bytes(cfg, 32, 1024) == 12 * 2 * 32 * 1024 * 768 * 2
+    assert B.gpt2_kv_cache_bytes(cfg, 2, 65) == 12 * 2 * 2 * 128 * 768 * 2
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(d_model=96, n_head=3), "GPT2_ERR_UNSUPPORTED"),        # head_dim 32
+    (dict(d_model=100, n_head=3), "GPT2_ERR_SHAPE"),             # not divisible
+    (dict(d_model=64, n_head=4), "GPT2_ERR_UNSUPPORTED"),        # head_dim 16 in bf16
+    (dict(dtype=7), "GPT2_ERR_UNSUPPORTED"),
+    (dict(n_layer=0), "GPT2_ERR_SHAPE"),
+    (dict(d_ff=100), "GPT2_ERR_UNSUPPORTED"),
+    (dict(n_positions=5000), "GPT2_ERR_UNSUPPORTED"),
+])
+def test_config_validation(B, change, status):
+    base = dict(vocab_size=1000, n_positions=128, d_model=128, n_head=2, n_layer=2, d_ff=512, ln_eps=1e-5,
+                dtype=B.GPT2_BF16)
+    base.update(change)
+    cfg = B.gpt2_config(**base)
+    n = ctypes.c_size_t()
+    assert B.load().gpt2_param_bytes(ctypes.byref(cfg), ctypes.byref(n)) == getattr(B, status)
+
+
+def test_fp32_head_dim_16_is_supported(B):
+    cfg = B.make_config(512, 64, 64, 4, 2, 256, 1e-5, "f32")
+    assert B.gpt2_param_blob_floats(cfg) == W.param_count(W.TINY)
+
+
+FAKE = 1 << 30  # aligned, never dereferenced: only host checks run
+
+
+@pytest.fixture()
+def handle(B):
+    cfg = B.make_config(1000, 128, 128, 2, 2, 512, 1e-5, "bf16")
+    pb = B.gpt2_param_bytes(cfg)
+    wb = B.gpt2_workspace_bytes(cfg, 2, 64)
+    h = B.gpt2_create(cfg, FAKE, pb, FAKE + (1 << 28), wb)
+    yield h, cfg
+    B.gpt2_destroy(h)
+
+
+def test_create_rejects_bad_arguments(B):
+    cfg = B.make_config(1000, 128, 128, 2, 2, 512, 1e-5, "bf16")
+    pb = B.gpt2_param_bytes(cfg)
+    wb = B.gpt2_workspace_bytes(cfg, 1, 1)
+    lib = B.load()
+    h = ctypes.c_void_p()
+    assert lib.gpt2_create(ctypes.byref(cfg), FAKE + 4, pb, FAKE, wb, ctypes.byref(h)) == B.GPT2_ERR_INVALID_ARG
+    assert lib.gpt2_create(ctypes.byref(cfg), FAKE, pb - 1, FAKE, wb, ctypes.byref(h)) == B.GPT2_ERR_WORKSPACE
+    assert lib.gpt2_create(ctypes.byref(cfg), FAKE, pb, FAKE, wb - 256, ctypes.byref(h)) == B.GPT2_ERR_WORKSPACE
+    assert lib.gpt2_create(ctypes.byref(cfg), None, pb, FAKE, wb, ctypes.byref(h)) == B.GPT2_ERR_INVALID_ARG
+
+
+def test_forward_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    fwd = lambda tok, Bz, T, lg=FAKE, hid=None, kv=None: lib.gpt2_forward(
+        h, tok, Bz, T, lg, hid, ctypes.byref(kv) if kv else None, None)
+    assert fwd(None, 1, 8) == B.GPT2_ERR_INVALID_ARG
+    assert fwd(FAKE, 1, 0) == B.GPT2_ERR_SHAPE
+    assert fwd(FAKE, 1, 129) == B.GPT2_ERR_SHAPE           # T > n_positions
+    assert fwd(FAKE, 0, 8) == B.GPT2_ERR_SHAPE
+    assert fwd(FAKE, 4, 64) == B.GPT2_ERR_WORKSPACE        # workspace sized for (2, 64)
+    assert fwd(FAKE + 2, 1, 8) == B.GPT2_ERR_INVALID_ARG   # misaligned ids
+    assert fwd(FAKE, 1, 8, hid=FAKE + 4) == B.GPT2_ERR_INVALID_ARG
+    kv = B.gpt2_kv_view(FAKE, 2, 32, 0)
+    assert fwd(FAKE, 1, 8, kv=kv) == B.GPT2_ERR_SHAPE      # kv.B != B
+    assert fwd(FAKE, 2, 40, kv=kv) == B.GPT2_ERR_CAPACITY  # T > max_T
+    kv = B.gpt2_kv_view(None, 2, 32, 0)
+    assert fwd(FAKE, 2, 8, kv=kv) == B.GPT2_ERR_INVALID_ARG
+
+
+def test_decode_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    kv = B.gpt2_kv_view(FAKE, 2, 32, 32)
+    assert lib.gpt2_decode_step(h, ctypes.byref(kv), FAKE, FAKE, None) == B.GPT2_ERR_CAPACITY
+    kv = B.gpt2_kv_view(FAKE, 2, 200, 0)
+    assert lib.gpt2_decode_step(h, ctypes.byref(kv), FAKE, FAKE, None) == B.GPT2_ERR_SHAPE
+    kv = B.gpt2_kv_view(FAKE, 2, 32, -1)
+    assert lib.gpt2_decode_step(h, ctypes.byref(kv), FAKE, FAKE, None) == B.GPT2_ERR_SHAPE
+    kv = B.gpt2_kv_view(FAKE, 2, 32, 3)
+    assert lib.gpt2_decode_step(h, ctypes.byref(kv), FAKE, None, None) == B.GPT2_ERR_INVALID_ARG
+
+
+def test_init_params_size_check(B, handle):
+    h, cfg = handle
+    n = B.gpt2_param_blob_floats(cfg)
+    assert B.load().gpt2_init_params(h, FAKE, n - 1, None) == B.GPT2_ERR_SHAPE
+    assert B.load().gpt2_init_params(h, None, n, None) == B.GPT2_ERR_INVALID_ARG
+
+
+def test_status_strings(B):
+    lib = B.load()
+    for s in range(7):
+        assert lib.gpt2_status_string(s)
+    assert lib.gpt2_last_error() is not None
