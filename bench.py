@@ -1,0 +1,247 @@
+"""Benchmark of the GPT-2 Pre-LN forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one full forward (embedding, every block, final LayerNorm, tied
+lm_head writing fp32 logits) of the workload's batch, from token ids already
+resident in HBM to logits in HBM.  Prints one JSON line.
+
+Default workload: GPT-2 small shape, bf16 matrices / fp32 accumulation,
+B=8, T=1024 (synthetic ids and random-init weights of that architecture).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (MFMA/vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+CLASSES = ["embed", "layernorm", "qkv_gemm", "attention", "attn_proj_gemm", "fc_gemm", "mlp_proj_gemm",
+           "lm_head_gemm"]
+
+
+def forward_flops(shape, B, T):
+    """Algorithmic FLOPs of one forward: 2*M*N*K per projection and the lm_head
+    (N = vocab, unpadded); causal attention counts only keys j <= i:
+    2 products (QK^T and PV) x 2 FLOP x hs x T(T+1)/2 per (b, h)."""
+    D, F, L, H, V = shape.d_model, shape.d_ff, shape.n_layer, shape.n_head, shape.vocab
+    M = B * T
+    hs = D // H
+    per_layer = 2 * M * (D * 3 * D + D * D + D * F + F * D)
+    attn = 2 * 2 * hs * (T * (T + 1) // 2) * B * H
+    return L * (per_layer + attn) + 2 * M * D * V
+
+
+def class_work(shape, B, T, cls):
+    """(algorithmic units per launch, unit, bound) for one kernel class."""
+    D, F, H, V = shape.d_model, shape.d_ff, shape.n_head, shape.vocab
+    M = B * T
+    hs = D // H
+    if cls == "qkv_gemm":
+        return 2.0 * M * D * 3 * D, "flop", "mfma"
+    if cls == "attn_proj_gemm":
+        return 2.0 * M * D * D, "flop", "mfma"
+    if cls == "fc_gemm":
+        return 2.0 * M * D * F, "flop", "mfma"
+    if cls == "mlp_proj_gemm":
+        return 2.0 * M * F * D, "flop", "mfma"
+    if cls == "lm_head_gemm":
+        return 2.0 * M * D * V, "flop", "mfma"
+    if cls == "attention":
+        return 2.0 * 2 * hs * (T * (T + 1) // 2) * B * H, "flop", "mfma"
+    if cls == "layernorm":   # read fp32 x, write bf16 h (gamma/beta negligible)
+        return float(M * D * (4 + 2)), "byte", "hbm"
+    if cls == "embed":       # read two bf16 rows, write fp32 x
+        return float(M * D * (2 + 2 + 4)), "byte", "hbm"
+    raise KeyError(cls)
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle, as it stands, on the first sequences of the same batch
+    until about `budget_s` seconds of host work have been spent."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    blob = W.make_params(w)
+    ids = W.make_ids(w)
+    P = oracle.prepare_params(blob, w.shape, w.dtype)
+    del blob
+    t0 = time.perf_counter()
+    n = 0
+    while n < w.batch:
+        oracle.forward(P, ids[n:n + 1])
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * w.seq_len / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {w.batch} sequences x {w.seq_len} tokens, full logits, fp64 numpy "
+                      f"oracle ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2-small-b8t1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-classes", action="store_true",
+                    help="also time every kernel class (one extra step per class)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
+              "sequence with no exchange, so N GPUs = N independent copies of this run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    from gpt_pre_ln_amd import binding
+    from gpt_pre_ln_amd.model import GPT2
+
+    binding.load()
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if w.decode:
+        return bench_decode(args, w)
+
+    B, T = w.batch, w.seq_len
+    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T)
+    model.load_blob(W.make_params(w))
+    ids = torch.from_numpy(W.make_ids(w)).to(dev)
+    logits = torch.empty((B, T, w.shape.vocab), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        model.forward(ids, out_logits=logits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # which kernel class dominates: one timed step per class (outside the timed region)
+    per_class = {}
+    for cls in CLASSES:
+        binding.gpt2_timing_enable(model.handle, cls, True)
+        step()
+        ms, n = binding.gpt2_timing_read(model.handle)
+        binding.gpt2_timing_enable(model.handle, cls, False)
+        per_class[cls] = {"ms_per_step": ms, "launches": n}
+    dominant = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
+
+    # timed region: K steps; the dominant class is bracketed by HIP events on its stream
+    binding.gpt2_timing_enable(model.handle, dominant, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom_ms, dom_n = binding.gpt2_timing_read(model.handle)
+    binding.gpt2_timing_enable(model.handle, dominant, False)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = B * T / (elapsed / args.steps)
+    flops = forward_flops(w.shape, B, T)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    units, unit_kind, bound = class_work(w.shape, B, T, dominant)
+    avg_s = dom_ms / 1e3 / max(dom_n, 1)
+    if unit_kind == "flop":
+        achieved = units / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        achieved = units / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = dominant
+    roof["avg_launch_ms"] = round(dom_ms / max(dom_n, 1), 5)
+    roof["launches_timed"] = dom_n
+
+    out = {
+        "metric": "forward tokens/s and % bf16 MFMA peak, GPT-2 small B=8 T=1024, 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": T, "d_model": w.shape.d_model,
+                   "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": w.shape.vocab},
+        "frac_of_peak": round(flops / (elapsed / args.steps) / (peak * 1e12), 4),
+        "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        "roofline": roof,
+        "per_class_ms": {c: round(v["ms_per_step"], 4) for c, v in per_class.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, w):
+    import torch
+    import workloads as W
+    from gpt_pre_ln_amd.model import GPT2
+
+    dev = torch.device("cuda:0")
+    B, P = w.batch, w.seq_len
+    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=P + 1)
+    model.load_blob(W.make_params(w))
+    prefix, new = W.make_decode_ids(w)
+    kv = model.new_kv_cache(B, P + 1)
+    model.forward(torch.from_numpy(prefix).to(dev), logits=False, kv=kv)
+    new_d = torch.from_numpy(new).to(dev)
+    logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device=dev)
+
+    def step():
+        kv.view.past_len = P          # re-run the same step: position P, cache slot P
+        model.decode_step(kv, new_d, out_logits=logits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    s = w.shape
+    D, F, L, V = s.d_model, s.d_ff, s.n_layer, s.vocab
+    weights = 2 * (L * (3 * D * D + D * D + 2 * D * F) + V * D)
+    kv_bytes = 2 * L * 2 * B * (P + 1) * D
+    logit_bytes = 4 * B * V
+    total = weights + kv_bytes + logit_bytes
+    gbs = total / dt / 1e9
+    out = {"metric": "decode tokens/s (GPT-2 small, B=32, cached prefix 1023)", "value": round(B / dt, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "batch": B, "prefix": P},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "kernel": "whole decode step", "algorithmic_bytes": total}}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
