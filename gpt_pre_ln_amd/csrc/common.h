@@ -112,14 +112,36 @@ __device__ __forceinline__ float exp_via_exp2(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-// gelu_new(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
-// tanh(y) = 1 - 2 / (exp(2y) + 1), which saturates to +-1 without NaN.
+// gelu_new(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+// Since 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)), this is x / (1 + exp(-2y)):
+// one base-2 exponential and one hardware reciprocal (v_rcp_f32, 1 ulp), no
+// IEEE division.  Saturates to x (large x) and to -0 (very negative x).
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  float y = k0 * (x + 0.044715f * (x * x * x));
-  float e = exp_via_exp2(2.0f * y);
-  float t = 1.0f - 2.0f / (e + 1.0f);
-  return 0.5f * x * (1.0f + t);
+  // -2 * sqrt(2/pi) * log2(e), and the same times 0.044715
+  const float c1 = -2.3022081981f, c3 = -0.1029432396f;
+  const float x2 = x * x;
+  const float z = x * (c1 + c3 * x2);          // -2y * log2(e)
+  const float e = __builtin_amdgcn_exp2f(z);   // exp(-2y)
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
+
+// Division by a runtime-invariant positive divisor through a precomputed
+// multiplier (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994): for 0 <= n < 2^31 and 1 <= d < 2^31,
+// n / d = (umulhi(n, magic) + n) >> shift with shift = ceil(log2 d),
+// magic = floor(2^32 (2^shift - d) / d) + 1.
+struct FastDiv {
+  uint32_t d, magic, shift;
+  __host__ __device__ FastDiv() : d(1), magic(1), shift(0) {}
+  __host__ explicit FastDiv(uint32_t div) : d(div) {
+    shift = 0;
+    while ((1u << shift) < div) ++shift;
+    const uint64_t one = 1;
+    magic = (uint32_t)(((one << 32) * ((one << shift) - div)) / div + 1);
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (__umulhi(n, magic) + n) >> shift;
+  }
+};
 
 }  // namespace gpt2

@@ -12,8 +12,10 @@
 //
 // Design (gfx950):
 //   * block tile BM x BN, k staged 128 bytes per step (64 bf16 / 32 fp32)
-//     through a double-buffered LDS ring, one barrier per k step; global loads
-//     of step k+1 are in flight while step k runs on the matrix cores.
+//     through an LDS ring filled by direct global->LDS loads
+//     (global_load_lds_dwordx4, no register staging), one fence-free barrier
+//     per k step; loads of step k+1 are in flight while step k runs on the
+//     matrix cores.
 //   * WGM x WGN waves; each wave owns a (BM/WGM) x (BN/WGN) sub-tile built from
 //     16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16, or 16x16x4_f32 for fp32).
 //   * operands are swapped in the MFMA (B rows first) so that every lane ends
@@ -31,29 +33,38 @@
 
 namespace gpt2 {
 
+// Epilogues see one 4-column group per call: apply(m, n, acc) with
+// acc = C[m][n .. n+3].  Those that read the output first (the residual)
+// expose the read as preload(), which the kernel issues for every fragment
+// before any store.
+
 template <typename T>
 struct EpiQKV {
+  static constexpr bool kPreload = false;
   const float* bias;  // [3D]
   T* q;               // [B][H][Tq][hs], scaled by q_scale
   T* k;               // [B][H][kvT][hs], rows t0 + t
   T* vt;              // [B][H][hs][kvT], columns t0 + t
-  int Tq;             // tokens per sequence in this call (rows m = b*Tq + t)
+  FastDiv Tq;         // tokens per sequence in this call (rows m = b*Tq + t)
+  FastDiv D;          // d_model (which third of the 3D columns)
   int t0;             // absolute position of row t = 0 (past length)
   int kvT;            // allocated positions per sequence in k / vt
-  int H, hs, D;
+  int H, hs_log2;
   float q_scale;
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
-    float4 b = *reinterpret_cast<const float4*>(bias + n);
-    float v0 = acc[0] + b.x, v1 = acc[1] + b.y, v2 = acc[2] + b.z, v3 = acc[3] + b.w;
-    int which = n / D;
-    int hd = n - which * D;
-    int head = hd / hs;
-    int d = hd - head * hs;
-    int bb = m / Tq;
-    int t = m - bb * Tq;
-    size_t bh = (size_t)bb * H + head;
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
+    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+    const float v0 = acc[0] + b.x, v1 = acc[1] + b.y, v2 = acc[2] + b.z, v3 = acc[3] + b.w;
+    const int which = (int)D.div((uint32_t)n);
+    const int hd = n - which * (int)D.d;
+    const int head = hd >> hs_log2;
+    const int d = hd - (head << hs_log2);
+    const int bb = (int)Tq.div((uint32_t)m);
+    const int t = m - bb * (int)Tq.d;
+    const size_t bh = (size_t)bb * H + head;
+    const int hs = 1 << hs_log2;
     if (which == 0) {
-      Elem<T>::store4(q + (bh * Tq + t) * hs + d, v0 * q_scale, v1 * q_scale, v2 * q_scale, v3 * q_scale);
+      Elem<T>::store4(q + (bh * Tq.d + t) * hs + d, v0 * q_scale, v1 * q_scale, v2 * q_scale, v3 * q_scale);
     } else if (which == 1) {
       Elem<T>::store4(k + (bh * kvT + t0 + t) * hs + d, v0, v1, v2, v3);
     } else {
@@ -67,38 +78,41 @@ struct EpiQKV {
 };
 
 struct EpiResidual {
+  static constexpr bool kPreload = true;
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
-    float4 b = *reinterpret_cast<const float4*>(bias + n);
-    float4* p = reinterpret_cast<float4*>(x + (size_t)m * ldx + n);
-    float4 r = *p;
-    r.x += acc[0] + b.x;
-    r.y += acc[1] + b.y;
-    r.z += acc[2] + b.z;
-    r.w += acc[3] + b.w;
-    *p = r;
+  __device__ __forceinline__ float4 preload(int m, int n) const {
+    return *reinterpret_cast<const float4*>(x + (size_t)m * ldx + n);
+  }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4& r) const {
+    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+    *reinterpret_cast<float4*>(x + (size_t)m * ldx + n) =
+        make_float4(r.x + (acc[0] + b.x), r.y + (acc[1] + b.y), r.z + (acc[2] + b.z), r.w + (acc[3] + b.w));
   }
 };
 
 template <typename T>
 struct EpiGelu {
+  static constexpr bool kPreload = false;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
-    float4 b = *reinterpret_cast<const float4*>(bias + n);
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
+    const float4 b = *reinterpret_cast<const float4*>(bias + n);
     Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(acc[0] + b.x), gelu_tanh(acc[1] + b.y),
                     gelu_tanh(acc[2] + b.z), gelu_tanh(acc[3] + b.w));
   }
 };
 
 struct EpiLogits {
+  static constexpr bool kPreload = false;
   float* out;   // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc) const {
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
     float* p = out + (size_t)m * ldo + n;
     if (n + 3 < n_valid) {
       p[0] = acc[0];
@@ -116,7 +130,7 @@ struct EpiLogits {
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),
 // K % (128 / sizeof(T)) == 0, N % 4 == 0.  `tile` picks the tile shape
 // (see gemm.hip); returns hipSuccess or the launch error.
-enum GemmTile { kTile128x128 = 0, kTile256x128 = 1, kTile64x64 = 2, kTile32x64 = 3 };
+enum GemmTile { kTile128x128 = 0, kTile256x256 = 1, kTile64x64 = 2, kTile32x64 = 3 };
 
 template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,

@@ -9,7 +9,17 @@ constexpr int kStepBytes = 128;  // k bytes per LDS stage and row (2 MFMA slabs)
 constexpr int kChunks = kStepBytes / 16;
 constexpr int kGroupM = 8;
 
+// schedule knobs
+constexpr int kPrio = 1;        // raise wave priority around each MFMA burst
+constexpr int kAllFrags = 2;    // read both slabs' fragments before the first MFMA
+constexpr int kSplitIssue = 4;  // issue the next stage's loads in two halves between slabs
+
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Map the linear block id to a (tile_m, tile_n) pair: XCD-contiguous ranges,
 // then GROUP_M tile-rows per group with tile_m varying fastest.
@@ -26,50 +36,58 @@ __device__ __forceinline__ void tile_of_block(int ntm, int ntn, int& tm, int& tn
   tn = r / gsz;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, class Epi>
+// One block computes a BM x BN tile.  Operand tiles travel global -> LDS with
+// global_load_lds_dwordx4 (no register staging): one wave instruction fills an
+// 8-row x 128-byte block, lane i writing slot i; the lane loads the global
+// chunk that belongs in that slot under the XOR swizzle.  S LDS stages form a
+// ring; stage kt+S-1 is requested right after the barrier of step kt.
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KNOB, class Epi>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ B, int M, int N,
                                                               int K, int lda, int ldb, Epi epi) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int CA = BM * kChunks, CB = BN * kChunks;
-  static_assert(CA % NT == 0 && CB % NT == 0, "tile chunks must split evenly over threads");
-  constexpr int LA = CA / NT, LB = CB / NT;
-  constexpr int KE = kStepBytes / (int)sizeof(T);  // k elements per stage
+  constexpr int RB = (BM + BN) / 8;  // 8-row blocks per stage, one wave instruction each
+  static_assert(RB % NW == 0, "row blocks must split evenly over waves");
+  constexpr int RBW = RB / NW;  // load instructions per wave per stage
+  static_assert(!(KNOB & kSplitIssue) || RBW % 2 == 0, "split issue needs an even count");
+  constexpr int STAGE = (BM + BN) * kChunks;  // u32x4 per stage
+  constexpr int KE = kStepBytes / (int)sizeof(T);
+  static_assert(S >= 2 && S <= 4, "2..4 stages");
 
-  extern __shared__ u32x4_t smem[];  // [2][(BM + BN) * kChunks]
-  constexpr int STAGE = (BM + BN) * kChunks;
+  extern __shared__ u32x4_t smem[];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-
   int tm, tn;
   tile_of_block((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Per-thread global source pointers and LDS slots (fixed over k).
-  const char* ga[LA];
-  const char* gb[LB];
-  int sa[LA], sb[LB];
+  // Loader: wave instruction j covers row block rb = j*NW + wave of the stage
+  // (A rows first, then B rows); lane -> row rb*8 + lane/8, slot lane%8.
+  const char* gsrc[RBW];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    int idx = tid + i * NT;
-    int row = idx / kChunks, c = idx % kChunks;
-    int gm = min(m0 + row, M - 1);
-    ga[i] = reinterpret_cast<const char*>(A + (size_t)gm * lda) + c * 16;
-    sa[i] = row * kChunks + swz(row, c);
+  for (int j = 0; j < RBW; ++j) {
+    const int rb = j * NW + wave;
+    const int row = rb * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);  // global chunk that lives in this lane's slot
+    const char* p;
+    if (row < BM) p = reinterpret_cast<const char*>(A + (size_t)min(m0 + row, M - 1) * lda);
+    else p = reinterpret_cast<const char*>(B + (size_t)min(n0 + row - BM, N - 1) * ldb);
+    gsrc[j] = p + c * 16;
   }
+  auto issue = [&](int kt, int j0, int j1) {
+    const size_t off = (size_t)kt * kStepBytes;
+    u32x4_t* base = smem + (kt % S) * STAGE;
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    int idx = tid + i * NT;
-    int row = idx / kChunks, c = idx % kChunks;
-    int gn = min(n0 + row, N - 1);
-    gb[i] = reinterpret_cast<const char*>(B + (size_t)gn * ldb) + c * 16;
-    sb[i] = BM * kChunks + row * kChunks + swz(row, c);
-  }
+    for (int j = j0; j < j1; ++j) {
+      u32x4_t* dst = base + (j * NW + wave) * 64;
+      __builtin_amdgcn_global_load_lds((const void*)(gsrc[j] + off), (__attribute__((address_space(3))) void*)dst,
+                                       16, 0, 0);
+    }
+  };
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -77,57 +95,72 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ra[LA], rb[LB];
-  auto gload = [&](int kt) {
-    const size_t off = (size_t)kt * kStepBytes;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ga[i] + off);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(gb[i] + off);
-  };
-  auto sstore = [&](int buf) {
-    u32x4_t* s = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) s[sa[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) s[sb[i]] = rb[i];
-  };
-
   const int KT = K / KE;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  const int lr = lane & 15;   // fragment row within a 16-row tile
-  const int lg = lane >> 4;   // lane group: 16-byte k-run within a 64-byte slab
-
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload(kt + 1);
-    const u32x4_t* s = smem + (kt & 1) * STAGE;
 #pragma unroll
-    for (int slab = 0; slab < 2; ++slab) {
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue(s, 0, RBW);
+
+  const int lr = lane & 15;  // fragment row within a 16-row tile
+  const int lg = lane >> 4;  // lane group: 16-byte k-run within a 64-byte slab
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt has landed once at most (later stages issued) * RBW loads are outstanding
+    const int later = min(S - 2, KT - 1 - kt);
+    if (S >= 4 && later >= 2) wait_vmcnt<2 * RBW>();
+    else if (S >= 3 && later >= 1) wait_vmcnt<RBW>();
+    else wait_vmcnt<0>();
+    // Barrier without a memory fence: the wait above covers this wave's LDS
+    // writes, and a fence would drain the loads still in flight.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const bool more = kt + S - 1 < KT;
+    if (!(KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW);
+
+    const u32x4_t* s = smem + (kt % S) * STAGE;
+    u32x4_t af[2][FM], bfr[2][FN];
+    auto read_frags = [&](int slab) {
       const int c = slab * 4 + lg;
-      u32x4_t af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        int r = wm * WTM + i * 16 + lr;
-        af[i] = s[r * kChunks + swz(r, c)];
+        const int r = wm * WTM + i * 16 + lr;
+        af[slab][i] = s[r * kChunks + swz(r, c)];
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        int r = wn * WTN + j * 16 + lr;
-        bfr[j] = s[BM * kChunks + r * kChunks + swz(r, c)];
+        const int r = BM + wn * WTN + j * 16 + lr;
+        bfr[slab][j] = s[r * kChunks + swz(r, c)];
       }
+    };
+    auto mfma_slab = [&](int slab) {
+      if (KNOB & kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) Mma<T>::run(acc[i][j], bfr[j], af[i]);
-    }
-    if (kt + 1 < KT) sstore((kt + 1) & 1);
-    __syncthreads();
+        for (int j = 0; j < FN; ++j) Mma<T>::run(acc[i][j], bfr[slab][j], af[slab][i]);
+      if (KNOB & kPrio) __builtin_amdgcn_s_setprio(0);
+    };
+    read_frags(0);
+    if (KNOB & kAllFrags) read_frags(1);
+    if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW / 2);
+    mfma_slab(0);
+    if (!(KNOB & kAllFrags)) read_frags(1);
+    if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, RBW / 2, RBW);
+    mfma_slab(1);
   }
 
-  // Epilogue: lane holds C[m][n .. n+3].
+  // Epilogue: lane holds C[m][n .. n+3].  Reads of the output (residual) are
+  // all issued before the first store.
+  float4 pre[FM][FN];
+  if constexpr (Epi::kPreload) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = min(m0 + wm * WTM + i * 16 + lr, M - 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = min(n0 + wn * WTN + j * 16 + lg * 4, N - 4);
+        pre[i][j] = epi.preload(m, n);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WTM + i * 16 + lr;
@@ -135,17 +168,17 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * WTN + j * 16 + lg * 4;
-      if (n < N) epi.apply(m, n, acc[i][j]);
+      if (n < N) epi.apply(m, n, acc[i][j], pre[i][j]);
     }
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, class Epi>
+template <typename T, int BM, int BN, int WGM, int WGN, int S, int KNOB, class Epi>
 hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
                        hipStream_t stream) {
   constexpr int NT = WGM * WGN * 64;
-  const size_t lds = 2 * (size_t)(BM + BN) * kStepBytes;
-  auto kern = gemm_kernel<T, BM, BN, WGM, WGN, Epi>;
+  const size_t lds = (size_t)S * (BM + BN) * kStepBytes;
+  auto kern = gemm_kernel<T, BM, BN, WGM, WGN, S, KNOB, Epi>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -164,15 +197,15 @@ template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,
                        const Epi& epi, hipStream_t stream) {
   switch (tile) {
-    case kTile256x128:
-      return launch_tile<T, 256, 128, 2, 2>(A, B, M, N, K, lda, ldb, epi, stream);
+    case kTile256x256:
+      return launch_tile<T, 256, 256, 2, 4, 2, kSplitIssue>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile64x64:
-      return launch_tile<T, 64, 64, 2, 2>(A, B, M, N, K, lda, ldb, epi, stream);
+      return launch_tile<T, 64, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile32x64:
-      return launch_tile<T, 32, 64, 2, 2>(A, B, M, N, K, lda, ldb, epi, stream);
+      return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x128:
     default:
-      return launch_tile<T, 128, 128, 2, 2>(A, B, M, N, K, lda, ldb, epi, stream);
+      return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kAllFrags>(A, B, M, N, K, lda, ldb, epi, stream);
   }
 }
 

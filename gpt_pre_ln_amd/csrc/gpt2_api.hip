@@ -191,12 +191,21 @@ const T* pp(const gpt2_model* m, size_t off) {
 }
 const float* pf(const gpt2_model* m, size_t off) { return reinterpret_cast<const float*>(m->params + off); }
 
+inline int ilog2(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
+// 256 CUs many times over (the lm_head); 128x128 otherwise (2 blocks per CU).
 GemmTile pick_tile(int M, int N) {
   if (M <= 32) return kTile32x64;
   if (M <= 64) return kTile64x64;
-  (void)N;
+  const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles256 >= 8 * 256) return kTile256x256;
   return kTile128x128;
 }
 
@@ -239,7 +248,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kQKV, st);
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, T_seq, 0, kvT, H, hs, D, q_scale};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale};
       GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D), h, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "c_attn");
     }
     {
@@ -307,7 +316,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, f
     T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
     GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
     {
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, 1, pos, kvT, H, hs, D, q_scale};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale};
       GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D), h, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
