@@ -64,6 +64,33 @@ def class_work(shape, B, T, cls):
     raise KeyError(cls)
 
 
+# kernel class -> kernel name as rocprofv3 reports it (short form)
+TRAFFIC_KERNELS = {"lm_head_gemm": "gemm_kernel<bf16_t, 256, 256, 2, 4, 2, 4, EpiLogits>",
+                   "fc_gemm": "gemm_kernel<bf16_t, 128, 128, 2, 2, 2, 3, EpiGelu<bf16_t> >",
+                   "qkv_gemm": "gemm_kernel<bf16_t, 128, 128, 2, 2, 2, 3, EpiQKV<bf16_t> >",
+                   "attention": "attn_prefill_kernel<bf16_t, 64>",
+                   "layernorm": "layernorm_kernel<bf16_t>"}
+
+
+def measured_traffic(workload, cls):
+    """HBM bytes per dispatch of the kernel (read + write) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none for
+    this workload or the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('gpt2-', 'gpt2_').replace('-', '_')}.json")
+    if not os.path.exists(path) or cls not in TRAFFIC_KERNELS:
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])).hexdigest()[:16]
+    if h != rec["source_hash"]:
+        return None
+    entry = rec["per_dispatch"].get("void " + TRAFFIC_KERNELS[cls])
+    if entry is None:
+        return None
+    return round(entry["read_bytes"] + entry["write_bytes"])
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle, as it stands, on the first sequences of the same batch
     until about `budget_s` seconds of host work have been spent."""
@@ -99,8 +126,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-small-b8t1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-classes", action="store_true",
-                    help="also time every kernel class (one extra step per class)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one device-to-device copy of 1 GiB (a plain copy kernel of known size, "
+                         "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the forward shards by "
@@ -120,6 +148,13 @@ def main():
 
     if w.decode:
         return bench_decode(args, w)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     B, T = w.batch, w.seq_len
     model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T)
@@ -171,6 +206,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     roof["kernel"] = dominant
+    roof["traffic"] = measured_traffic(w.name, dominant)
     roof["avg_launch_ms"] = round(dom_ms / max(dom_n, 1), 5)
     roof["launches_timed"] = dom_n
 

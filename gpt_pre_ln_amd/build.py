@@ -20,7 +20,7 @@ SOURCES = ["gpt2_api.hip", "gemm.hip", "attention.hip", "rowops.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    "-O3", "-std=c++20", "-fPIC", "--offload-arch=gfx950",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

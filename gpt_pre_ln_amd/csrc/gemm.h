@@ -33,14 +33,14 @@
 
 namespace gpt2 {
 
-// Epilogues see one 4-column group per call: apply(m, n, acc) with
-// acc = C[m][n .. n+3].  Those that read the output first (the residual)
-// expose the read as preload(), which the kernel issues for every fragment
-// before any store.
+// Epilogues see one 4-column group per call: apply(m, n, acc, pre, bias) with
+// acc = C[m][n .. n+3].  The kernel fetches what an epilogue reads -- bias(n)
+// and, when kPreload, preload(m, n) (the residual) -- for every fragment before
+// the first store.
 
 template <typename T>
 struct EpiQKV {
-  static constexpr bool kPreload = false;
+  static constexpr bool kPreload = false, kBias = true;
   const float* bias;  // [3D]
   T* q;               // [B][H][Tq][hs], scaled by q_scale
   T* k;               // [B][H][kvT][hs], rows t0 + t
@@ -51,9 +51,9 @@ struct EpiQKV {
   int kvT;            // allocated positions per sequence in k / vt
   int H, hs_log2;
   float q_scale;
+  __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
-    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4& b) const {
     const float v0 = acc[0] + b.x, v1 = acc[1] + b.y, v2 = acc[2] + b.z, v3 = acc[3] + b.w;
     const int which = (int)D.div((uint32_t)n);
     const int hd = n - which * (int)D.d;
@@ -78,15 +78,15 @@ struct EpiQKV {
 };
 
 struct EpiResidual {
-  static constexpr bool kPreload = true;
+  static constexpr bool kPreload = true, kBias = true;
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
+  __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int m, int n) const {
     return *reinterpret_cast<const float4*>(x + (size_t)m * ldx + n);
   }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4& r) const {
-    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4& r, const float4& b) const {
     *reinterpret_cast<float4*>(x + (size_t)m * ldx + n) =
         make_float4(r.x + (acc[0] + b.x), r.y + (acc[1] + b.y), r.z + (acc[2] + b.z), r.w + (acc[3] + b.w));
   }
@@ -94,25 +94,26 @@ struct EpiResidual {
 
 template <typename T>
 struct EpiGelu {
-  static constexpr bool kPreload = false;
+  static constexpr bool kPreload = false, kBias = true;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
+  __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
-    const float4 b = *reinterpret_cast<const float4*>(bias + n);
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4& b) const {
     Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(acc[0] + b.x), gelu_tanh(acc[1] + b.y),
                     gelu_tanh(acc[2] + b.z), gelu_tanh(acc[3] + b.w));
   }
 };
 
 struct EpiLogits {
-  static constexpr bool kPreload = false;
+  static constexpr bool kPreload = false, kBias = false;
   float* out;   // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&) const {
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4&) const {
     float* p = out + (size_t)m * ldo + n;
     if (n + 3 < n_valid) {
       p[0] = acc[0];

@@ -147,9 +147,14 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
     mfma_slab(1);
   }
 
-  // Epilogue: lane holds C[m][n .. n+3].  Reads of the output (residual) are
-  // all issued before the first store.
-  float4 pre[FM][FN];
+  // Epilogue: lane holds C[m][n .. n+3].  Reads of the output (residual) and
+  // the bias are all issued before the first store.
+  float4 pre[FM][FN], bia[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = min(n0 + wn * WTN + j * 16 + lg * 4, N - 4);
+    bia[j] = Epi::kBias ? epi.bias4(n) : float4{};
+  }
   if constexpr (Epi::kPreload) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * WTN + j * 16 + lg * 4;
-      if (n < N) epi.apply(m, n, acc[i][j], pre[i][j]);
+      if (n < N) epi.apply(m, n, acc[i][j], pre[i][j], bia[j]);
     }
   }
 }
