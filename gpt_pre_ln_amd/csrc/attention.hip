@@ -273,70 +273,120 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
 
 constexpr int kDecKeys = 256;  // keys per split block
 
-// One block per (bh, split): scores for up to 256 keys, block softmax,
-// partial output o[d] = sum_j p_j v_j with its (max, sum).
+// One block per (bh, split) of up to 256 keys.  All global reads are 16-byte
+// coalesced runs: K rows are read 8 lanes per row (each lane a 16-byte chunk
+// of head_dim), V^T rows 32 lanes per row (each lane 8 consecutive keys).
+// Writes the partial (max, sum, o[HS]) of its split.
 template <typename T, int HS>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q,
                                                                  const T* __restrict__ k,
                                                                  const T* __restrict__ vt,
                                                                  float* __restrict__ part, int n_keys,
                                                                  int kvT, int nsplit) {
-  __shared__ float sq[HS];
+  constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+  constexpr int KCH = HS / EPC;                     // chunks per K row
+  constexpr int ROWS_K = 256 / KCH;                 // K rows per pass
+  constexpr int VCH = kDecKeys / EPC;               // chunks per V^T row (256 keys)
+  constexpr int ROWS_V = 256 / VCH;                 // V^T rows per pass
+  static_assert(KCH >= 1 && KCH <= 64 && (KCH & (KCH - 1)) == 0, "K chunking");
   __shared__ float sp[kDecKeys];
   __shared__ float sred[8];
-  const int tid = threadIdx.x;
+  __shared__ float so[HS][VCH + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const int j0 = split * kDecKeys;
   const int nj = min(kDecKeys, n_keys - j0);
-  if (tid < HS) sq[tid] = Elem<T>::to_f32(q[(size_t)bh * HS + tid]);
-  __syncthreads();
 
-  // scores: one key per thread
-  float s = -INFINITY;
-  if (tid < nj) {
-    const T* kr = k + ((size_t)bh * kvT + j0 + tid) * HS;
-    float acc = 0.f;
+  // q chunk owned by this lane (fixed over passes)
+  const int kc = tid % KCH;
+  float qv[EPC];
+  {
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)bh * HS + kc * EPC);
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int d = 0; d < HS; d += 4) {
-      float4 kv4 = Elem<T>::load4(kr + d);
-      acc += sq[d] * kv4.x + sq[d + 1] * kv4.y + sq[d + 2] * kv4.z + sq[d + 3] * kv4.w;
+      for (int e = 0; e < 4; ++e) {
+        qv[2 * e] = bf16_to_f32(raw[e] & 0xFFFF);
+        qv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+      }
+    } else {
+      const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = f[e];
     }
-    s = acc;
   }
+  // scores: pass p covers rows p*ROWS_K .. +ROWS_K; KCH lanes per row
+  const T* kb = k + ((size_t)bh * kvT + j0) * HS;
+#pragma unroll 4
+  for (int p = 0; p < kDecKeys / ROWS_K; ++p) {
+    const int r = p * ROWS_K + tid / KCH;
+    float acc = 0.f;
+    if (r < nj) {
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kb + (size_t)r * HS + kc * EPC);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc += qv[2 * e] * bf16_to_f32(raw[e] & 0xFFFF) + qv[2 * e + 1] * bf16_to_f32(raw[e] >> 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += qv[e] * __builtin_bit_cast(f32x4_t, raw)[e];
+      }
+    }
+#pragma unroll
+    for (int o = KCH / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (tid % KCH == 0) sp[r] = r < nj ? acc : -INFINITY;
+  }
+  __syncthreads();
+  // block softmax over the split
+  const float s = sp[tid];
   float mx = wave_max(s);
-  if ((tid & 63) == 0) sred[tid >> 6] = mx;
+  if (lane == 0) sred[tid >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
-  const float p = tid < nj ? __builtin_amdgcn_exp2f((s - mx) * kLog2e) : 0.f;
-  sp[tid] = p;
-  float ls = wave_sum(p);
+  const float pv = tid < nj ? __builtin_amdgcn_exp2f((s - mx) * kLog2e) : 0.f;
+  float ls = wave_sum(pv);
   __syncthreads();
-  if ((tid & 63) == 0) sred[4 + (tid >> 6)] = ls;
+  sp[tid] = pv;
+  if (lane == 0) sred[4 + (tid >> 6)] = ls;
   __syncthreads();
   ls = sred[4] + sred[5] + sred[6] + sred[7];
 
-  // o[d] = sum_j p_j V^T[d][j0 + j]: 4 threads per d, each a quarter of the keys
-  constexpr int TPD = 256 / HS;           // threads per d
-  constexpr int KPT = kDecKeys / TPD;     // keys per thread
-  const int d = tid / TPD, part_i = tid % TPD;
-  const T* vr = vt + ((size_t)bh * HS + d) * kvT + j0 + part_i * KPT;
-  float acc = 0.f;
-  const int jbeg = part_i * KPT;
-#pragma unroll 4
-  for (int j = 0; j < KPT; j += 4) {
-    if (jbeg + j < nj) {
-      float4 v4 = Elem<T>::load4(vr + j);
-      // keys past nj have p == 0; their cache entries may be unwritten: guard each
-      float v[4] = {v4.x, v4.y, v4.z, v4.w};
+  // o[d] = sum_j p_j V^T[d][j0 + j]: lane owns chunk vc (EPC keys) of rows d
+  const int vc = tid % VCH;
+  float pk[EPC];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (jbeg + j + e < nj) acc += sp[jbeg + j + e] * v[e];
+  for (int e = 0; e < EPC; ++e) pk[e] = sp[vc * EPC + e];
+  const T* vb = vt + (size_t)bh * HS * kvT + j0 + vc * EPC;
+  const bool chunk_ok = vc * EPC < nj;  // keys past nj have p = 0; skip unwritten chunks
+  for (int p = 0; p < HS / ROWS_V; ++p) {
+    const int d = p * ROWS_V + tid / VCH;
+    float acc = 0.f;
+    if (chunk_ok) {
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(vb + (size_t)d * kvT);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = vc * EPC + 2 * e < nj ? bf16_to_f32(raw[e] & 0xFFFF) : 0.f;
+          const float v1 = vc * EPC + 2 * e + 1 < nj ? bf16_to_f32(raw[e] >> 16) : 0.f;
+          acc += pk[2 * e] * v0 + pk[2 * e + 1] * v1;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = vc * EPC + e < nj ? __builtin_bit_cast(f32x4_t, raw)[e] : 0.f;
+          acc += pk[e] * v0;
+        }
+      }
     }
+    so[d][vc] = acc;
   }
-#pragma unroll
-  for (int o = TPD / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  __syncthreads();
   float* dst = part + ((size_t)bh * nsplit + split) * (HS + 2);
-  if (part_i == 0) dst[d] = acc;
+  if (tid < HS) {
+    float o = 0.f;
+#pragma unroll 8
+    for (int c = 0; c < VCH; ++c) o += so[tid][c];
+    dst[tid] = o;
+  }
   if (tid == 0) {
     dst[HS] = mx;
     dst[HS + 1] = ls;

@@ -15,8 +15,10 @@ struct bf16_t {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-// 16-byte fragment as a native clang vector (element access compiles to plain
-// register moves; HIP's uint4 is a union wrapper and is not used for fragments).
+// 16-byte fragment as a native clang vector.  Two compiler pitfalls are avoided
+// throughout: HIP's uint4 (a union wrapper) is never used for fragments, and
+// __builtin_bit_cast is applied to whole vectors, never to a vector element --
+// on this toolchain bit_cast(float, v[e]) reads element 0 for every e.
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 

@@ -196,6 +196,60 @@ hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ skinny
+// GEMMs with at most 32 rows (the decode step: one row per sequence) are
+// bound by streaming B once.  The work is split over (64-column block,
+// 256-element k split); each wave reads its 16 B rows and both 16-row A
+// fragments straight from global memory (no LDS: nothing is shared), and
+// writes fp32 partial sums.  A second kernel adds the splits and applies the
+// same fused epilogue as the tiled kernel.
+constexpr int kSkinnyK = 256;
+
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_skinny_partial_kernel(const T* __restrict__ A, const T* __restrict__ B,
+                                                                   float* __restrict__ part, int M, int N, int K,
+                                                                   int lda, int ldb) {
+  constexpr int SLAB = Mma<T>::kPerSlab;  // k elements per 16-byte-per-lane fragment step
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int s = blockIdx.y;
+  const int k0 = s * kSkinnyK, k1 = min(k0 + kSkinnyK, K);
+  const T* brow = B + (size_t)min(n0 + lr, N - 1) * ldb;
+  const T* arow0 = A + (size_t)min(lr, M - 1) * lda;
+  const T* arow1 = A + (size_t)min(16 + lr, M - 1) * lda;
+  const int lofs = lg * (16 / (int)sizeof(T));
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = k0; k < k1; k += SLAB) {
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + k + lofs);
+    const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(arow0 + k + lofs);
+    const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(arow1 + k + lofs);
+    Mma<T>::run(acc0, b, a0);
+    Mma<T>::run(acc1, b, a1);
+  }
+  // lane holds C[m][n0 + 4*lg .. +3] for m = lr (acc0) and 16 + lr (acc1)
+  const int n = n0 + lg * 4;
+  if (n < N) {
+    if (lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + lr) * N + n) = acc0;
+    if (16 + lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + 16 + lr) * N + n) = acc1;
+  }
+}
+
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(const float* __restrict__ part, int S, int M,
+                                                                  int N, Epi epi) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (idx >= M * n4) return;
+  const int m = idx / n4, n = (idx - m * n4) * 4;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) acc += *reinterpret_cast<const f32x4_t*>(part + ((size_t)s * M + m) * N + n);
+  const float4 pre = Epi::kPreload ? epi.preload(m, n) : float4{};
+  const float4 bia = Epi::kBias ? epi.bias4(n) : float4{};
+  epi.apply(m, n, acc, pre, bia);
+}
+
 }  // namespace
 
 template <typename T, class Epi>
@@ -214,9 +268,30 @@ hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int 
   }
 }
 
+size_t skinny_partials_floats(int M, int N, int K) {
+  return (size_t)((K + kSkinnyK - 1) / kSkinnyK) * M * N;
+}
+
+template <typename T, class Epi>
+hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
+                              float* part, hipStream_t stream) {
+  if (M > 32 || M < 1) return hipErrorInvalidValue;
+  const int S = (K + kSkinnyK - 1) / kSkinnyK;
+  hipLaunchKernelGGL(gemm_skinny_partial_kernel<T>, dim3((N + 63) / 64, S), dim3(256), 0, stream, A, B, part, M, N,
+                     K, lda, ldb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int total = M * (N / 4);
+  hipLaunchKernelGGL(gemm_skinny_reduce_kernel<Epi>, dim3((total + 255) / 256), dim3(256), 0, stream, part, S, M, N,
+                     epi);
+  return hipGetLastError();
+}
+
 #define GPT2_INSTANTIATE_GEMM(T, EPI)                                                               \
   template hipError_t launch_gemm<T, EPI>(GemmTile, const T*, const T*, int, int, int, int, int, \
-                                          const EPI&, hipStream_t);
+                                          const EPI&, hipStream_t);                                      \
+  template hipError_t launch_gemm_skinny<T, EPI>(const T*, const T*, int, int, int, int, int, const EPI&, float*, \
+                                                 hipStream_t);
 
 GPT2_INSTANTIATE_GEMM(float, EpiQKV<float>)
 GPT2_INSTANTIATE_GEMM(float, EpiResidual)
