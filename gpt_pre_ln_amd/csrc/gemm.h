@@ -19,8 +19,11 @@
 //   * WGM x WGN waves; each wave owns a (BM/WGM) x (BN/WGN) sub-tile built from
 //     16x16 MFMA tiles (v_mfma_f32_16x16x32_bf16, or 16x16x4_f32 for fp32).
 //   * operands are swapped in the MFMA (B rows first) so that every lane ends
-//     with 4 consecutive output columns of one row: epilogue stores are
-//     8- or 16-byte vectors.
+//     with 4 consecutive output columns of one row.
+//   * epilogue: bias added in registers, then each wave stages its sub-tile
+//     through its own slice of the operand LDS and reads it back so that one
+//     store instruction covers whole row segments (or, for the transposed
+//     V^T output, whole column segments) instead of 16 rows x 16 columns.
 //   * LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r lives at
 //     slot c ^ (r & 7) so the 16 rows read by a lane group fall in distinct
 //     bank groups.
@@ -33,14 +36,16 @@
 
 namespace gpt2 {
 
-// Epilogues see one 4-column group per call: apply(m, n, acc, pre, bias) with
-// acc = C[m][n .. n+3].  The kernel fetches what an epilogue reads -- bias(n)
-// and, when kPreload, preload(m, n) (the residual) -- for every fragment before
-// the first store.
+// Epilogues.  The kernel adds the bias (bias4(n), when kBias) to the
+// accumulators first and then hands over 4-element groups:
+//   apply(m, n, v, pre)  v = C[m][n .. n+3]; pre = preload(m, n) when kPreload
+//                        (the residual), fetched before the group's stores;
+//   apply_t(m, n, v)     v = C[m .. m+3][n], only when kTransposed and
+//                        transposed(n) holds for the (64-aligned) column block.
 
 template <typename T>
 struct EpiQKV {
-  static constexpr bool kPreload = false, kBias = true;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = true;
   const float* bias;  // [3D]
   T* q;               // [B][H][Tq][hs], scaled by q_scale
   T* k;               // [B][H][kvT][hs], rows t0 + t
@@ -51,10 +56,12 @@ struct EpiQKV {
   int kvT;            // allocated positions per sequence in k / vt
   int H, hs_log2;
   float q_scale;
+  int M;              // rows of the product (B * Tq)
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4& b) const {
-    const float v0 = acc[0] + b.x, v1 = acc[1] + b.y, v2 = acc[2] + b.z, v3 = acc[3] + b.w;
+  // the value third (columns 2D .. 3D) is stored transposed
+  __device__ __forceinline__ bool transposed(int n) const { return D.div((uint32_t)n) == 2; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
     const int which = (int)D.div((uint32_t)n);
     const int hd = n - which * (int)D.d;
     const int head = hd >> hs_log2;
@@ -64,21 +71,43 @@ struct EpiQKV {
     const size_t bh = (size_t)bb * H + head;
     const int hs = 1 << hs_log2;
     if (which == 0) {
-      Elem<T>::store4(q + (bh * Tq.d + t) * hs + d, v0 * q_scale, v1 * q_scale, v2 * q_scale, v3 * q_scale);
+      Elem<T>::store4(q + (bh * Tq.d + t) * hs + d, v[0] * q_scale, v[1] * q_scale, v[2] * q_scale, v[3] * q_scale);
     } else if (which == 1) {
-      Elem<T>::store4(k + (bh * kvT + t0 + t) * hs + d, v0, v1, v2, v3);
+      Elem<T>::store4(k + (bh * kvT + t0 + t) * hs + d, v[0], v[1], v[2], v[3]);
     } else {
       T* p = vt + (bh * hs + d) * kvT + t0 + t;
-      p[0] = Elem<T>::from_f32(v0);
-      p[kvT] = Elem<T>::from_f32(v1);
-      p[2 * (size_t)kvT] = Elem<T>::from_f32(v2);
-      p[3 * (size_t)kvT] = Elem<T>::from_f32(v3);
+      p[0] = Elem<T>::from_f32(v[0]);
+      p[kvT] = Elem<T>::from_f32(v[1]);
+      p[2 * (size_t)kvT] = Elem<T>::from_f32(v[2]);
+      p[3 * (size_t)kvT] = Elem<T>::from_f32(v[3]);
+    }
+  }
+  // v = C[m .. m+3][n] with n in the value third: positions t .. t+3 of one
+  // V^T row, stored as one vector when they lie in one sequence and aligned.
+  __device__ __forceinline__ void apply_t(int m, int n, const f32x4_t& v) const {
+    const int hd = n - 2 * (int)D.d;
+    const int head = hd >> hs_log2;
+    const int d = hd - (head << hs_log2);
+    const int hs = 1 << hs_log2;
+    const int bb = (int)Tq.div((uint32_t)m);
+    const int t = m - bb * (int)Tq.d;
+    if (m + 3 < M && t + 3 < (int)Tq.d && ((t0 + t) & 3) == 0) {
+      Elem<T>::store4(vt + (((size_t)bb * H + head) * hs + d) * kvT + t0 + t, v[0], v[1], v[2], v[3]);
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int me = m + e;
+      if (me >= M) break;
+      const int be = (int)Tq.div((uint32_t)me);
+      const int te = me - be * (int)Tq.d;
+      vt[(((size_t)be * H + head) * hs + d) * kvT + t0 + te] = Elem<T>::from_f32(v[e]);
     }
   }
 };
 
 struct EpiResidual {
-  static constexpr bool kPreload = true, kBias = true;
+  static constexpr bool kPreload = true, kBias = true, kTransposed = false;
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
@@ -86,46 +115,51 @@ struct EpiResidual {
   __device__ __forceinline__ float4 preload(int m, int n) const {
     return *reinterpret_cast<const float4*>(x + (size_t)m * ldx + n);
   }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4& r, const float4& b) const {
-    *reinterpret_cast<float4*>(x + (size_t)m * ldx + n) =
-        make_float4(r.x + (acc[0] + b.x), r.y + (acc[1] + b.y), r.z + (acc[2] + b.z), r.w + (acc[3] + b.w));
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4& r) const {
+    *reinterpret_cast<float4*>(x + (size_t)m * ldx + n) = make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);
   }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
 template <typename T>
 struct EpiGelu {
-  static constexpr bool kPreload = false, kBias = true;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = false;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4& b) const {
-    Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(acc[0] + b.x), gelu_tanh(acc[1] + b.y),
-                    gelu_tanh(acc[2] + b.z), gelu_tanh(acc[3] + b.w));
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
+    Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
   }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
+// fp32 logits rows of ldo floats (ldo = vocabulary size, so rows are only
+// 4-byte aligned): each 4-column group goes out as one unaligned 16-byte
+// store, masked per element at the vocabulary edge.
+typedef float f32x4_u4_t __attribute__((ext_vector_type(4), aligned(4)));
 struct EpiLogits {
-  static constexpr bool kPreload = false, kBias = false;
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false;
   float* out;   // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
   __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
-  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& acc, const float4&, const float4&) const {
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
     float* p = out + (size_t)m * ldo + n;
     if (n + 3 < n_valid) {
-      p[0] = acc[0];
-      p[1] = acc[1];
-      p[2] = acc[2];
-      p[3] = acc[3];
+      *reinterpret_cast<f32x4_u4_t*>(p) = v;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (n + e < n_valid) p[e] = acc[e];
+        if (n + e < n_valid) p[e] = v[e];
     }
   }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),

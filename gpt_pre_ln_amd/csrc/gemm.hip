@@ -147,33 +147,87 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
     mfma_slab(1);
   }
 
-  // Epilogue: lane holds C[m][n .. n+3].  Reads of the output (residual) and
-  // the bias are all issued before the first store.
-  float4 pre[FM][FN], bia[FN];
+  // Epilogue.  Lane holds C[m][n .. n+3] of each fragment; the bias is added
+  // in that layout first.
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = min(n0 + wn * WTN + j * 16 + lg * 4, N - 4);
-    bia[j] = Epi::kBias ? epi.bias4(n) : float4{};
-  }
-  if constexpr (Epi::kPreload) {
+    if constexpr (Epi::kBias) {
+      const float4 b = epi.bias4(min(n0 + wn * WTN + j * 16 + lg * 4, N - 4));
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = min(m0 + wm * WTM + i * 16 + lr, M - 1);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = min(n0 + wn * WTN + j * 16 + lg * 4, N - 4);
-        pre[i][j] = epi.preload(m, n);
-      }
+      for (int i = 0; i < FM; ++i) acc[i][j] += f32x4_t{b.x, b.y, b.z, b.w};
     }
   }
+
+  // Each wave then stages its WTM x WTN sub-tile through a private slice
+  // of the (now idle) operand LDS, R rows at a time, and reads it back so
+  // that 16-byte groups of consecutive lanes cover consecutive columns of one
+  // row (row mode) or consecutive rows of one column (transposed mode, for
+  // outputs stored transposed): each store instruction then writes whole
+  // row segments instead of 16 rows x 16 columns.
+  constexpr int LDS_F = S * (BM + BN) * kStepBytes / 4;  // floats of LDS
+  constexpr int PER_WAVE = LDS_F / NW;
+  constexpr int R = WTM < PER_WAVE / WTN ? WTM : PER_WAVE / WTN;  // rows staged per round
+  static_assert(R % 16 == 0 && WTM % R == 0, "staging rounds must hold whole fragments");
+  constexpr int CPR = WTN / 4;  // 16-byte chunks per staged row (row mode)
+  constexpr int CPT = R / 4;    // 16-byte chunks per staged column (transposed mode)
+  static_assert(CPR <= 16 && CPT <= 16 && 64 % CPR == 0 && 64 % CPT == 0, "lane mapping");
+
+  // every wave is past its last operand read (its MFMAs consumed them) and
+  // the last stage's loads have landed (vmcnt(0) in the last step)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  float* stg = reinterpret_cast<float*>(smem) + wave * PER_WAVE;
+  const int mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+  const bool tr = Epi::kTransposed && epi.transposed(nw);
+
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 16 + lr;
-    if (m >= M) continue;
+  for (int rd = 0; rd < WTM / R; ++rd) {
+    const int mr = mw + rd * R;  // first row of this round
+    if (!tr) {
+      // row-major [R][WTN] with chunk c of row r at slot c ^ (r % CPR)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WTN + j * 16 + lg * 4;
-      if (n < N) epi.apply(m, n, acc[i][j], pre[i][j], bia[j]);
+      for (int i = 0; i < R / 16; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int r = i * 16 + lr, c = j * 4 + lg;
+          *reinterpret_cast<f32x4_t*>(stg + r * WTN + ((c ^ (r & (CPR - 1))) << 2)) = acc[rd * (R / 16) + i][j];
+        }
+      constexpr int RPI = 64 / CPR;  // rows per read instruction
+      const int c = lane % CPR;
+      const int n = nw + c * 4;
+      float4 pre[R / RPI];
+      if constexpr (Epi::kPreload) {
+#pragma unroll
+        for (int q = 0; q < R / RPI; ++q)
+          pre[q] = epi.preload(min(mr + q * RPI + lane / CPR, M - 1), min(n, N - 4));
+      }
+#pragma unroll
+      for (int q = 0; q < R / RPI; ++q) {
+        const int r = q * RPI + lane / CPR;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * WTN + ((c ^ (r & (CPR - 1))) << 2));
+        const int m = mr + r;
+        if (m < M && n < N) epi.apply(m, n, v, pre[q]);
+      }
+    } else {
+      // column-major [WTN][R] with chunk c of column n at slot c ^ (n % CPT)
+#pragma unroll
+      for (int i = 0; i < R / 16; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = i * 16 + lr, col = j * 16 + lg * 4 + e;
+            stg[col * R + (((r >> 2) ^ (col & (CPT - 1))) << 2) + (r & 3)] = acc[rd * (R / 16) + i][j][e];
+          }
+      constexpr int CPI = 64 / CPT;  // columns per read instruction
+      const int c = lane % CPT;
+#pragma unroll
+      for (int q = 0; q < WTN / CPI; ++q) {
+        const int col = q * CPI + lane / CPT;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + col * R + ((c ^ (col & (CPT - 1))) << 2));
+        const int m = mr + c * 4, n = nw + col;
+        if (m < M && n < N) epi.apply_t(m, n, v);
+      }
     }
   }
 }
@@ -246,8 +300,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(const float* __
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) acc += *reinterpret_cast<const f32x4_t*>(part + ((size_t)s * M + m) * N + n);
   const float4 pre = Epi::kPreload ? epi.preload(m, n) : float4{};
-  const float4 bia = Epi::kBias ? epi.bias4(n) : float4{};
-  epi.apply(m, n, acc, pre, bia);
+  if constexpr (Epi::kBias) {
+    const float4 b = epi.bias4(n);
+    acc += f32x4_t{b.x, b.y, b.z, b.w};
+  }
+  epi.apply(m, n, acc, pre);
 }
 
 }  // namespace

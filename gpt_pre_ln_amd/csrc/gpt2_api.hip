@@ -265,7 +265,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kQKV, st);
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, skinny, st), "c_attn");
     }
     {
@@ -334,7 +334,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, f
     T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
     GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
     {
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, skinny, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
