@@ -23,17 +23,38 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// max over the lanes l, l^16, l^32, l^48 (the four lane groups holding one
+// query of an MFMA fragment), with the gfx950 row-swap permutes.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, r16[0]), __builtin_bit_cast(float, r16[1]));
+  const unsigned w = __builtin_bit_cast(unsigned, v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, r32[0]), __builtin_bit_cast(float, r32[1]));
+}
+
 template <int CH>
 __device__ __forceinline__ int swz_ch(int row, int c) {
   return c ^ (row & ((CH < 8 ? CH : 8) - 1));
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Block barrier without a memory fence (a fence would also wait for the next
+// tile's loads in flight); callers wait for their own loads first.
+__device__ __forceinline__ void barrier_nofence() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__ q,
-                                                            const T* __restrict__ k,
-                                                            const T* __restrict__ vt,
-                                                            T* __restrict__ out, int BH, int H,
-                                                            int Tq, int kvT, int n_qtiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_prefill_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, T* __restrict__ out, int BH, int H,
+    int Tq, int kvT, int n_qtiles) {
   constexpr int QW = 32, NW = 4, BQ = QW * NW, BKEYS = 64;
   constexpr int ESZ = (int)sizeof(T);
   constexpr int KROWB = HS * ESZ, KCH = KROWB / 16;     // K tile rows (keys)
@@ -41,16 +62,19 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
   constexpr int NSLAB = KROWB / 64;
   constexpr int KF = BKEYS / 16, DF = HS / 16, QF = QW / 16;
   constexpr int KPS = Mma<T>::kPerSlab;      // keys per PV matrix step
-  constexpr int KFPS = KPS / 16;             // key fragments per PV step (2 bf16, 1 fp32)
   constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
   constexpr int K_CHUNKS = BKEYS * KCH, V_CHUNKS = HS * VCH;
-  constexpr int LK = (K_CHUNKS + 255) / 256, LV = (V_CHUNKS + 255) / 256;
+  // direct global->LDS loads: one instruction fills 64 consecutive chunks
+  constexpr int KI = K_CHUNKS / 64 / NW, VI = V_CHUNKS / 64 / NW;  // instructions per wave per tile
   static_assert(NSLAB >= 1 && KROWB % 64 == 0, "head_dim bytes must be a multiple of 64");
+  static_assert(KI * 64 * NW == K_CHUNKS && VI * 64 * NW == V_CHUNKS && KI >= 1 && VI >= 1, "tile split");
+  static_assert(KI + VI <= 63, "loads in flight must fit the vmcnt counter");
 
   __shared__ u32x4_t sK[2][K_CHUNKS];
   __shared__ u32x4_t sV[2][V_CHUNKS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x % BH;
   const int qt = n_qtiles - 1 - blockIdx.x / BH;
@@ -67,6 +91,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
   const T* kb = k + (size_t)bh * kvT * HS;
   const T* vb = vt + (size_t)bh * HS * kvT;
 
+  // K tile row r holds key key_of_row(r) of the tile.  For bf16 the rows are
+  // permuted within each 32-key group (r = 16h + 4g + i holds key 8g + 4h + i)
+  // so that the S^T fragments give lane group g the probabilities of keys
+  // 8g .. 8g+7 of the group: exactly the 16 contiguous bytes of a V^T row that
+  // the same lane supplies to the P V product.
+  auto key_of_row = [](int r) {
+    if constexpr (ESZ == 2) return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+    else return r;
+  };
+
   // Query fragments stay in registers: lane (lr, lg) holds query q0w+qf*16+lr,
   // bytes slab*64 + lg*16 .. +16 of its row.
   u32x4_t qfrag[QF][NSLAB];
@@ -78,139 +112,142 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
     for (int s = 0; s < NSLAB; ++s) qfrag[qf][s] = *reinterpret_cast<const u32x4_t*>(p + s * 64 + lg * 16);
   }
 
-  u32x4_t rk[LK], rv[LV];
-  auto gload = [&](int kt) {
+  // Tile loads: wave instruction j fills LDS chunks (j*NW + wave)*64 + lane;
+  // chunk slot s of row r holds the row's global chunk swz_ch(r, s) (the XOR
+  // swizzle is an involution).  Keys past the end are clamped to the last
+  // valid one for K (their scores are masked) and fixed up for V^T below.
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      int idx = tid + i * 256;
-      if (idx < K_CHUNKS) {
-        int row = idx / KCH, c = idx % KCH;
-        int key = min(kt * BKEYS + row, nkeys - 1);
-        rk[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(kb + (size_t)key * HS) + c * 16);
-      }
+    for (int j = 0; j < KI; ++j) {
+      const int ci = (j * NW + wave) * 64 + lane;
+      const int row = ci / KCH, slot = ci % KCH;
+      const int key = min(kt * BKEYS + key_of_row(row), nkeys - 1);
+      const char* src = reinterpret_cast<const char*>(kb + (size_t)key * HS) + swz_ch<KCH>(row, slot) * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)&sK[buf][(j * NW + wave) * 64], 16,
+                                       0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      int idx = tid + i * 256;
-      if (idx < V_CHUNKS) {
-        int d = idx / VCH, c = idx % VCH;
-        int key0 = kt * BKEYS + c * EPC;
-        const T* src = vb + (size_t)d * kvT + key0;
-        if (key0 + EPC <= nkeys) {
-          rv[i] = *reinterpret_cast<const u32x4_t*>(src);
-        } else {
-          // partial chunk at the end of the sequence: zero the invalid keys
-          u32x4_t w = {0u, 0u, 0u, 0u};
-          if (key0 < nkeys) {
-            const u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(src);
-            const int valid_bytes = (nkeys - key0) * ESZ;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              int lo = j * 4;
-              if (lo + 4 <= valid_bytes) w[j] = t4[j];
-              else if (lo < valid_bytes) w[j] = t4[j] & 0xFFFFu;  // only bf16 can split a word
-            }
-          }
-          rv[i] = w;
-        }
-      }
+    for (int j = 0; j < VI; ++j) {
+      const int ci = (j * NW + wave) * 64 + lane;
+      const int d = ci / VCH, slot = ci % VCH;
+      // chunks wholly past the end read the tile's first chunk instead (in bounds; zeroed below)
+      int c = swz_ch<VCH>(d, slot);
+      if (kt * BKEYS + c * EPC >= nkeys) c = 0;
+      const T* src = vb + (size_t)d * kvT + kt * BKEYS + c * EPC;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)&sV[buf][(j * NW + wave) * 64], 16,
+                                       0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      int idx = tid + i * 256;
-      if (idx < K_CHUNKS) {
-        int row = idx / KCH, c = idx % KCH;
-        sK[buf][row * KCH + swz_ch<KCH>(row, c)] = rk[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      int idx = tid + i * 256;
-      if (idx < V_CHUNKS) {
-        int d = idx / VCH, c = idx % VCH;
-        sV[buf][d * VCH + swz_ch<VCH>(d, c)] = rv[i];
-      }
+  // V^T of a tile that runs past the last key: zero the keys >= nkeys (their
+  // probabilities are 0, but the cache there is uninitialised and 0 * NaN is NaN).
+  auto fix_tail = [&](int kt, int buf) {
+    const int valid = nkeys - kt * BKEYS;  // 1 .. BKEYS-1
+    T* base = reinterpret_cast<T*>(&sV[buf][0]);
+    for (int idx = tid; idx < HS * BKEYS; idx += 256) {
+      const int d = idx / BKEYS, key = idx % BKEYS;
+      if (key >= valid) base[(d * VCH + swz_ch<VCH>(d, key / EPC)) * EPC + key % EPC] = Elem<T>::from_f32(0.f);
     }
   };
 
-  f32x4_t o[DF][QF];
-  float m_run[QF], l_run[QF];
+  // Running state per query (lane (lr, lg) holds query q0w + qf*16 + lr):
+  //   m_run  reference maximum the exponentials are taken against;
+  //   o      O^T[d = df*16 + 4*lg + e][query], unnormalised;
+  //   lsum   row sums of P, all four elements equal, produced by the matrix
+  //          cores as 1^T P^T (a fragment of ones in place of V^T).
+  // The reference maximum is only moved when a tile's maximum exceeds it by
+  // more than kSlack (so exp2 arguments stay <= kSlack * log2 e, far from
+  // overflow): most tiles then need no rescaling of o and lsum at all.
+  constexpr float kSlack = 5.5f;
+  f32x4_t o[DF][QF], lsum[QF];
+  float m_run[QF], mb[QF];
 #pragma unroll
   for (int qf = 0; qf < QF; ++qf) {
     m_run[qf] = -INFINITY;
-    l_run[qf] = 0.f;
+    mb[qf] = -INFINITY;
+    lsum[qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int df = 0; df < DF; ++df) o[df][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const u32x4_t ones = ESZ == 2 ? u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                : u32x4_t{0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0, 0);
+  wait_vmcnt<0>();
+  barrier_nofence();
+  if (BKEYS > nkeys) {
+    fix_tail(0, 0);
+    __syncthreads();
+  }
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) gload(kt + 1);
     const int buf = kt & 1;
+    // the other buffer was released by the barrier that ended the previous tile
+    if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);
     const int key0 = kt * BKEYS;
     if (key0 <= q0w + QW - 1) {  // wave-uniform: otherwise the whole tile is masked for this wave
+      // S^T = K Q^T: lane holds S^T[key = key0 + key_of_row(kf*16 + 4*lg + e)][query = q0w + qf*16 + lr]
       f32x4_t s[KF][QF];
-#pragma unroll
-      for (int kf = 0; kf < KF; ++kf)
-#pragma unroll
-        for (int qf = 0; qf < QF; ++qf) s[kf][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int sl = 0; sl < NSLAB; ++sl) {
 #pragma unroll
         for (int kf = 0; kf < KF; ++kf) {
-          int row = kf * 16 + lr;
-          u32x4_t kfr = sK[buf][row * KCH + swz_ch<KCH>(row, sl * 4 + lg)];
+          const int row = kf * 16 + lr;
+          const u32x4_t kfr = sK[buf][row * KCH + swz_ch<KCH>(row, sl * 4 + lg)];
 #pragma unroll
-          for (int qf = 0; qf < QF; ++qf) Mma<T>::run(s[kf][qf], kfr, qfrag[qf][sl]);
+          for (int qf = 0; qf < QF; ++qf) {
+            if (sl == 0) s[kf][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            Mma<T>::run(s[kf][qf], kfr, qfrag[qf][sl]);
+          }
         }
       }
-      // lane holds S^T[key = key0 + kf*16 + 4*lg + e][query = q0w + qf*16 + lr]
-      const bool diag = key0 + BKEYS - 1 > q0w;
+      if (key0 + BKEYS - 1 > q0w) {  // the tile straddles this wave's diagonal
 #pragma unroll
-      for (int qf = 0; qf < QF; ++qf) {
-        const int qi = q0w + qf * 16 + lr;
-        if (diag) {
+        for (int qf = 0; qf < QF; ++qf) {
+          const int lim = q0w + qf * 16 + lr - key0;  // tile keys > lim are masked
 #pragma unroll
           for (int kf = 0; kf < KF; ++kf)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (key0 + kf * 16 + 4 * lg + e > qi) s[kf][qf][e] = -INFINITY;
-        }
-        float mx = s[0][qf][0];
-#pragma unroll
-        for (int kf = 0; kf < KF; ++kf)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kf][qf][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qf], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[qf] - m_new) * kLog2e);
-        m_run[qf] = m_new;
-        const float mb = m_new * kLog2e;
-        float ls = 0.f;
-#pragma unroll
-        for (int kf = 0; kf < KF; ++kf)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p = __builtin_amdgcn_exp2f(s[kf][qf][e] * kLog2e - mb);
-            s[kf][qf][e] = p;
-            ls += p;
-          }
-        l_run[qf] = l_run[qf] * alpha + ls;
-#pragma unroll
-        for (int df = 0; df < DF; ++df) {
-          o[df][qf][0] *= alpha;
-          o[df][qf][1] *= alpha;
-          o[df][qf][2] *= alpha;
-          o[df][qf][3] *= alpha;
+              if (key_of_row(kf * 16 + 4 * lg + e) > lim) s[kf][qf][e] = -INFINITY;
         }
       }
-      // O^T += V^T P^T, KPS keys per matrix step
+      // tile maximum per query: 16 values in the lane, then across the four
+      // lanes (lr, lr+16, lr+32, lr+48) that hold the same query
+      float mx[QF];
+      bool grow = false;
+#pragma unroll
+      for (int qf = 0; qf < QF; ++qf) {
+        float m = fmaxf(s[0][qf][0], s[0][qf][1]);
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+          for (int e = (kf == 0 ? 2 : 0); e < 4; ++e) m = fmaxf(m, s[kf][qf][e]);
+        m = max_over_lane_groups(m);
+        mx[qf] = m;
+        grow |= m > m_run[qf] + kSlack;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int qf = 0; qf < QF; ++qf) {
+          const float m_new = fmaxf(m_run[qf], mx[qf]);
+          const float alpha = __builtin_amdgcn_exp2f((m_run[qf] - m_new) * kLog2e);
+          m_run[qf] = m_new;
+          mb[qf] = m_new * kLog2e;
+          lsum[qf] *= alpha;
+#pragma unroll
+          for (int df = 0; df < DF; ++df) o[df][qf] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int qf = 0; qf < QF; ++qf)
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kf][qf][e] = __builtin_amdgcn_exp2f(fmaf(s[kf][qf][e], kLog2e, -mb[qf]));
+
+      // O^T += V^T P^T and lsum += 1^T P^T, KPS keys per matrix step
 #pragma unroll
       for (int st = 0; st < BKEYS / KPS; ++st) {
         u32x4_t pf[QF];
@@ -222,42 +259,34 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
             pf[qf] = u32x4_t{pack2_bf16(p0[0], p0[1]), pack2_bf16(p0[2], p0[3]), pack2_bf16(p1[0], p1[1]),
                              pack2_bf16(p1[2], p1[3])};
           } else {
-            const f32x4_t& p0 = s[st][qf];
-            pf[qf] = __builtin_bit_cast(u32x4_t, p0);
+            pf[qf] = __builtin_bit_cast(u32x4_t, s[st][qf]);
           }
+          Mma<T>::run(lsum[qf], ones, pf[qf]);
         }
 #pragma unroll
         for (int df = 0; df < DF; ++df) {
           const int d = df * 16 + lr;
-          u32x4_t vf;
-          if constexpr (ESZ == 2) {
-            // keys st*32 + 4*lg + 0..3 and st*32 + 16 + 4*lg + 0..3 (8 bytes each)
-            const int c0 = st * 4 + (lg >> 1), c1 = c0 + 2, half = lg & 1;
-            const u32x2_t* row = reinterpret_cast<const u32x2_t*>(&sV[buf][d * VCH]);
-            const u32x2_t a0 = row[swz_ch<VCH>(d, c0) * 2 + half];
-            const u32x2_t a1 = row[swz_ch<VCH>(d, c1) * 2 + half];
-            vf = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-          } else {
-            // keys st*16 + 4*lg + 0..3 (16 bytes)
-            vf = sV[buf][d * VCH + swz_ch<VCH>(d, st * 4 + lg)];
-          }
+          // bf16: keys st*32 + 8*lg .. +7; fp32: keys st*16 + 4*lg .. +3 (16 bytes)
+          const u32x4_t vf = sV[buf][d * VCH + swz_ch<VCH>(d, st * 4 + lg)];
 #pragma unroll
           for (int qf = 0; qf < QF; ++qf) Mma<T>::run(o[df][qf], vf, pf[qf]);
         }
       }
-      (void)KFPS;
     }
-    if (kt + 1 < n_kt) sstore((kt + 1) & 1);
-    __syncthreads();
+    if (kt + 1 < n_kt) {
+      wait_vmcnt<0>();   // this wave's part of the next tile has landed
+      barrier_nofence();  // ... everyone's, and everyone is done with this tile
+      if ((kt + 2) * BKEYS > nkeys) {
+        fix_tail(kt + 1, buf ^ 1);
+        __syncthreads();
+      }
+    }
   }
 
   // Normalise and merge heads: lane holds O^T[d = df*16 + 4*lg + e][query = q0w + qf*16 + lr]
 #pragma unroll
   for (int qf = 0; qf < QF; ++qf) {
-    float l = l_run[qf];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / lsum[qf][0];
     const int qi = q0w + qf * 16 + lr;
     if (qi < Tq) {
       T* dst = out + ((size_t)b * Tq + qi) * D + h * HS;

@@ -29,9 +29,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-// Two floats -> packed pair of bf16 (lo in bits 0..15).
+// Two floats -> packed pair of bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_vec_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_vec_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_vec_t{lo, hi}, bf16x2_vec_t));
 }
 
 // Element traits: loading/storing groups of 4 elements as fp32.
