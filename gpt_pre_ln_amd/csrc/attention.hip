@@ -24,14 +24,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // max over the lanes l, l^16, l^32, l^48 (the four lane groups holding one
-// query of an MFMA fragment), with the gfx950 row-swap permutes.
+// query of an MFMA fragment).
 __device__ __forceinline__ float max_over_lane_groups(float v) {
-  const unsigned u = __builtin_bit_cast(unsigned, v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = fmaxf(__builtin_bit_cast(float, r16[0]), __builtin_bit_cast(float, r16[1]));
-  const unsigned w = __builtin_bit_cast(unsigned, v);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__builtin_bit_cast(float, r32[0]), __builtin_bit_cast(float, r32[1]));
+  const auto mx = [](float a, float b) { return fmaxf(a, b); };
+  return combine_xor32(combine_xor16(v, mx), mx);
 }
 
 template <int CH>

@@ -99,16 +99,46 @@ template <> struct Mma<float> {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Wave-wide reductions without LDS round trips: DPP exchanges inside each
+// 16-lane row (quad swaps, then half-row and row mirrors), then the gfx950
+// row-swap permutes across rows.  Every step combines a lane with a partner
+// that combines the same two values, so all 64 lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-
+// op over the lanes l and l ^ 16 (rows 0/1 and 2/3 of the wave exchanged).
+// The two results of a swap are copied to plain scalars before any bit cast
+// (bit-casting an element of the returned pair in place reads element 0).
+template <class Op>
+__device__ __forceinline__ float combine_xor16(float v, Op op) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+// op over the lanes l and l ^ 32 (the two halves of the wave exchanged).
+template <class Op>
+__device__ __forceinline__ float combine_xor32(float v, Op op) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_f32<0x141>(v));  // row_half_mirror: the other quad of the 8
+  v = op(v, dpp_f32<0x140>(v));  // row_mirror: the other 8 of the 16
+  v = combine_xor16(v, op);
+  return combine_xor32(v, op);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // exp(x) through the hardware base-2 exponential.

@@ -28,51 +28,55 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   }
 }
 
-template <typename T>
+// One wave per row; lane holds float4 groups c = lane*4 + i*256.  NV > 0:
+// exactly NV groups per lane (d_model = 256*NV, no bounds tests); NV == 0:
+// up to kMaxV4 groups with tests.  Two passes over the registers: mean, then
+// the variance of the centred values.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
                                                          const float* __restrict__ beta, T* __restrict__ y,
                                                          float* __restrict__ y32, int M, int D, float eps) {
+  constexpr int NMAX = NV > 0 ? NV : kMaxV4;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const float* xr = x + (size_t)row * D;
-  float4 v[kMaxV4];
+  auto valid = [&](int i) { return NV > 0 || lane * 4 + i * 256 < D; };
+  float4 v[NMAX], gv[NMAX], bv[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      v[i] = *reinterpret_cast<const float4*>(xr + lane * 4 + i * 256);
+      gv[i] = *reinterpret_cast<const float4*>(gamma + lane * 4 + i * 256);
+      bv[i] = *reinterpret_cast<const float4*>(beta + lane * 4 + i * 256);
+    }
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxV4; ++i) {
-    const int c = lane * 4 + i * 256;
-    if (c < D) {
-      v[i] = *reinterpret_cast<const float4*>(xr + c);
-      sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-    }
-  }
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float mean = wave_sum(sum) / (float)D;
   float sq = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxV4; ++i) {
-    const int c = lane * 4 + i * 256;
-    if (c < D) {
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
       v[i].x -= mean;
       v[i].y -= mean;
       v[i].z -= mean;
       v[i].w -= mean;
       sq += (v[i].x * v[i].x + v[i].y * v[i].y) + (v[i].z * v[i].z + v[i].w * v[i].w);
     }
-  }
   const float var = wave_sum(sq) / (float)D;
   const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-  for (int i = 0; i < kMaxV4; ++i) {
-    const int c = lane * 4 + i * 256;
-    if (c < D) {
-      const float4 g = *reinterpret_cast<const float4*>(gamma + c);
-      const float4 b = *reinterpret_cast<const float4*>(beta + c);
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      const int c = lane * 4 + i * 256;
+      const float4 g = gv[i], b = bv[i];
       const float o0 = v[i].x * rstd * g.x + b.x, o1 = v[i].y * rstd * g.y + b.y;
       const float o2 = v[i].z * rstd * g.z + b.z, o3 = v[i].w * rstd * g.w + b.w;
       Elem<T>::store4(y + (size_t)row * D + c, o0, o1, o2, o3);
       if (y32) *reinterpret_cast<float4*>(y32 + (size_t)row * D + c) = make_float4(o0, o1, o2, o3);
     }
-  }
 }
 
 // 32x32 tile transpose through LDS; 256 threads = 32 x 8.
@@ -113,8 +117,17 @@ template <typename T>
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32, int M, int D,
                             float eps, hipStream_t stream) {
   if (D > 256 * kMaxV4 || D % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(layernorm_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, x, gamma, beta, y, y32, M, D,
-                     eps);
+  const dim3 grid((M + 3) / 4), block(256);
+  switch (D) {
+    case 768:
+      hipLaunchKernelGGL((layernorm_kernel<T, 3>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+      break;
+    case 1024:
+      hipLaunchKernelGGL((layernorm_kernel<T, 4>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+      break;
+    default:
+      hipLaunchKernelGGL((layernorm_kernel<T, 0>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+  }
   return hipGetLastError();
 }
 
