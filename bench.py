@@ -3,8 +3,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one full forward (embedding, every block, final LayerNorm, tied
-lm_head writing fp32 logits) of the workload's batch, from token ids already
-resident in HBM to logits in HBM.  Prints one JSON line.
+lm_head writing the logits) of the workload's batch, from token ids already
+resident in HBM to logits in HBM.  Prints one JSON line.  The logits are
+stored in the model's arithmetic dtype (bf16 for the bf16 workloads, as a
+bf16 GPT2LMHeadModel returns them); --logits-dtype f32 stores fp32 logits,
+and for a bf16 run the line also carries the fp32-logits throughput.
 
 Default workload: GPT-2 small shape, bf16 matrices / fp32 accumulation,
 B=8, T=1024 (synthetic ids and random-init weights of that architecture).
@@ -126,6 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-small-b8t1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--logits-dtype", choices=["f32", "bf16"], default=None,
+                    help="element type of the logits (default: the workload's arithmetic dtype)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one device-to-device copy of 1 GiB (a plain copy kernel of known size, "
                          "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -157,11 +162,12 @@ def main():
         del src, dst
 
     B, T = w.batch, w.seq_len
-    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T)
-    model.load_blob(W.make_params(w))
+    logits_dtype = args.logits_dtype or w.dtype
+    blob = W.make_params(w)
+    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
+    model.load_blob(blob)
     ids = torch.from_numpy(W.make_ids(w)).to(dev)
-    logits = torch.empty((B, T, w.shape.vocab), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    logits = torch.empty((B, T, w.shape.vocab), dtype=model.logits_torch_dtype, device=dev)
 
     def step():
         model.forward(ids, out_logits=logits)
@@ -210,6 +216,24 @@ def main():
     roof["avg_launch_ms"] = round(dom_ms / max(dom_n, 1), 5)
     roof["launches_timed"] = dom_n
 
+    # the same forward storing fp32 logits (reported beside the headline value)
+    alt = None
+    if logits_dtype != "f32":
+        del logits
+        model32 = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype="f32")
+        model32.load_blob(blob)
+        logits32 = torch.empty((B, T, w.shape.vocab), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            model32.forward(ids, out_logits=logits32)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            model32.forward(ids, out_logits=logits32)
+        torch.cuda.synchronize()
+        el32 = (time.perf_counter() - t1) / args.steps
+        alt = {"value": round(B * T / el32, 1), "ms_per_step": round(el32 * 1e3, 4)}
+        del model32, logits32
+
     out = {
         "metric": "forward tokens/s and % bf16 MFMA peak, GPT-2 small B=8 T=1024, 1 GPU",
         "value": round(tokens_per_s, 1),
@@ -224,12 +248,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "d_model": w.shape.d_model,
-                   "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": w.shape.vocab},
+                   "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": w.shape.vocab,
+                   "logits_dtype": logits_dtype},
         "frac_of_peak": round(flops / (elapsed / args.steps) / (peak * 1e12), 4),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "roofline": roof,
         "per_class_ms": {c: round(v["ms_per_step"], 4) for c, v in per_class.items()},
     }
+    if alt is not None:
+        out["fp32_logits"] = alt
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
@@ -242,13 +269,14 @@ def bench_decode(args, w):
 
     dev = torch.device("cuda:0")
     B, P = w.batch, w.seq_len
-    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=P + 1)
+    logits_dtype = args.logits_dtype or w.dtype
+    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=P + 1, logits_dtype=logits_dtype)
     model.load_blob(W.make_params(w))
     prefix, new = W.make_decode_ids(w)
     kv = model.new_kv_cache(B, P + 1)
     model.forward(torch.from_numpy(prefix).to(dev), logits=False, kv=kv)
     new_d = torch.from_numpy(new).to(dev)
-    logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device=dev)
+    logits = torch.empty((B, w.shape.vocab), dtype=model.logits_torch_dtype, device=dev)
 
     def step():
         kv.view.past_len = P          # re-run the same step: position P, cache slot P
@@ -266,13 +294,13 @@ def bench_decode(args, w):
     D, F, L, V = s.d_model, s.d_ff, s.n_layer, s.vocab
     weights = 2 * (L * (3 * D * D + D * D + 2 * D * F) + V * D)
     kv_bytes = 2 * L * 2 * B * (P + 1) * D
-    logit_bytes = 4 * B * V
+    logit_bytes = (2 if logits_dtype == "bf16" else 4) * B * V
     total = weights + kv_bytes + logit_bytes
     gbs = total / dt / 1e9
     out = {"metric": "decode tokens/s (GPT-2 small, B=32, cached prefix 1023)", "value": round(B / dt, 1),
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "batch": B, "prefix": P},
+           "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "batch": B, "prefix": P, "logits_dtype": logits_dtype},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                         "kernel": "whole decode step", "algorithmic_bytes": total}}

@@ -35,7 +35,7 @@ class gpt2_config(ctypes.Structure):
     _fields_ = [("vocab_size", ctypes.c_int32), ("n_positions", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("n_head", ctypes.c_int32),
                 ("n_layer", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("logits_dtype", ctypes.c_int32)]
 
 
 class gpt2_kv_view(ctypes.Structure):
@@ -98,9 +98,16 @@ def _check(status: int, where: str):
         raise GPT2Error(status, where)
 
 
-def make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps=1e-5, dtype="bf16"):
-    dt = {"f32": GPT2_F32, "bf16": GPT2_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
-    return gpt2_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dt)
+def _dtype_code(dtype) -> int:
+    return {"f32": GPT2_F32, "bf16": GPT2_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps=1e-5, dtype="bf16",
+                logits_dtype=None):
+    """logits_dtype defaults to the arithmetic dtype (bf16 logits for a bf16 model)."""
+    dt = _dtype_code(dtype)
+    ldt = dt if logits_dtype is None else _dtype_code(logits_dtype)
+    return gpt2_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dt, ldt)
 
 
 # ------------------------------------------------------------ thin wrappers

@@ -137,26 +137,32 @@ struct EpiGelu {
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
-// fp32 logits rows of ldo floats (ldo = vocabulary size, so rows are only
-// 4-byte aligned): each 4-column group goes out as one unaligned 16-byte
-// store, masked per element at the vocabulary edge.
+// Logits rows of ldo elements (ldo = vocabulary size, so rows are only
+// element-aligned), fp32 or bf16 (O): each 4-column group goes out as one
+// unaligned 16- or 8-byte store, masked per element at the vocabulary edge.
 typedef float f32x4_u4_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_u2_t __attribute__((ext_vector_type(2), aligned(2)));
+template <typename O>
 struct EpiLogits {
   static constexpr bool kPreload = false, kBias = false, kTransposed = false;
-  float* out;   // [M][ldo], only columns n < n_valid are written
+  O* out;       // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
   __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
-    float* p = out + (size_t)m * ldo + n;
+    O* p = out + (size_t)m * ldo + n;
     if (n + 3 < n_valid) {
-      *reinterpret_cast<f32x4_u4_t*>(p) = v;
+      if constexpr (sizeof(O) == 4) {
+        *reinterpret_cast<f32x4_u4_t*>(p) = v;
+      } else {
+        *reinterpret_cast<u32x2_u2_t*>(p) = u32x2_u2_t{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (n + e < n_valid) p[e] = v[e];
+        if (n + e < n_valid) p[e] = Elem<O>::from_f32(v[e]);
     }
   }
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}

@@ -353,10 +353,12 @@ hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int l
 GPT2_INSTANTIATE_GEMM(float, EpiQKV<float>)
 GPT2_INSTANTIATE_GEMM(float, EpiResidual)
 GPT2_INSTANTIATE_GEMM(float, EpiGelu<float>)
-GPT2_INSTANTIATE_GEMM(float, EpiLogits)
+GPT2_INSTANTIATE_GEMM(float, EpiLogits<float>)
+GPT2_INSTANTIATE_GEMM(float, EpiLogits<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiQKV<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
-GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits)
+GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
+GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
 
 }  // namespace gpt2

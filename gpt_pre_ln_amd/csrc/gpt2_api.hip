@@ -45,6 +45,7 @@ gpt2_status check_config(const gpt2_config* c) {
       c->d_ff < 1)
     return GPT2_ERR_SHAPE;
   if (c->dtype != GPT2_F32 && c->dtype != GPT2_BF16) return GPT2_ERR_UNSUPPORTED;
+  if (c->logits_dtype != GPT2_F32 && c->logits_dtype != GPT2_BF16) return GPT2_ERR_UNSUPPORTED;
   if (!(c->ln_eps >= 0.f) || !std::isfinite(c->ln_eps)) return GPT2_ERR_INVALID_ARG;
   if (c->d_model % c->n_head != 0) return GPT2_ERR_SHAPE;
   const int hs = c->d_model / c->n_head;
@@ -225,10 +226,24 @@ hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& ep
   return launch_gemm<T>(pick_tile(M, N), A, Bw, M, N, K, K, K, epi, st);
 }
 
+// lm_head: logits = h @ wte^T (tied, no bias), stored as cfg.logits_dtype.
+template <typename T>
+hipError_t launch_lm_head(gpt2_model* m, const T* h, void* logits, int M, hipStream_t st) {
+  const gpt2_config& c = m->cfg;
+  const int V = c.vocab_size, D = c.d_model;
+  const GemmTile tile = pick_tile(M, vocab_pad(c));
+  if (c.logits_dtype == GPT2_BF16) {
+    EpiLogits<bf16_t> e{static_cast<bf16_t*>(logits), V, V};
+    return launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st);
+  }
+  EpiLogits<float> e{static_cast<float*>(logits), V, V};
+  return launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st);
+}
+
 // ------------------------------------------------------------------ forward
 
 template <typename T>
-gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, float* logits, float* hidden,
+gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, void* logits, float* hidden,
                         gpt2_kv_view* kv, hipStream_t st) {
   const gpt2_config& c = m->cfg;
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
@@ -302,16 +317,14 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
   }
   if (logits) {
     TimedScope ts(m, kLMHead, st);
-    EpiLogits e{logits, V, V};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
-             "lm_head");
+    GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
   }
   if (kv) kv->past_len = T_seq;
   return GPT2_OK;
 }
 
 template <typename T>
-gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, float* logits, hipStream_t st) {
+gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, hipStream_t st) {
   const gpt2_config& c = m->cfg;
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
   const int B = kv->B, M = B, pos = kv->past_len;
@@ -353,11 +366,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, f
     }
   }
   GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st), "ln_f");
-  {
-    EpiLogits e{logits, V, V};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
-             "lm_head");
-  }
+  GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
   kv->past_len = pos + 1;
   return GPT2_OK;
 }
@@ -487,11 +496,12 @@ gpt2_status gpt2_init_params(gpt2_model* m, const float* d_blob, size_t n, void*
   return m->cfg.dtype == GPT2_BF16 ? run_init<bf16_t>(m, d_blob, st) : run_init<float>(m, d_blob, st);
 }
 
-gpt2_status gpt2_forward(gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, float* logits, float* hidden,
+gpt2_status gpt2_forward(gpt2_model* m, const int32_t* tokens, int32_t B, int32_t T, void* logits, float* hidden,
                          gpt2_kv_view* kv, void* stream) {
   if (!m || !tokens) return GPT2_ERR_INVALID_ARG;
   if (B < 1 || T < 1 || T > m->cfg.n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
-  if (!aligned(tokens, 4) || (logits && !aligned(logits, 4)) || (hidden && !aligned(hidden, 16)))
+  const size_t lsz = m->cfg.logits_dtype == GPT2_BF16 ? 2 : 4;
+  if (!aligned(tokens, 4) || (logits && !aligned(logits, lsz)) || (hidden && !aligned(hidden, 16)))
     return GPT2_ERR_INVALID_ARG;
   if (ws_layout(m->cfg, B, T).total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
   if (kv) {
@@ -504,9 +514,10 @@ gpt2_status gpt2_forward(gpt2_model* m, const int32_t* tokens, int32_t B, int32_
                                    : run_forward<float>(m, tokens, B, T, logits, hidden, kv, st);
 }
 
-gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, float* logits, void* stream) {
+gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, void* stream) {
   if (!m || !kv || !tokens || !logits || !kv->d_kv) return GPT2_ERR_INVALID_ARG;
-  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(logits, 4)) return GPT2_ERR_INVALID_ARG;
+  const size_t lsz = m->cfg.logits_dtype == GPT2_BF16 ? 2 : 4;
+  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(logits, lsz)) return GPT2_ERR_INVALID_ARG;
   if (kv->B < 1 || kv->max_T < 1 || kv->max_T > m->cfg.n_positions) return GPT2_ERR_SHAPE;
   if (kv->past_len < 0) return GPT2_ERR_SHAPE;
   if (kv->past_len >= kv->max_T) return GPT2_ERR_CAPACITY;

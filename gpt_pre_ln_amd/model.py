@@ -26,10 +26,13 @@ class KVCache:
 
 class GPT2:
     def __init__(self, vocab_size, n_positions, d_model, n_head, n_layer, d_ff, dtype="bf16",
-                 max_batch=1, max_seq=None, ln_eps=1e-5, device="cuda:0"):
+                 max_batch=1, max_seq=None, ln_eps=1e-5, device="cuda:0", logits_dtype=None):
+        """logits_dtype: "f32" or "bf16" element type of the logits (default: dtype)."""
         self.device = torch.device(device)
-        self.cfg = B.make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dtype)
+        self.cfg = B.make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dtype,
+                                 logits_dtype)
         self.dtype = dtype
+        self.logits_torch_dtype = torch.bfloat16 if self.cfg.logits_dtype == B.GPT2_BF16 else torch.float32
         max_seq = max_seq or n_positions
         self.param_bytes = B.gpt2_param_bytes(self.cfg)
         self.ws_bytes = max(B.gpt2_workspace_bytes(self.cfg, max_batch, max_seq),
@@ -38,6 +41,7 @@ class GPT2:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.handle = B.gpt2_create(self.cfg, self.params.data_ptr(), self.param_bytes,
                                     self.ws.data_ptr(), self.ws_bytes)
+        self._destroy = B.load().gpt2_destroy  # held so that teardown at interpreter exit still works
 
     @classmethod
     def from_shape(cls, shape, dtype, **kw):
@@ -46,8 +50,9 @@ class GPT2:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None:
-            B.gpt2_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and destroy is not None:
+            destroy(h)
             self.handle = None
 
     @property
@@ -67,15 +72,24 @@ class GPT2:
         torch.cuda.current_stream(self.device).synchronize()
         del d_blob
 
+    def _logits_out(self, shape, out):
+        if out is None:
+            return torch.empty(shape, dtype=self.logits_torch_dtype, device=self.device)
+        if out.dtype != self.logits_torch_dtype or tuple(out.shape) != tuple(shape) or not out.is_contiguous() \
+                or out.device != self.device:
+            raise ValueError(f"out_logits must be a contiguous {self.logits_torch_dtype} tensor of shape {shape} "
+                             f"on {self.device}")
+        return out
+
     def forward(self, ids: torch.Tensor, logits: bool = True, hidden: bool = False, kv: KVCache | None = None,
                 out_logits: torch.Tensor | None = None):
-        """ids: int32 [B, T] on the device. Returns (logits [B,T,V] fp32 | None, hidden [B,T,D] | None)."""
+        """ids: int32 [B, T] on the device.
+        Returns (logits [B,T,V] of logits_dtype | None, hidden [B,T,D] fp32 | None)."""
         assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.device == self.device
         Bsz, T = ids.shape
         lg = None
         if logits:
-            lg = out_logits if out_logits is not None else torch.empty(
-                (Bsz, T, self.cfg.vocab_size), dtype=torch.float32, device=self.device)
+            lg = self._logits_out((Bsz, T, self.cfg.vocab_size), out_logits)
         hd = torch.empty((Bsz, T, self.cfg.d_model), dtype=torch.float32, device=self.device) if hidden else None
         B.gpt2_forward(self.handle, ids.data_ptr(), Bsz, T, lg.data_ptr() if lg is not None else None,
                        hd.data_ptr() if hd is not None else None, kv.view if kv is not None else None,
@@ -86,10 +100,9 @@ class GPT2:
         return KVCache(self.cfg, batch, max_T, self.device)
 
     def decode_step(self, kv: KVCache, new_ids: torch.Tensor, out_logits: torch.Tensor | None = None):
-        """new_ids: int32 [B] on the device. Returns logits [B, V] fp32."""
+        """new_ids: int32 [B] on the device. Returns logits [B, V] of logits_dtype."""
         assert new_ids.dtype == torch.int32 and new_ids.is_contiguous()
-        lg = out_logits if out_logits is not None else torch.empty(
-            (kv.view.B, self.cfg.vocab_size), dtype=torch.float32, device=self.device)
+        lg = self._logits_out((kv.view.B, self.cfg.vocab_size), out_logits)
         B.gpt2_decode_step(self.handle, kv.view, new_ids.data_ptr(), lg.data_ptr(), self.stream)
         return lg
 

@@ -50,14 +50,17 @@ typedef enum {
 typedef enum { GPT2_F32 = 0, GPT2_BF16 = 1 } gpt2_dtype;
 
 /* Model hyper-parameters, the GPT2Config fields of pwwt.cn section GPT2Config.
- * Supported: d_model % 64 == 0, d_model % n_head == 0, head_dim = d_model/n_head
- * in {16, 32, 64} (16 and 32 with GPT2_F32 only), d_ff % 64 == 0,
- * n_positions <= 4096.
+ * Supported: d_model % 64 == 0, d_model <= 2048, d_model % n_head == 0,
+ * head_dim = d_model/n_head in {16, 64} (16 with GPT2_F32 only),
+ * d_ff % 64 == 0, n_positions <= 4096, vocab_size <= 2^24.
  * dtype GPT2_F32: every kernel computes and stores in fp32.
  * dtype GPT2_BF16: matrices, wte and wpe are held in bf16 (round to nearest
  * even from the fp32 blob), biases and LayerNorm parameters in fp32; matrix
  * products take bf16 operands with fp32 accumulation; the residual stream,
- * LayerNorm statistics, softmax and GELU are fp32; logits are fp32. */
+ * LayerNorm statistics, softmax and GELU are fp32.
+ * logits_dtype: element type of the logits the forward and decode calls write
+ * (GPT2_F32 or GPT2_BF16; the lm_head accumulates in fp32 either way and
+ * GPT2_BF16 rounds each logit to nearest even on the store). */
 typedef struct {
   int32_t vocab_size;
   int32_t n_positions;
@@ -66,7 +69,8 @@ typedef struct {
   int32_t n_layer;
   int32_t d_ff;
   float ln_eps;
-  int32_t dtype; /* gpt2_dtype */
+  int32_t dtype;        /* gpt2_dtype of the arithmetic */
+  int32_t logits_dtype; /* gpt2_dtype of d_logits */
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_model;
@@ -117,21 +121,21 @@ gpt2_status gpt2_init_params(gpt2_model* model, const float* d_blob, size_t n_fl
 
 /* Full forward of B sequences of T tokens (1 <= T <= n_positions).
  *   d_tokens: int32 [B, T] token ids.
- *   d_logits: fp32 [B, T, vocab_size] or NULL (skip the lm_head).
+ *   d_logits: [B, T, vocab_size] of cfg.logits_dtype, or NULL (skip the lm_head).
  *   d_hidden: fp32 [B, T, d_model] output of the final LayerNorm, or NULL.
  *   kv:       NULL, or a cache view with kv->B == B and kv->max_T >= T: keys and
  *             values of positions [0, T) are written into it and kv->past_len
  *             is set to T (prefill).
  * The workspace must hold gpt2_workspace_bytes(cfg, B, T). */
 gpt2_status gpt2_forward(gpt2_model* model, const int32_t* d_tokens, int32_t B, int32_t T,
-                         float* d_logits, float* d_hidden, gpt2_kv_view* kv, void* stream);
+                         void* d_logits, float* d_hidden, gpt2_kv_view* kv, void* stream);
 
 /* One decode step: one new token per sequence at position kv->past_len.
- *   d_new_tokens: int32 [kv->B]; d_logits: fp32 [kv->B, vocab_size].
+ *   d_new_tokens: int32 [kv->B]; d_logits: [kv->B, vocab_size] of cfg.logits_dtype.
  * Requires kv->past_len < kv->max_T (else GPT2_ERR_CAPACITY).  Appends the new
  * keys/values to the cache and increments kv->past_len (host side, at enqueue). */
 gpt2_status gpt2_decode_step(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_new_tokens,
-                             float* d_logits, void* stream);
+                             void* d_logits, void* stream);
 
 /* Optional per-layer trace for debugging: when d_trace is non-NULL, the next
  * gpt2_forward calls copy the residual stream after every block (X_{l+1},

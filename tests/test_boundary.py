@@ -74,17 +74,24 @@ def test_kv_cache_bytes(B):
     (dict(d_model=100, n_head=3), "GPT2_ERR_SHAPE"),             # not divisible
     (dict(d_model=64, n_head=4), "GPT2_ERR_UNSUPPORTED"),        # head_dim 16 in bf16
     (dict(dtype=7), "GPT2_ERR_UNSUPPORTED"),
+    (dict(logits_dtype=3), "GPT2_ERR_UNSUPPORTED"),
     (dict(n_layer=0), "GPT2_ERR_SHAPE"),
     (dict(d_ff=100), "GPT2_ERR_UNSUPPORTED"),
     (dict(n_positions=5000), "GPT2_ERR_UNSUPPORTED"),
 ])
 def test_config_validation(B, change, status):
     base = dict(vocab_size=1000, n_positions=128, d_model=128, n_head=2, n_layer=2, d_ff=512, ln_eps=1e-5,
-                dtype=B.GPT2_BF16)
+                dtype=B.GPT2_BF16, logits_dtype=B.GPT2_BF16)
     base.update(change)
     cfg = B.gpt2_config(**base)
     n = ctypes.c_size_t()
     assert B.load().gpt2_param_bytes(ctypes.byref(cfg), ctypes.byref(n)) == getattr(B, status)
+
+
+def test_logits_dtype_defaults_to_the_arithmetic_dtype(B):
+    assert B.make_config(512, 64, 64, 4, 2, 256, 1e-5, "f32").logits_dtype == B.GPT2_F32
+    assert B.make_config(512, 64, 64, 2, 2, 256, 1e-5, "bf16").logits_dtype == B.GPT2_BF16
+    assert B.make_config(512, 64, 64, 2, 2, 256, 1e-5, "bf16", "f32").logits_dtype == B.GPT2_F32
 
 
 def test_fp32_head_dim_16_is_supported(B):
@@ -128,6 +135,7 @@ def test_forward_host_checks(B, handle):
     assert fwd(FAKE, 0, 8) == B.GPT2_ERR_SHAPE
     assert fwd(FAKE, 4, 64) == B.GPT2_ERR_WORKSPACE        # workspace sized for (2, 64)
     assert fwd(FAKE + 2, 1, 8) == B.GPT2_ERR_INVALID_ARG   # misaligned ids
+    assert fwd(FAKE, 1, 8, lg=FAKE + 1) == B.GPT2_ERR_INVALID_ARG  # bf16 logits need 2-byte alignment
     assert fwd(FAKE, 1, 8, hid=FAKE + 4) == B.GPT2_ERR_INVALID_ARG
     kv = B.gpt2_kv_view(FAKE, 2, 32, 0)
     assert fwd(FAKE, 1, 8, kv=kv) == B.GPT2_ERR_SHAPE      # kv.B != B

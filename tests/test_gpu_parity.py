@@ -59,7 +59,7 @@ def test_tiny_fp32_full_logits():
     torch.cuda.synchronize()
     P = oracle.prepare_params(blob, w.shape, w.dtype)
     ref = oracle.forward(P, ids)
-    assert_logits(lg.cpu().numpy(), ref, "f32", w.name)
+    assert_logits(lg.float().cpu().numpy(), ref, "f32", w.name)
     ref_h = np.stack([oracle.forward_hidden(P, ids[b]) for b in range(w.batch)])
     assert normwise(hid.cpu().numpy(), ref_h) <= TOL_F32
 
@@ -103,7 +103,7 @@ def test_ragged_shapes_logits_hidden_trace(case):
         e = normwise(trace_np[l], ref_l)
         assert e <= tol, f"layer {l} residual stream normwise {e:.3e}"
     assert normwise(hid.cpu().numpy(), ref_h) <= tol
-    assert_logits(lg.cpu().numpy(), ref, dtype, f"ragged {case}")
+    assert_logits(lg.float().cpu().numpy(), ref, dtype, f"ragged {case}")
 
 
 # ------------------------------------------------------------ invariants on GPU
@@ -116,11 +116,11 @@ def test_causality_bitwise_gpu(dtype):
     blob = W.make_params(s, _init_small(0.08), 5)
     ids = np.random.default_rng(6).integers(0, 600, size=(2, 300)).astype(np.int32)
     m = _model(s, dtype, 2, 300, blob)
-    base = m.forward(_ids_dev(ids))[0].cpu().numpy()
+    base = m.forward(_ids_dev(ids))[0].float().cpu().numpy()
     for t in (0, 63, 127, 128, 298):
         ids2 = ids.copy()
         ids2[:, t + 1] = (ids2[:, t + 1] + 7) % 600
-        out = m.forward(_ids_dev(ids2))[0].cpu().numpy()
+        out = m.forward(_ids_dev(ids2))[0].float().cpu().numpy()
         np.testing.assert_array_equal(out[:, :t + 1], base[:, :t + 1])
         assert not np.array_equal(out[:, t + 1], base[:, t + 1])
 
@@ -137,11 +137,60 @@ def test_identity_blocks_gpu(dtype):
             view[f"h.{l}.{k}"][...] = 0.0
     ids = np.random.default_rng(9).integers(0, 900, size=(2, 100)).astype(np.int32)
     m = _model(s, dtype, 2, 100, blob)
-    lg = m.forward(_ids_dev(ids))[0].cpu().numpy()
+    lg = m.forward(_ids_dev(ids))[0].float().cpu().numpy()
     P = oracle.prepare_params(blob, s, dtype)
     x0 = P["wte"][ids] + P["wpe"][:100]
     expect = oracle.layer_norm(x0, P["ln_f.w"], P["ln_f.b"]) @ P["wte"].T
     assert_logits(lg, expect, dtype, "identity")
+
+
+def test_sharp_attention_scores():
+    """Attention scores spread over hundreds of natural-log units within a row.
+
+    The online softmax must take every exponential against a maximum shared by
+    all lanes holding a query: a maximum taken over a subset of the keys leaves
+    exp() arguments far above 88 and the output overflows.  fp32, exact parity.
+    """
+    _announce("sharp attention f32")
+    s = W.ModelShape(vocab=512, n_positions=256, d_model=128, n_head=2, n_layer=2, d_ff=512)
+    blob = W.make_params(s, _init_small(0.08), 15)
+    view = W.unpack(blob, s)
+    for l in range(s.n_layer):
+        view[f"h.{l}.attn.c_attn.w"][...] *= 6.5
+    ids = np.random.default_rng(16).integers(0, 512, size=(2, 200)).astype(np.int32)
+    P = oracle.prepare_params(blob, s, "f32")
+    tr = {}
+    ref_h = np.stack([oracle.forward_hidden(P, ids[b], trace=tr) for b in range(2)])
+    # the case is only meaningful if the scores really are that spread out
+    h0 = tr["attn_norm"][0]
+    qkv = h0 @ P["h.0.attn.c_attn.w"] + P["h.0.attn.c_attn.b"]
+    q, k = qkv[:, :64], qkv[:, 128:192]
+    sc = (q @ k.T) / 8.0
+    spread = max(np.ptp(sc[i, :i + 1]) for i in range(1, 200))
+    assert spread > 200.0, f"score spread only {spread:.1f}"
+    m = _model(s, "f32", 2, 200, blob)
+    lg = m.forward(_ids_dev(ids))[0].float().cpu().numpy()
+    assert_logits(lg, np.einsum("btd,vd->btv", ref_h, P["wte"]), "f32", "sharp attention")
+
+
+def test_fp32_logits_from_bf16_model():
+    """logits_dtype f32 on a bf16 model: the same lm_head products, stored unrounded."""
+    _announce("bf16 model, fp32 logits")
+    from gpt_pre_ln_amd.model import GPT2
+    s = W.ModelShape(vocab=1001, n_positions=256, d_model=128, n_head=2, n_layer=2, d_ff=512)
+    blob = W.make_params(s, _init_small(0.08), 17)
+    ids = np.random.default_rng(18).integers(0, 1001, size=(2, 150)).astype(np.int32)
+    m32 = GPT2.from_shape(s, "bf16", max_batch=2, max_seq=150, logits_dtype="f32")
+    m32.load_blob(blob)
+    m16 = _model(s, "bf16", 2, 150, blob)
+    lg32 = m32.forward(_ids_dev(ids))[0]
+    lg16 = m16.forward(_ids_dev(ids))[0]
+    assert lg32.dtype == torch.float32 and lg16.dtype == torch.bfloat16
+    # the bf16 logits are the fp32 ones rounded to nearest even
+    np.testing.assert_array_equal(lg32.to(torch.bfloat16).float().cpu().numpy(), lg16.float().cpu().numpy())
+    P = oracle.prepare_params(blob, s, "bf16")
+    ref = oracle.forward(P, ids)
+    assert_logits(lg32.cpu().numpy(), ref, "bf16", "fp32 logits")
 
 
 def test_batch_independence_gpu():
@@ -150,9 +199,9 @@ def test_batch_independence_gpu():
     blob = W.make_params(s, _init_small(0.08), 10)
     ids = np.random.default_rng(11).integers(0, 500, size=(4, 150)).astype(np.int32)
     m = _model(s, "bf16", 4, 150, blob)
-    base = m.forward(_ids_dev(ids))[0].cpu().numpy()
+    base = m.forward(_ids_dev(ids))[0].float().cpu().numpy()
     perm = [3, 1, 0, 2]
-    out = m.forward(_ids_dev(ids[perm]))[0].cpu().numpy()
+    out = m.forward(_ids_dev(ids[perm]))[0].float().cpu().numpy()
     np.testing.assert_array_equal(out, base[perm])
 
 
@@ -176,7 +225,7 @@ def test_decode_small_shapes(dtype):
     P = oracle.prepare_params(blob, s, dtype)
     ref_all = oracle.forward(P, ids)
     for i in range(steps):
-        lg = m.decode_step(kv, _ids_dev(ids[:, Pn + i])).cpu().numpy()
+        lg = m.decode_step(kv, _ids_dev(ids[:, Pn + i])).float().cpu().numpy()
         assert kv.past_len == Pn + i + 1
         assert_logits(lg, ref_all[:, Pn + i], dtype, f"decode step {i}")
 
@@ -208,7 +257,7 @@ def test_gpt2_small_b8t1024():
     # sequences are independent: the oracle runs sequences 0 and 7 in full
     for b in (0, 7):
         ref = oracle.forward(P, ids[b:b + 1])[0]
-        assert_logits(lg[b].cpu().numpy(), ref, w.dtype, f"{w.name} seq {b}")
+        assert_logits(lg[b].float().cpu().numpy(), ref, w.dtype, f"{w.name} seq {b}")
 
 
 def test_gpt2_small_decode_b32p1023():
@@ -219,10 +268,10 @@ def test_gpt2_small_decode_b32p1023():
     m = _model(w.shape, w.dtype, w.batch, w.seq_len + 1, blob)
     kv = m.new_kv_cache(w.batch, w.seq_len + 1)
     m.forward(_ids_dev(prefix), logits=False, kv=kv)
-    lg = m.decode_step(kv, _ids_dev(new)).cpu().numpy()
+    lg = m.decode_step(kv, _ids_dev(new)).float().cpu().numpy()
     # the GPU's own full forward over prefix ++ new, last row, for every sequence
     full = np.concatenate([prefix, new[:, None]], axis=1).astype(np.int32)
-    lg_full = m.forward(_ids_dev(full))[0][:, -1].cpu().numpy()
+    lg_full = m.forward(_ids_dev(full))[0][:, -1].float().cpu().numpy()
     assert normwise(lg, lg_full) <= TOL_BF16
     P = oracle.prepare_params(blob, w.shape, w.dtype)
     sel = [0, 31]
@@ -242,7 +291,7 @@ def test_large_workloads(name, prefix):
     m = _model(w.shape, w.dtype, w.batch, w.seq_len, blob)
     lg = m.forward(_ids_dev(ids))[0]
     torch.cuda.synchronize()
-    got = lg[0, :prefix].cpu().numpy()
+    got = lg[0, :prefix].float().cpu().numpy()
     del lg, m
     P = oracle.prepare_params(blob, w.shape, w.dtype)
     del blob
