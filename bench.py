@@ -68,11 +68,11 @@ def class_work(shape, B, T, cls):
 
 
 # kernel class -> kernel name as rocprofv3 reports it (short form)
-TRAFFIC_KERNELS = {"lm_head_gemm": "gemm_kernel<bf16_t, 256, 256, 2, 4, 2, 4, EpiLogits>",
+TRAFFIC_KERNELS = {"lm_head_gemm": "gemm_kernel<bf16_t, 256, 256, 2, 4, 2, 4, EpiLogits<bf16_t> >",
                    "fc_gemm": "gemm_kernel<bf16_t, 128, 128, 2, 2, 2, 3, EpiGelu<bf16_t> >",
                    "qkv_gemm": "gemm_kernel<bf16_t, 128, 128, 2, 2, 2, 3, EpiQKV<bf16_t> >",
                    "attention": "attn_prefill_kernel<bf16_t, 64>",
-                   "layernorm": "layernorm_kernel<bf16_t>"}
+                   "layernorm": "layernorm_kernel<bf16_t, 3>"}
 
 
 def measured_traffic(workload, cls):
