@@ -15,6 +15,10 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
 // y[m, :] = gamma * (x - mean) / sqrt(var + eps) + beta over D (biased
 // variance, two passes over the row held in registers); optional fp32 copy.
 // russellluo.com "Hidden State 如何流过 GPT-2 Block", Pre-Norm; dpshk.com 3.2.
+// Read `bytes` (a multiple of 16, 16-byte aligned) and discard them, so that a
+// following kernel finds the data in the caches.
+hipError_t launch_touch(const void* p, size_t bytes, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32,
                             int M, int D, float eps, hipStream_t stream);

@@ -3,6 +3,8 @@
 // wavefront reductions (mean, then the centred sum of squares) with no LDS.
 #include "rowops.h"
 
+#include <algorithm>
+
 namespace gpt2 {
 
 namespace {
@@ -110,6 +112,23 @@ template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq, int pos0, int D,
                         hipStream_t stream) {
   hipLaunchKernelGGL(embed_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D);
+  return hipGetLastError();
+}
+
+// Reads `n16` 16-byte chunks and discards them: brings a weight matrix into the
+// caches (memory-side cache and L2) ahead of the GEMM that streams it.
+__global__ __launch_bounds__(256) void touch_kernel(const u32x4_t* __restrict__ p, size_t n16) {
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) acc ^= p[i];
+  asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));  // keep the loads
+}
+
+hipError_t launch_touch(const void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 2048);
+  hipLaunchKernelGGL(touch_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const u32x4_t*>(p),
+                     n16);
   return hipGetLastError();
 }
 
