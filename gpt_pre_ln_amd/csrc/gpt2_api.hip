@@ -226,14 +226,16 @@ hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& ep
   return launch_gemm<T>(pick_tile(M, N), A, Bw, M, N, K, K, K, epi, st);
 }
 
-// Weight prefetch.  Inside a forward a layer's weight matrices have dropped
+// Weight read-ahead.  Inside a forward a layer's weight matrices have dropped
 // out of the caches by the time they are used again (the activations stream
-// several hundred MB between two uses), and a GEMM that meets its weights
-// cold reads them from every XCD at once.  Reading the matrix once just
-// before the GEMM (a plain read kernel on the same stream) is cheaper than
-// that cold start: -0.45 ms on a GPT-2 small B=8 T=1024 forward.  Running the
-// reads on a second stream, overlapped with the kernel before the GEMM, was
-// measured too and lost to the contention it causes in that kernel.
+// several hundred MB between two uses), and a GEMM that meets its weights cold
+// reads them from all eight XCDs at once: the qkv GEMM of GPT-2 small at B=8
+// T=1024 takes 59 us cold against 47 us after one plain read of its weights.
+// The LayerNorm before each pair of GEMMs therefore also reads their weights
+// (it is bound by HBM and a few MB more cost it ~2 us).  Measured
+// alternatives: a separate read kernel before each GEMM (0.08 ms slower per
+// forward) and reads on a second stream overlapping the preceding kernel
+// (slower still: they contend with it).
 // lm_head: logits = h @ wte^T (tied, no bias), stored as cfg.logits_dtype.
 template <typename T>
 hipError_t launch_lm_head(gpt2_model* m, const T* h, void* logits, int M, hipStream_t st) {
@@ -265,8 +267,13 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
   float* skinny = reinterpret_cast<float*>(m->ws + W.skinny);
   const int kvT = kv ? kv_stride(kv->max_T) : kv_stride(T_seq);
   const float q_scale = 1.0f / std::sqrt((float)hs);
-  // Weight prefetch before each tiled GEMM (the skinny ones read each weight once anyway).
-  auto pre_w = [&](const T* w, size_t elems) { return M > 32 ? launch_touch(w, elems * sizeof(T), st) : hipSuccess; };
+  // Weight read-ahead for the tiled GEMMs (the skinny ones read each weight once
+  // anyway): ln_1 reads c_attn.w .. attn.c_proj.w, ln_2 mlp.c_fc.w .. mlp.c_proj.w
+  // (adjacent in the parameter region), in bytes rounded down to 16.
+  const bool pre = M > 32;
+  auto span = [&](size_t first, size_t last, size_t last_elems) {
+    return ((last + last_elems * sizeof(T)) - first) / 16 * 16;
+  };
 
   {
     TimedScope ts(m, kEmbed, st);
@@ -286,11 +293,12 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kLN, st);
-      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st,
+                                   pre ? m->params + o.w_qkv : nullptr, span(o.w_qkv, o.w_o, (size_t)D * D)),
+               "ln_1");
     }
     {
       TimedScope ts(m, kQKV, st);
-      GPT2_HIP(pre_w(pp<T>(m, o.w_qkv), (size_t)3 * D * D), "prefetch c_attn.w");
       EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, skinny, st), "c_attn");
     }
@@ -300,23 +308,22 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kOProj, st);
-      GPT2_HIP(pre_w(pp<T>(m, o.w_o), (size_t)D * D), "prefetch attn.c_proj.w");
       EpiResidual e{pf(m, o.b_o), x, D};
       GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, skinny, st), "attn.c_proj");
     }
     {
       TimedScope ts(m, kLN, st);
-      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st), "ln_2");
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st,
+                                   pre ? m->params + o.w_fc : nullptr, span(o.w_fc, o.w_pr, (size_t)D * F)),
+               "ln_2");
     }
     {
       TimedScope ts(m, kFC, st);
-      GPT2_HIP(pre_w(pp<T>(m, o.w_fc), (size_t)F * D), "prefetch mlp.c_fc.w");
       EpiGelu<T> e{pf(m, o.b_fc), u, F};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, skinny, st), "c_fc");
     }
     {
       TimedScope ts(m, kMLPProj, st);
-      GPT2_HIP(pre_w(pp<T>(m, o.w_pr), (size_t)D * F), "prefetch mlp.c_proj.w");
       EpiResidual e{pf(m, o.b_pr), x, D};
       GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, skinny, st), "mlp.c_proj");
     }

@@ -15,13 +15,13 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
 // y[m, :] = gamma * (x - mean) / sqrt(var + eps) + beta over D (biased
 // variance, two passes over the row held in registers); optional fp32 copy.
 // russellluo.com "Hidden State 如何流过 GPT-2 Block", Pre-Norm; dpshk.com 3.2.
-// Read `bytes` (a multiple of 16, 16-byte aligned) and discard them, so that a
-// following kernel finds the data in the caches.
-hipError_t launch_touch(const void* p, size_t bytes, hipStream_t stream);
-
+// prefetch / prefetch_bytes (optional; 16-byte aligned, a multiple of 16): a
+// region the kernel also reads and discards, so that the GEMMs that follow
+// find their weights in the caches.
 template <typename T>
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32,
-                            int M, int D, float eps, hipStream_t stream);
+                            int M, int D, float eps, hipStream_t stream, const void* prefetch = nullptr,
+                            size_t prefetch_bytes = 0);
 
 // dst[n][k] = convert(src[k][n]) for a [K][N] fp32 source (Conv1D [in, out]
 // -> [out, in]); dst rows N..N_pad-1 are zero-filled.

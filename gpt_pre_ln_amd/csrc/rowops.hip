@@ -37,8 +37,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
                                                          const float* __restrict__ beta, T* __restrict__ y,
-                                                         float* __restrict__ y32, int M, int D, float eps) {
+                                                         float* __restrict__ y32, int M, int D, float eps,
+                                                         const u32x4_t* __restrict__ pf, size_t pf16) {
   constexpr int NMAX = NV > 0 ? NV : kMaxV4;
+  // Optional read-ahead of the next GEMMs' weights (pf16 16-byte chunks),
+  // spread over the grid; the values are discarded.
+  if (pf16) {
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < pf16; i += (size_t)gridDim.x * 256) acc ^= pf[i];
+    asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
+  }
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -115,37 +123,25 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
   return hipGetLastError();
 }
 
-// Reads `n16` 16-byte chunks and discards them: brings a weight matrix into the
-// caches (memory-side cache and L2) ahead of the GEMM that streams it.
-__global__ __launch_bounds__(256) void touch_kernel(const u32x4_t* __restrict__ p, size_t n16) {
-  u32x4_t acc = {0u, 0u, 0u, 0u};
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) acc ^= p[i];
-  asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));  // keep the loads
-}
-
-hipError_t launch_touch(const void* p, size_t bytes, hipStream_t stream) {
-  const size_t n16 = bytes / 16;
-  if (n16 == 0) return hipSuccess;
-  const size_t blocks = std::min<size_t>((n16 + 255) / 256, 2048);
-  hipLaunchKernelGGL(touch_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const u32x4_t*>(p),
-                     n16);
-  return hipGetLastError();
-}
-
 template <typename T>
 hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32, int M, int D,
-                            float eps, hipStream_t stream) {
+                            float eps, hipStream_t stream, const void* prefetch, size_t prefetch_bytes) {
   if (D > 256 * kMaxV4 || D % 4 != 0) return hipErrorInvalidValue;
   const dim3 grid((M + 3) / 4), block(256);
+  const u32x4_t* pf = static_cast<const u32x4_t*>(prefetch);
+  const size_t pf16 = prefetch ? prefetch_bytes / 16 : 0;
   switch (D) {
     case 768:
-      hipLaunchKernelGGL((layernorm_kernel<T, 3>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+      hipLaunchKernelGGL((layernorm_kernel<T, 3>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps, pf,
+                         pf16);
       break;
     case 1024:
-      hipLaunchKernelGGL((layernorm_kernel<T, 4>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+      hipLaunchKernelGGL((layernorm_kernel<T, 4>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps, pf,
+                         pf16);
       break;
     default:
-      hipLaunchKernelGGL((layernorm_kernel<T, 0>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps);
+      hipLaunchKernelGGL((layernorm_kernel<T, 0>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D, eps, pf,
+                         pf16);
   }
   return hipGetLastError();
 }
@@ -169,7 +165,7 @@ hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipS
 #define GPT2_ROWOPS(T)                                                                                          \
   template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, hipStream_t); \
   template hipError_t launch_layernorm<T>(const float*, const float*, const float*, T*, float*, int, int, float,    \
-                                          hipStream_t);                                                             \
+                                          hipStream_t, const void*, size_t);                                        \
   template hipError_t launch_transpose_convert<T>(const float*, T*, int, int, int, hipStream_t);                   \
   template hipError_t launch_convert<T>(const float*, T*, size_t, size_t, hipStream_t);
 
