@@ -29,8 +29,9 @@ HIP_FLAGS = [
 
 # Per-source extras.  attention.hip: keep MFMA accumulators in ordinary VGPRs
 # (the softmax rescales them every tile; in AGPRs each rescale is a round trip
-# of v_accvgpr_read / v_accvgpr_write).
-SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# of v_accvgpr_read / v_accvgpr_write), and let max() skip NaN canonicalisation
+# (no NaN reaches it; masked scores are -inf, which stays allowed).
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -112,25 +112,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   // chunk slot s of row r holds the row's global chunk swz_ch(r, s) (the XOR
   // swizzle is an involution).  Keys past the end are clamped to the last
   // valid one for K (their scores are masked) and fixed up for V^T below.
+  // Per-thread source offsets within a tile (bytes), fixed over the tiles:
+  // K row key_of_row(row), swizzled chunk; V^T row d, swizzled chunk.
+  int koff[KI], krow[KI], voff[VI], vcol[VI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int ci = (j * NW + wave) * 64 + lane;
+    const int row = ci / KCH, slot = ci % KCH;
+    krow[j] = key_of_row(row);
+    koff[j] = krow[j] * KROWB + swz_ch<KCH>(row, slot) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int ci = (j * NW + wave) * 64 + lane;
+    const int d = ci / VCH, slot = ci % VCH;
+    vcol[j] = swz_ch<VCH>(d, slot) * EPC;
+    voff[j] = d * kvT * ESZ + vcol[j] * ESZ;
+  }
   auto issue = [&](int kt, int buf) {
+    const char* kt_base = reinterpret_cast<const char*>(kb + (size_t)kt * BKEYS * HS);
+    const char* vt_base = reinterpret_cast<const char*>(vb + (size_t)kt * BKEYS);
+    const bool tail = (kt + 1) * BKEYS > nkeys;  // block-uniform
 #pragma unroll
     for (int j = 0; j < KI; ++j) {
-      const int ci = (j * NW + wave) * 64 + lane;
-      const int row = ci / KCH, slot = ci % KCH;
-      const int key = min(kt * BKEYS + key_of_row(row), nkeys - 1);
-      const char* src = reinterpret_cast<const char*>(kb + (size_t)key * HS) + swz_ch<KCH>(row, slot) * 16;
+      const char* src = kt_base + koff[j];
+      if (tail && kt * BKEYS + krow[j] >= nkeys)  // past the last key: read the last valid row (masked)
+        src += (nkeys - 1 - kt * BKEYS - krow[j]) * KROWB;
       __builtin_amdgcn_global_load_lds((const void*)src,
                                        (__attribute__((address_space(3))) void*)&sK[buf][(j * NW + wave) * 64], 16,
                                        0, 0);
     }
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
-      const int ci = (j * NW + wave) * 64 + lane;
-      const int d = ci / VCH, slot = ci % VCH;
+      const char* src = vt_base + voff[j];
       // chunks wholly past the end read the tile's first chunk instead (in bounds; zeroed below)
-      int c = swz_ch<VCH>(d, slot);
-      if (kt * BKEYS + c * EPC >= nkeys) c = 0;
-      const T* src = vb + (size_t)d * kvT + kt * BKEYS + c * EPC;
+      if (tail && kt * BKEYS + vcol[j] >= nkeys) src -= vcol[j] * ESZ;
       __builtin_amdgcn_global_load_lds((const void*)src,
                                        (__attribute__((address_space(3))) void*)&sV[buf][(j * NW + wave) * 64], 16,
                                        0, 0);

@@ -177,11 +177,10 @@ template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,
                        const Epi& epi, hipStream_t stream);
 
-// M <= 32 (decode): split-K partial products into `part` (at least
-// skinny_partials_floats(M, N, K) floats), then a reduce that applies `epi`.
-size_t skinny_partials_floats(int M, int N, int K);
+// M <= 32 (decode): one kernel for the product and the fused epilogue `epi`;
+// K % 32 == 0 (bf16) or K % 16 == 0 (fp32), no workspace.
 template <typename T, class Epi>
 hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
-                              float* part, hipStream_t stream);
+                              hipStream_t stream);
 
 }  // namespace gpt2

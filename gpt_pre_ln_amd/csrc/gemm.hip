@@ -252,59 +252,55 @@ hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int
 
 // ------------------------------------------------------------------ skinny
 // GEMMs with at most 32 rows (the decode step: one row per sequence) are
-// bound by streaming B once.  The work is split over (64-column block,
-// 256-element k split); each wave reads its 16 B rows and both 16-row A
-// fragments straight from global memory (no LDS: nothing is shared), and
-// writes fp32 partial sums.  A second kernel adds the splits and applies the
-// same fused epilogue as the tiled kernel.
-constexpr int kSkinnyK = 256;
-
-template <typename T>
-__global__ __launch_bounds__(256) void gemm_skinny_partial_kernel(const T* __restrict__ A, const T* __restrict__ B,
-                                                                   float* __restrict__ part, int M, int N, int K,
-                                                                   int lda, int ldb) {
+// bound by streaming B once and by the fixed cost of each launch.  One kernel
+// does the whole product and its epilogue: a block owns 16 columns; its NWS
+// waves take the 32-element (bf16) or 16-element (fp32) k steps round-robin,
+// reading their 16 B rows and both 16-row A fragments straight from global
+// memory (nothing is shared, so nothing is staged), then the block adds the
+// wave results in LDS and wave 0 applies the fused epilogue.  N/16 blocks of
+// up to 16 waves keep the whole weight matrix in flight.
+template <typename T, int NWS, class Epi>
+__global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restrict__ A, const T* __restrict__ B, int M,
+                                                                int N, int K, int lda, int ldb, Epi epi) {
   constexpr int SLAB = Mma<T>::kPerSlab;  // k elements per 16-byte-per-lane fragment step
+  __shared__ f32x4_t red[NWS][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const int s = blockIdx.y;
-  const int k0 = s * kSkinnyK, k1 = min(k0 + kSkinnyK, K);
+  const int n0 = blockIdx.x * 16;
   const T* brow = B + (size_t)min(n0 + lr, N - 1) * ldb;
   const T* arow0 = A + (size_t)min(lr, M - 1) * lda;
   const T* arow1 = A + (size_t)min(16 + lr, M - 1) * lda;
   const int lofs = lg * (16 / (int)sizeof(T));
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int k = k0; k < k1; k += SLAB) {
+  for (int k = wave * SLAB; k < K; k += NWS * SLAB) {
     const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + k + lofs);
     const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(arow0 + k + lofs);
     const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(arow1 + k + lofs);
     Mma<T>::run(acc0, b, a0);
     Mma<T>::run(acc1, b, a1);
   }
+  red[wave][0][lane] = acc0;
+  red[wave][1][lane] = acc1;
+  __syncthreads();
+  if (wave != 0) return;
+  acc0 = red[0][0][lane];
+  acc1 = red[0][1][lane];
+#pragma unroll
+  for (int w = 1; w < NWS; ++w) {
+    acc0 += red[w][0][lane];
+    acc1 += red[w][1][lane];
+  }
   // lane holds C[m][n0 + 4*lg .. +3] for m = lr (acc0) and 16 + lr (acc1)
   const int n = n0 + lg * 4;
-  if (n < N) {
-    if (lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + lr) * N + n) = acc0;
-    if (16 + lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + 16 + lr) * N + n) = acc1;
-  }
-}
-
-template <class Epi>
-__global__ __launch_bounds__(256) void gemm_skinny_reduce_kernel(const float* __restrict__ part, int S, int M,
-                                                                  int N, Epi epi) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int n4 = N / 4;
-  if (idx >= M * n4) return;
-  const int m = idx / n4, n = (idx - m * n4) * 4;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) acc += *reinterpret_cast<const f32x4_t*>(part + ((size_t)s * M + m) * N + n);
-  const float4 pre = Epi::kPreload ? epi.preload(m, n) : float4{};
+  if (n >= N) return;
   if constexpr (Epi::kBias) {
     const float4 b = epi.bias4(n);
-    acc += f32x4_t{b.x, b.y, b.z, b.w};
+    acc0 += f32x4_t{b.x, b.y, b.z, b.w};
+    acc1 += f32x4_t{b.x, b.y, b.z, b.w};
   }
-  epi.apply(m, n, acc, pre);
+  if (lr < M) epi.apply(lr, n, acc0, Epi::kPreload ? epi.preload(lr, n) : float4{});
+  if (16 + lr < M) epi.apply(16 + lr, n, acc1, Epi::kPreload ? epi.preload(16 + lr, n) : float4{});
 }
 
 }  // namespace
@@ -325,29 +321,22 @@ hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int 
   }
 }
 
-size_t skinny_partials_floats(int M, int N, int K) {
-  return (size_t)((K + kSkinnyK - 1) / kSkinnyK) * M * N;
-}
-
 template <typename T, class Epi>
 hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
-                              float* part, hipStream_t stream) {
+                              hipStream_t stream) {
   if (M > 32 || M < 1) return hipErrorInvalidValue;
-  const int S = (K + kSkinnyK - 1) / kSkinnyK;
-  hipLaunchKernelGGL(gemm_skinny_partial_kernel<T>, dim3((N + 63) / 64, S), dim3(256), 0, stream, A, B, part, M, N,
-                     K, lda, ldb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int total = M * (N / 4);
-  hipLaunchKernelGGL(gemm_skinny_reduce_kernel<Epi>, dim3((total + 255) / 256), dim3(256), 0, stream, part, S, M, N,
-                     epi);
+  const dim3 grid((N + 15) / 16);
+  if (K >= 2048)
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, 16, Epi>), grid, dim3(1024), 0, stream, A, B, M, N, K, lda, ldb, epi);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, 8, Epi>), grid, dim3(512), 0, stream, A, B, M, N, K, lda, ldb, epi);
   return hipGetLastError();
 }
 
 #define GPT2_INSTANTIATE_GEMM(T, EPI)                                                               \
   template hipError_t launch_gemm<T, EPI>(GemmTile, const T*, const T*, int, int, int, int, int, \
                                           const EPI&, hipStream_t);                                      \
-  template hipError_t launch_gemm_skinny<T, EPI>(const T*, const T*, int, int, int, int, int, const EPI&, float*, \
+  template hipError_t launch_gemm_skinny<T, EPI>(const T*, const T*, int, int, int, int, int, const EPI&,         \
                                                  hipStream_t);
 
 GPT2_INSTANTIATE_GEMM(float, EpiQKV<float>)

@@ -110,7 +110,7 @@ size_t blob_floats(const gpt2_config& c) {
 }
 
 struct WsLayout {
-  size_t x, h, q, k, vt, a, u, part, skinny, total;
+  size_t x, h, q, k, vt, a, u, part, total;
 };
 
 WsLayout ws_layout(const gpt2_config& c, int B, int T) {
@@ -132,13 +132,6 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   W.a = take(M * D * es);
   W.u = take(M * F * es);
   W.part = take(decode_partials_floats(B, c.n_head, hs) * 4);
-  // split-K partials of the skinny GEMMs (used when B*T <= 32)
-  const int Ms = (int)std::min<size_t>(M, 32);
-  const size_t sk = std::max({skinny_partials_floats(Ms, 3 * c.d_model, c.d_model),
-                              skinny_partials_floats(Ms, c.d_model, c.d_model),
-                              skinny_partials_floats(Ms, c.d_ff, c.d_model),
-                              skinny_partials_floats(Ms, c.d_model, c.d_ff)});
-  W.skinny = take(sk * 4);
   W.total = off;
   return W;
 }
@@ -218,11 +211,11 @@ GemmTile pick_tile(int M, int N) {
   return kTile128x128;
 }
 
-// Block projections: the skinny split-K path for at most 32 rows, the tiled
+// Block projections: the one-kernel skinny path for at most 32 rows, the tiled
 // MFMA kernel otherwise.
 template <typename T, class Epi>
-hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& epi, float* skinny, hipStream_t st) {
-  if (M <= 32) return launch_gemm_skinny<T>(A, Bw, M, N, K, K, K, epi, skinny, st);
+hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& epi, hipStream_t st) {
+  if (M <= 32) return launch_gemm_skinny<T>(A, Bw, M, N, K, K, K, epi, st);
   return launch_gemm<T>(pick_tile(M, N), A, Bw, M, N, K, K, K, epi, st);
 }
 
@@ -264,7 +257,6 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
   T* q = reinterpret_cast<T*>(m->ws + W.q);
   T* a = reinterpret_cast<T*>(m->ws + W.a);
   T* u = reinterpret_cast<T*>(m->ws + W.u);
-  float* skinny = reinterpret_cast<float*>(m->ws + W.skinny);
   const int kvT = kv ? kv_stride(kv->max_T) : kv_stride(T_seq);
   const float q_scale = 1.0f / std::sqrt((float)hs);
   // Weight read-ahead for the tiled GEMMs (the skinny ones read each weight once
@@ -300,7 +292,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     {
       TimedScope ts(m, kQKV, st);
       EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale, M};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, skinny, st), "c_attn");
+      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     {
       TimedScope ts(m, kAttn, st);
@@ -309,7 +301,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     {
       TimedScope ts(m, kOProj, st);
       EpiResidual e{pf(m, o.b_o), x, D};
-      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, skinny, st), "attn.c_proj");
+      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
     }
     {
       TimedScope ts(m, kLN, st);
@@ -320,12 +312,12 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     {
       TimedScope ts(m, kFC, st);
       EpiGelu<T> e{pf(m, o.b_fc), u, F};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, skinny, st), "c_fc");
+      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
     {
       TimedScope ts(m, kMLPProj, st);
       EpiResidual e{pf(m, o.b_pr), x, D};
-      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, skinny, st), "mlp.c_proj");
+      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
     }
     if (m->trace && (size_t)(l + 1) * M * D <= m->trace_floats) {
       GPT2_HIP(hipMemcpyAsync(m->trace + (size_t)l * M * D, x, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st),
@@ -356,7 +348,6 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   T* a = reinterpret_cast<T*>(m->ws + W.a);
   T* u = reinterpret_cast<T*>(m->ws + W.u);
   float* part = reinterpret_cast<float*>(m->ws + W.part);
-  float* skinny = reinterpret_cast<float*>(m->ws + W.skinny);
   const int kvT = kv_stride(kv->max_T);
   const float q_scale = 1.0f / std::sqrt((float)hs);
 
@@ -369,21 +360,21 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
     GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
     {
       EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale, M};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, skinny, st), "c_attn");
+      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
     {
       EpiResidual e{pf(m, o.b_o), x, D};
-      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, skinny, st), "attn.c_proj");
+      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
     }
     GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st), "ln_2");
     {
       EpiGelu<T> e{pf(m, o.b_fc), u, F};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, skinny, st), "c_fc");
+      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
     {
       EpiResidual e{pf(m, o.b_pr), x, D};
-      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, skinny, st), "mlp.c_proj");
+      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
     }
   }
   GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st), "ln_f");
