@@ -183,4 +183,11 @@ template <typename T, class Epi>
 hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
                               hipStream_t stream);
 
+// M <= 32, no epilogue: part[s][m][n] (s < skinny_splits(K, sizeof(T)), fp32)
+// receives the partial product of the s-th k range; the consumer adds them.
+int skinny_splits(int K, int elem_bytes);
+template <typename T>
+hipError_t launch_gemm_skinny_splitk(const T* A, const T* B, int M, int N, int K, int lda, int ldb, float* part,
+                                     hipStream_t stream);
+
 }  // namespace gpt2

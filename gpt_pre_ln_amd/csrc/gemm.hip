@@ -259,21 +259,24 @@ hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int
 // memory (nothing is shared, so nothing is staged), then the block adds the
 // wave results in LDS and wave 0 applies the fused epilogue.  N/16 blocks of
 // up to 16 waves keep the whole weight matrix in flight.
-template <typename T, int NWS, class Epi>
-__global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restrict__ A, const T* __restrict__ B, int M,
-                                                                int N, int K, int lda, int ldb, Epi epi) {
+// Shared body: waves of the block take the k steps of [k0, k1) round-robin;
+// the block sum lands in wave 0 (lane holds C[m][n0 + 4*lg .. +3] for
+// m = lr in acc0 and m = 16 + lr in acc1); returns false in the other waves.
+template <typename T, int NWS>
+__device__ __forceinline__ bool skinny_block_product(const T* __restrict__ A, const T* __restrict__ B, int M, int N,
+                                                     int lda, int ldb, int n0, int k0, int k1, f32x4_t (*red)[2][64],
+                                                     f32x4_t& acc0, f32x4_t& acc1) {
   constexpr int SLAB = Mma<T>::kPerSlab;  // k elements per 16-byte-per-lane fragment step
-  __shared__ f32x4_t red[NWS][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
   const T* brow = B + (size_t)min(n0 + lr, N - 1) * ldb;
   const T* arow0 = A + (size_t)min(lr, M - 1) * lda;
   const T* arow1 = A + (size_t)min(16 + lr, M - 1) * lda;
   const int lofs = lg * (16 / (int)sizeof(T));
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int k = wave * SLAB; k < K; k += NWS * SLAB) {
+  for (int k = k0 + wave * SLAB; k < k1; k += NWS * SLAB) {
     const u32x4_t b = *reinterpret_cast<const u32x4_t*>(brow + k + lofs);
     const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(arow0 + k + lofs);
     const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(arow1 + k + lofs);
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restri
   red[wave][0][lane] = acc0;
   red[wave][1][lane] = acc1;
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0) return false;
   acc0 = red[0][0][lane];
   acc1 = red[0][1][lane];
 #pragma unroll
@@ -291,7 +294,17 @@ __global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restri
     acc0 += red[w][0][lane];
     acc1 += red[w][1][lane];
   }
-  // lane holds C[m][n0 + 4*lg .. +3] for m = lr (acc0) and 16 + lr (acc1)
+  return true;
+}
+
+template <typename T, int NWS, class Epi>
+__global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restrict__ A, const T* __restrict__ B, int M,
+                                                                int N, int K, int lda, int ldb, Epi epi) {
+  __shared__ f32x4_t red[NWS][2][64];
+  const int n0 = blockIdx.x * 16;
+  f32x4_t acc0, acc1;
+  if (!skinny_block_product<T, NWS>(A, B, M, N, lda, ldb, n0, 0, K, red, acc0, acc1)) return;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int n = n0 + lg * 4;
   if (n >= N) return;
   if constexpr (Epi::kBias) {
@@ -301,6 +314,24 @@ __global__ __launch_bounds__(NWS * 64) void gemm_skinny_kernel(const T* __restri
   }
   if (lr < M) epi.apply(lr, n, acc0, Epi::kPreload ? epi.preload(lr, n) : float4{});
   if (16 + lr < M) epi.apply(16 + lr, n, acc1, Epi::kPreload ? epi.preload(16 + lr, n) : float4{});
+}
+
+// Split-K variant without an epilogue: block (column group, split s) writes
+// the partial product of k in [s*kchunk, (s+1)*kchunk) to part[s][m][n].
+template <typename T, int NWS>
+__global__ __launch_bounds__(NWS * 64) void gemm_skinny_split_kernel(const T* __restrict__ A, const T* __restrict__ B,
+                                                                      float* __restrict__ part, int M, int N, int K,
+                                                                      int lda, int ldb, int kchunk) {
+  __shared__ f32x4_t red[NWS][2][64];
+  const int n0 = blockIdx.x * 16, s = blockIdx.y;
+  const int k0 = s * kchunk, k1 = min(K, k0 + kchunk);
+  f32x4_t acc0, acc1;
+  if (!skinny_block_product<T, NWS>(A, B, M, N, lda, ldb, n0, k0, k1, red, acc0, acc1)) return;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int n = n0 + lg * 4;
+  if (n >= N) return;
+  if (lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + lr) * N + n) = acc0;
+  if (16 + lr < M) *reinterpret_cast<f32x4_t*>(part + ((size_t)s * M + 16 + lr) * N + n) = acc1;
 }
 
 }  // namespace
@@ -332,6 +363,26 @@ hipError_t launch_gemm_skinny(const T* A, const T* B, int M, int N, int K, int l
     hipLaunchKernelGGL((gemm_skinny_kernel<T, 8, Epi>), grid, dim3(512), 0, stream, A, B, M, N, K, lda, ldb, epi);
   return hipGetLastError();
 }
+
+int skinny_splits(int K, int elem_bytes) {
+  const int step = 8 * (elem_bytes == 2 ? Mma<bf16_t>::kPerSlab : Mma<float>::kPerSlab);
+  return (K + step - 1) / step;
+}
+
+template <typename T>
+hipError_t launch_gemm_skinny_splitk(const T* A, const T* B, int M, int N, int K, int lda, int ldb, float* part,
+                                     hipStream_t stream) {
+  if (M > 32 || M < 1) return hipErrorInvalidValue;
+  const int kchunk = 8 * Mma<T>::kPerSlab;  // one k step per wave of an 8-wave block
+  const dim3 grid((N + 15) / 16, skinny_splits(K, sizeof(T)));
+  hipLaunchKernelGGL((gemm_skinny_split_kernel<T, 8>), grid, dim3(512), 0, stream, A, B, part, M, N, K, lda, ldb,
+                     kchunk);
+  return hipGetLastError();
+}
+template hipError_t launch_gemm_skinny_splitk<float>(const float*, const float*, int, int, int, int, int, float*,
+                                                     hipStream_t);
+template hipError_t launch_gemm_skinny_splitk<bf16_t>(const bf16_t*, const bf16_t*, int, int, int, int, int, float*,
+                                                      hipStream_t);
 
 #define GPT2_INSTANTIATE_GEMM(T, EPI)                                                               \
   template hipError_t launch_gemm<T, EPI>(GemmTile, const T*, const T*, int, int, int, int, int, \

@@ -110,7 +110,7 @@ size_t blob_floats(const gpt2_config& c) {
 }
 
 struct WsLayout {
-  size_t x, h, q, k, vt, a, u, part, total;
+  size_t x, h, q, k, vt, a, u, part, rpart, total;
 };
 
 WsLayout ws_layout(const gpt2_config& c, int B, int T) {
@@ -132,6 +132,9 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   W.a = take(M * D * es);
   W.u = take(M * F * es);
   W.part = take(decode_partials_floats(B, c.n_head, hs) * 4);
+  // split-K partials of the decode step's residual projections (at most 32 rows)
+  const int ks = std::max(skinny_splits(c.d_model, (int)es), skinny_splits(c.d_ff, (int)es));
+  W.rpart = take((size_t)ks * std::min<size_t>(M, 32) * D * 4);
   W.total = off;
   return W;
 }
@@ -348,6 +351,12 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   T* a = reinterpret_cast<T*>(m->ws + W.a);
   T* u = reinterpret_cast<T*>(m->ws + W.u);
   float* part = reinterpret_cast<float*>(m->ws + W.part);
+  // The residual projections (attn.c_proj, mlp.c_proj) write split-K partial
+  // products; the LayerNorm that follows each adds them, the bias and the
+  // residual stream, writes x back and normalises: no reduce launch.
+  float* rpart = reinterpret_cast<float*>(m->ws + W.rpart);
+  const int ks_o = skinny_splits(D, sizeof(T)), ks_p = skinny_splits(F, sizeof(T));
+  const float* pending_bias = nullptr;  // mlp.c_proj bias of the previous layer, when partials are pending
   const int kvT = kv_stride(kv->max_T);
   const float q_scale = 1.0f / std::sqrt((float)hs);
 
@@ -357,27 +366,28 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
     char* base = reinterpret_cast<char*>(kv->d_kv) + (size_t)l * kv_layer_bytes(c, B, kv->max_T);
     T* kl = reinterpret_cast<T*>(base);
     T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
-    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st), "ln_1");
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
+                                 pending_bias ? rpart : nullptr, ks_p, pending_bias),
+             "ln_1");
     {
       EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
-    {
-      EpiResidual e{pf(m, o.b_o), x, D};
-      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
-    }
-    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st), "ln_2");
+    GPT2_HIP(launch_gemm_skinny_splitk<T>(a, pp<T>(m, o.w_o), M, D, D, D, D, rpart, st), "attn.c_proj");
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0, rpart,
+                                 ks_o, pf(m, o.b_o)),
+             "ln_2");
     {
       EpiGelu<T> e{pf(m, o.b_fc), u, F};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
-    {
-      EpiResidual e{pf(m, o.b_pr), x, D};
-      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
-    }
+    GPT2_HIP(launch_gemm_skinny_splitk<T>(u, pp<T>(m, o.w_pr), M, D, F, F, F, rpart, st), "mlp.c_proj");
+    pending_bias = pf(m, o.b_pr);
   }
-  GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st), "ln_f");
+  GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
+                               pending_bias ? rpart : nullptr, ks_p, pending_bias),
+           "ln_f");
   GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
   kv->past_len = pos + 1;
   return GPT2_OK;

@@ -18,10 +18,14 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
 // prefetch / prefetch_bytes (optional; 16-byte aligned, a multiple of 16): a
 // region the kernel also reads and discards, so that the GEMMs that follow
 // find their weights in the caches.
+// rpart / rks / rbias (optional): first x += (sum_{s<rks} rpart[s][row][:] +
+// rbias), the residual add of a split-K projection, written back to x (one
+// block of four waves per row; not combined with prefetch).
 template <typename T>
-hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32,
+hipError_t launch_layernorm(float* x, const float* gamma, const float* beta, T* y, float* y32,
                             int M, int D, float eps, hipStream_t stream, const void* prefetch = nullptr,
-                            size_t prefetch_bytes = 0);
+                            size_t prefetch_bytes = 0, const float* rpart = nullptr, int rks = 0,
+                            const float* rbias = nullptr);
 
 // dst[n][k] = convert(src[k][n]) for a [K][N] fp32 source (Conv1D [in, out]
 // -> [out, in]); dst rows N..N_pad-1 are zero-filled.

@@ -30,36 +30,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   }
 }
 
-// One wave per row; lane holds float4 groups c = lane*4 + i*256.  NV > 0:
-// exactly NV groups per lane (d_model = 256*NV, no bounds tests); NV == 0:
-// up to kMaxV4 groups with tests.  Two passes over the registers: mean, then
-// the variance of the centred values.
-template <typename T, int NV>
-__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
-                                                         const float* __restrict__ beta, T* __restrict__ y,
-                                                         float* __restrict__ y32, int M, int D, float eps,
-                                                         const u32x4_t* __restrict__ pf, size_t pf16) {
-  constexpr int NMAX = NV > 0 ? NV : kMaxV4;
-  // Optional read-ahead of the next GEMMs' weights (pf16 16-byte chunks),
-  // spread over the grid; the values are discarded.
-  if (pf16) {
-    u32x4_t acc = {0u, 0u, 0u, 0u};
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < pf16; i += (size_t)gridDim.x * 256) acc ^= pf[i];
-    asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
-  }
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= M) return;
-  const float* xr = x + (size_t)row * D;
+// Normalises one row held as float4 groups c = lane*4 + i*256 (v) and
+// stores it: two wave reductions (mean, then the variance of the centred
+// values), then y = (v - mean) * rstd * gamma + beta.
+template <typename T, int NV, int NMAX>
+__device__ __forceinline__ void layernorm_row(float4 (&v)[NMAX], const float4 (&gv)[NMAX], const float4 (&bv)[NMAX],
+                                              int lane, int row, int D, float eps, T* __restrict__ y,
+                                              float* __restrict__ y32) {
   auto valid = [&](int i) { return NV > 0 || lane * 4 + i * 256 < D; };
-  float4 v[NMAX], gv[NMAX], bv[NMAX];
-#pragma unroll
-  for (int i = 0; i < NMAX; ++i)
-    if (valid(i)) {
-      v[i] = *reinterpret_cast<const float4*>(xr + lane * 4 + i * 256);
-      gv[i] = *reinterpret_cast<const float4*>(gamma + lane * 4 + i * 256);
-      bv[i] = *reinterpret_cast<const float4*>(beta + lane * 4 + i * 256);
-    }
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < NMAX; ++i)
@@ -87,6 +65,103 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
       Elem<T>::store4(y + (size_t)row * D + c, o0, o1, o2, o3);
       if (y32) *reinterpret_cast<float4*>(y32 + (size_t)row * D + c) = make_float4(o0, o1, o2, o3);
     }
+}
+
+// One wave per row; lane holds float4 groups c = lane*4 + i*256.  NV > 0:
+// exactly NV groups per lane (d_model = 256*NV, no bounds tests); NV == 0:
+// up to kMaxV4 groups with tests.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                         const float* __restrict__ beta, T* __restrict__ y,
+                                                         float* __restrict__ y32, int M, int D, float eps,
+                                                         const u32x4_t* __restrict__ pf, size_t pf16) {
+  constexpr int NMAX = NV > 0 ? NV : kMaxV4;
+  // Optional read-ahead of the next GEMMs' weights (pf16 16-byte chunks),
+  // spread over the grid; the values are discarded.
+  if (pf16) {
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < pf16; i += (size_t)gridDim.x * 256) acc ^= pf[i];
+    asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
+  }
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const float* xr = x + (size_t)row * D;
+  float4 v[NMAX], gv[NMAX], bv[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (NV > 0 || lane * 4 + i * 256 < D) {
+      v[i] = *reinterpret_cast<const float4*>(xr + lane * 4 + i * 256);
+      gv[i] = *reinterpret_cast<const float4*>(gamma + lane * 4 + i * 256);
+      bv[i] = *reinterpret_cast<const float4*>(beta + lane * 4 + i * 256);
+    }
+  layernorm_row<T, NV>(v, gv, bv, lane, row, D, eps, y, y32);
+}
+
+// Residual add fused in front of the LayerNorm, for few rows: one block of
+// four waves per row.  x += (sum over s of rpart[s][row] + rbias) is written
+// back, then normalised.  Wave w sums the contiguous slices
+// [w*q, min((w+1)*q, rks)), q = ceil(rks/4), in increasing s; wave 0 adds the
+// four wave sums in order w = 0..3 (so the result does not depend on timing).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layernorm_residual_kernel(float* __restrict__ x,
+                                                                  const float* __restrict__ gamma,
+                                                                  const float* __restrict__ beta, T* __restrict__ y,
+                                                                  float* __restrict__ y32, int M, int D, float eps,
+                                                                  const float* __restrict__ rpart, int rks,
+                                                                  const float* __restrict__ rbias) {
+  constexpr int NMAX = NV > 0 ? NV : kMaxV4;
+  __shared__ float4 red[3][NMAX][64];
+  const int row = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  auto valid = [&](int i) { return NV > 0 || lane * 4 + i * 256 < D; };
+  const int q = (rks + 3) / 4;
+  const int s0 = w * q, s1 = min(s0 + q, rks);
+  const size_t sstride = (size_t)M * D;
+  const float* pr = rpart + (size_t)row * D;
+  float4 acc[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (s0 < s1) {
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i)
+      if (valid(i)) acc[i] = *reinterpret_cast<const float4*>(pr + s0 * sstride + lane * 4 + i * 256);
+    for (int s = s0 + 1; s < s1; ++s) {
+      float4 p[NMAX];
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i)
+        if (valid(i)) p[i] = *reinterpret_cast<const float4*>(pr + s * sstride + lane * 4 + i * 256);
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i)
+        if (valid(i)) acc[i] = make_float4(acc[i].x + p[i].x, acc[i].y + p[i].y, acc[i].z + p[i].z, acc[i].w + p[i].w);
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) red[w - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (w > 0) return;
+  float* xr = x + (size_t)row * D;
+  float4 v[NMAX], gv[NMAX], bv[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      const int c = lane * 4 + i * 256;
+      float4 a = acc[i];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const float4 b = red[j][i][lane];
+        a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+      }
+      const float4 rb = *reinterpret_cast<const float4*>(rbias + c);
+      const float4 x0 = *reinterpret_cast<const float4*>(xr + c);
+      v[i] = make_float4(x0.x + (a.x + rb.x), x0.y + (a.y + rb.y), x0.z + (a.z + rb.z), x0.w + (a.w + rb.w));
+      *reinterpret_cast<float4*>(xr + c) = v[i];
+      gv[i] = *reinterpret_cast<const float4*>(gamma + c);
+      bv[i] = *reinterpret_cast<const float4*>(beta + c);
+    }
+  layernorm_row<T, NV>(v, gv, bv, lane, row, D, eps, y, y32);
 }
 
 // 32x32 tile transpose through LDS; 256 threads = 32 x 8.
@@ -124,9 +199,29 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
 }
 
 template <typename T>
-hipError_t launch_layernorm(const float* x, const float* gamma, const float* beta, T* y, float* y32, int M, int D,
-                            float eps, hipStream_t stream, const void* prefetch, size_t prefetch_bytes) {
+hipError_t launch_layernorm(float* x, const float* gamma, const float* beta, T* y, float* y32, int M, int D,
+                            float eps, hipStream_t stream, const void* prefetch, size_t prefetch_bytes,
+                            const float* rpart, int rks, const float* rbias) {
   if (D > 256 * kMaxV4 || D % 4 != 0) return hipErrorInvalidValue;
+  if (M == 0) return hipSuccess;
+  if (rpart) {
+    if (rks < 1 || !rbias || prefetch) return hipErrorInvalidValue;
+    const dim3 grid(M), block(256);
+    switch (D) {
+      case 768:
+        hipLaunchKernelGGL((layernorm_residual_kernel<T, 3>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D,
+                           eps, rpart, rks, rbias);
+        break;
+      case 1024:
+        hipLaunchKernelGGL((layernorm_residual_kernel<T, 4>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D,
+                           eps, rpart, rks, rbias);
+        break;
+      default:
+        hipLaunchKernelGGL((layernorm_residual_kernel<T, 0>), grid, block, 0, stream, x, gamma, beta, y, y32, M, D,
+                           eps, rpart, rks, rbias);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((M + 3) / 4), block(256);
   const u32x4_t* pf = static_cast<const u32x4_t*>(prefetch);
   const size_t pf16 = prefetch ? prefetch_bytes / 16 : 0;
@@ -164,8 +259,8 @@ hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipS
 
 #define GPT2_ROWOPS(T)                                                                                          \
   template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, hipStream_t); \
-  template hipError_t launch_layernorm<T>(const float*, const float*, const float*, T*, float*, int, int, float,    \
-                                          hipStream_t, const void*, size_t);                                        \
+  template hipError_t launch_layernorm<T>(float*, const float*, const float*, T*, float*, int, int, float,          \
+                                          hipStream_t, const void*, size_t, const float*, int, const float*);       \
   template hipError_t launch_transpose_convert<T>(const float*, T*, int, int, int, hipStream_t);                   \
   template hipError_t launch_convert<T>(const float*, T*, size_t, size_t, hipStream_t);
 
