@@ -383,3 +383,69 @@ def test_page_shapes_small_model():
     for name in oracle.TRACE_POINTS:
         assert len(trace[name]) == 12
         assert all(list(t.shape) == g["hidden_trace"]["shape"] for t in trace[name])
+
+
+# ---------------------------------------------------------------- next-token loss
+
+
+def test_lm_loss_uniform_logits_is_log_vocab():
+    """ln_f gamma = beta = 0 makes every logit 0: each scored position costs
+    exactly log(V) and so does the mean (closed form)."""
+    s = _tiny_shape(L=2, vocab=97)
+    _, P = _random_params(s, 31)
+    P["ln_f.w"] = np.zeros_like(P["ln_f.w"])
+    P["ln_f.b"] = np.zeros_like(P["ln_f.b"])
+    ids = np.random.default_rng(32).integers(0, 97, size=(3, 11))
+    mean, per = oracle.lm_loss(P, ids)
+    assert per.shape == (3, 10)
+    np.testing.assert_allclose(per, math.log(97), rtol=1e-15, atol=0)
+    assert abs(mean - math.log(97)) <= 1e-15 * math.log(97)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lm_loss_vs_torch_cross_entropy(dtype):
+    """Library routine: torch's cross-entropy (fp64) on the logits shifted by
+    hand -- logits[:, :-1] against labels[:, 1:] -- with ignore_index -100."""
+    s = _tiny_shape(L=2, vocab=211)
+    _, P = _random_params(s, 33, dtype)
+    rng = np.random.default_rng(34)
+    ids = rng.integers(0, 211, size=(2, 17))
+    labels = rng.integers(0, 211, size=(2, 17))
+    labels[0, 5] = labels[1, 16] = -100
+    mean, per = oracle.lm_loss(P, ids, labels)
+    lg = torch.from_numpy(oracle.forward(P, ids))
+    lab = torch.from_numpy(labels.astype(np.int64))
+    ref_per = F.cross_entropy(lg[:, :-1].reshape(-1, 211), lab[:, 1:].reshape(-1), reduction="none",
+                              ignore_index=-100).reshape(2, 16).numpy()
+    ref_mean = F.cross_entropy(lg[:, :-1].reshape(-1, 211), lab[:, 1:].reshape(-1), ignore_index=-100).item()
+    np.testing.assert_allclose(per, ref_per, rtol=1e-13, atol=1e-13)
+    assert abs(mean - ref_mean) <= 1e-13 * abs(ref_mean)
+    assert per[0, 4] == 0.0 and per[1, 15] == 0.0
+    # labels default to the input ids
+    np.testing.assert_array_equal(oracle.lm_loss(P, ids)[1], oracle.lm_loss(P, ids, ids)[1])
+
+
+def test_lm_loss_shift_invariants():
+    """Position t is scored against label t+1 only: label 0 never matters, and
+    changing label t+1 changes loss t and nothing else."""
+    s = _tiny_shape(L=1, vocab=64)
+    _, P = _random_params(s, 35)
+    ids = np.random.default_rng(36).integers(0, 64, size=(1, 9))
+    _, base = oracle.lm_loss(P, ids)
+    lab = ids.copy()
+    lab[0, 0] = (lab[0, 0] + 1) % 64
+    np.testing.assert_array_equal(oracle.lm_loss(P, ids, lab)[1], base)
+    for t in (0, 3, 7):
+        lab = ids.copy()
+        lab[0, t + 1] = (lab[0, t + 1] + 5) % 64
+        _, per = oracle.lm_loss(P, ids, lab)
+        changed = np.nonzero(per[0] != base[0])[0].tolist()
+        assert changed == [t]
+
+
+def test_lm_loss_all_ignored_is_nan():
+    s = _tiny_shape(L=1, vocab=64)
+    _, P = _random_params(s, 37)
+    ids = np.random.default_rng(38).integers(0, 64, size=(2, 5))
+    mean, per = oracle.lm_loss(P, ids, np.full((2, 5), -100))
+    assert math.isnan(mean) and (per == 0).all()
