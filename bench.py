@@ -216,6 +216,20 @@ def main():
     roof["avg_launch_ms"] = round(dom_ms / max(dom_n, 1), 5)
     roof["launches_timed"] = dom_n
 
+    # forward + shifted next-token cross-entropy, logits never stored
+    # (gpt2_forward_loss; reported beside the headline value)
+    loss_mean = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        model.loss(ids, out_mean=loss_mean)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        model.loss(ids, out_mean=loss_mean)
+    torch.cuda.synchronize()
+    el_loss = (time.perf_counter() - t2) / args.steps
+    loss_step = {"value": round(B * T / el_loss, 1), "unit": "tokens/s", "ms_per_step": round(el_loss * 1e3, 4),
+                 "mean_loss": round(float(loss_mean.item()), 5)}
+
     # the same forward storing fp32 logits (reported beside the headline value)
     alt = None
     if logits_dtype != "f32":
@@ -255,6 +269,7 @@ def main():
         "roofline": roof,
         "per_class_ms": {c: round(v["ms_per_step"], 4) for c, v in per_class.items()},
     }
+    out["loss_step"] = loss_step
     if alt is not None:
         out["fp32_logits"] = alt
     if not args.no_cpu_baseline:

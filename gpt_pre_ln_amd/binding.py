@@ -68,6 +68,7 @@ _SIG = {
     "gpt2_init_params": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "gpt2_forward": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                     ctypes.POINTER(gpt2_kv_view), _P]),
+    "gpt2_forward_loss": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
     "gpt2_set_trace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "gpt2_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
@@ -155,6 +156,11 @@ def gpt2_init_params(handle, d_blob: int, n_floats: int, stream: int):
 def gpt2_forward(handle, d_tokens: int, B: int, T: int, d_logits, d_hidden, kv, stream: int):
     _check(load().gpt2_forward(handle, d_tokens, B, T, d_logits, d_hidden,
                                ctypes.byref(kv) if kv is not None else None, stream), "gpt2_forward")
+
+
+def gpt2_forward_loss(handle, d_tokens: int, d_labels, B: int, T: int, d_token_loss, d_mean_loss, stream: int):
+    _check(load().gpt2_forward_loss(handle, d_tokens, d_labels, B, T, d_token_loss, d_mean_loss, stream),
+           "gpt2_forward_loss")
 
 
 def gpt2_decode_step(handle, kv, d_new_tokens: int, d_logits: int, stream: int):

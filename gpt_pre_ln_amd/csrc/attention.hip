@@ -21,8 +21,6 @@ namespace gpt2 {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // max over the lanes l, l^16, l^32, l^48 (the four lane groups holding one
 // query of an MFMA fragment).
 __device__ __forceinline__ float max_over_lane_groups(float v) {

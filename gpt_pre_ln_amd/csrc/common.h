@@ -8,6 +8,8 @@
 
 namespace gpt2 {
 
+constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = 2^(x * log2(e))
+
 // bf16 is stored as raw 16-bit patterns; arithmetic is always fp32.
 struct bf16_t {
   uint16_t bits;
@@ -133,6 +135,17 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
   v = op(v, dpp_f32<0x140>(v));  // row_mirror: the other 8 of the 16
   v = combine_xor16(v, op);
   return combine_xor32(v, op);
+}
+// op over aligned groups of W consecutive lanes (W = 1, 2, 4, 8 or 16): the
+// DPP steps of wave_reduce; every lane of a group ends with its result.
+template <int W, class Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16, "group width");
+  if constexpr (W >= 2) v = op(v, dpp_f32<0xB1>(v));
+  if constexpr (W >= 4) v = op(v, dpp_f32<0x4E>(v));
+  if constexpr (W >= 8) v = op(v, dpp_f32<0x141>(v));
+  if constexpr (W >= 16) v = op(v, dpp_f32<0x140>(v));
+  return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
   return wave_reduce(v, [](float a, float b) { return a + b; });

@@ -42,10 +42,14 @@ namespace gpt2 {
 //                        (the residual), fetched before the group's stores;
 //   apply_t(m, n, v)     v = C[m .. m+3][n], only when kTransposed and
 //                        transposed(n) holds for the (64-aligned) column block.
+// kRowReduce epilogues (EpiCE) instead receive, per row m and per column
+// slice s of one wave's width (gemm_slice_width), the maximum and the sum of
+// exp(C - maximum) over the slice's columns below n_valid, and the single
+// entry C[m][label(m)] from the lane that holds it.
 
 template <typename T>
 struct EpiQKV {
-  static constexpr bool kPreload = false, kBias = true, kTransposed = true;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = true, kRowReduce = false;
   const float* bias;  // [3D]
   T* q;               // [B][H][Tq][hs], scaled by q_scale
   T* k;               // [B][H][kvT][hs], rows t0 + t
@@ -107,7 +111,7 @@ struct EpiQKV {
 };
 
 struct EpiResidual {
-  static constexpr bool kPreload = true, kBias = true, kTransposed = false;
+  static constexpr bool kPreload = true, kBias = true, kTransposed = false, kRowReduce = false;
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
@@ -124,7 +128,7 @@ struct EpiResidual {
 
 template <typename T>
 struct EpiGelu {
-  static constexpr bool kPreload = false, kBias = true, kTransposed = false;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
@@ -144,7 +148,7 @@ typedef float f32x4_u4_t __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_u2_t __attribute__((ext_vector_type(2), aligned(2)));
 template <typename O>
 struct EpiLogits {
-  static constexpr bool kPreload = false, kBias = false, kTransposed = false;
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false;
   O* out;       // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
@@ -168,10 +172,41 @@ struct EpiLogits {
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
+// Next-token cross-entropy partials of the tied lm_head (pwwt.cn
+// "逐行拆GPT-2源码", GPT2LMHeadModel: logits of position t are scored against
+// the label of position t + 1): the logits are reduced in registers and never
+// stored.  Row m = b*T + t of the product has label labels[m + 1] when
+// t < T - 1, none otherwise.
+struct EpiCE {
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = true;
+  float2* part;            // [M][nseg]: (max, sum of exp(C - max)) per column slice
+  int nseg;                // slices per row
+  const int32_t* labels;   // [M]
+  FastDiv T;               // positions per sequence
+  int n_valid;             // vocabulary size: columns >= n_valid are padding
+  float* tgt;              // [M]: C[m][label], written only for labels in [0, n_valid)
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int, int, const f32x4_t&, const float4&) const {}
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+  __device__ __forceinline__ int label(int m) const {
+    const int t = m - (int)T.div((uint32_t)m) * (int)T.d;
+    return t + 1 < (int)T.d ? labels[m + 1] : -1;
+  }
+  __device__ __forceinline__ void partial(int m, int s, float mx, float sum) const {
+    part[(size_t)m * nseg + s] = make_float2(mx, sum);
+  }
+  __device__ __forceinline__ void target(int m, float v) const { tgt[m] = v; }
+};
+
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),
 // K % (128 / sizeof(T)) == 0, N % 4 == 0.  `tile` picks the tile shape
 // (see gemm.hip); returns hipSuccess or the launch error.
 enum GemmTile { kTile128x128 = 0, kTile256x256 = 1, kTile64x64 = 2, kTile32x64 = 3 };
+
+// Width of the column slice one wave owns in `tile` (the kRowReduce slice).
+int gemm_slice_width(GemmTile tile);
 
 template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,

@@ -1,6 +1,8 @@
 // Matrix-core GEMM kernel (see gemm.h for the design notes).
 #include "gemm.h"
 
+#include <type_traits>
+
 namespace gpt2 {
 
 namespace {
@@ -13,6 +15,7 @@ constexpr int kGroupM = 8;
 constexpr int kPrio = 1;        // raise wave priority around each MFMA burst
 constexpr int kAllFrags = 2;    // read both slabs' fragments before the first MFMA
 constexpr int kSplitIssue = 4;  // issue the next stage's loads in two halves between slabs
+constexpr int kInterleave = 8;  // issue the second slab's fragment reads among the first slab's MFMAs
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
@@ -139,10 +142,29 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
       if (KNOB & kPrio) __builtin_amdgcn_s_setprio(0);
     };
     read_frags(0);
-    if (KNOB & kAllFrags) read_frags(1);
-    if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW / 2);
-    mfma_slab(0);
-    if (!(KNOB & kAllFrags)) read_frags(1);
+    if (KNOB & kInterleave) {
+      if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW / 2);
+      if (KNOB & kPrio) __builtin_amdgcn_s_setprio(1);
+      read_frags(1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Mma<T>::run(acc[i][j], bfr[0][j], af[0][i]);
+      // slab-0 MFMAs and slab-1 LDS reads alternate: FM*FN MFMAs over FM+FN reads
+      constexpr int NR = FM + FN, MPR = (FM * FN) / NR > 0 ? (FM * FN) / NR : 1;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+      if (KNOB & kPrio) __builtin_amdgcn_s_setprio(0);
+    } else {
+      if (KNOB & kAllFrags) read_frags(1);
+      if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW / 2);
+      mfma_slab(0);
+      if (!(KNOB & kAllFrags)) read_frags(1);
+    }
     if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, RBW / 2, RBW);
     mfma_slab(1);
   }
@@ -156,6 +178,61 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
       for (int i = 0; i < FM; ++i) acc[i][j] += f32x4_t{b.x, b.y, b.z, b.w};
     }
+  }
+
+  if constexpr (Epi::kRowReduce) {
+    // Straight from the accumulators, no staging: for fragment row i a lane
+    // holds row m = .. + i*16 + lr at columns nw + j*16 + lg*4 + e, and the
+    // four lanes lr + 16*lg (lg = 0..3) together hold the wave's WTN columns
+    // of that row.  Max, then sum of exp(C - max), over the columns below
+    // n_valid: in registers, then across those four lanes (row-swap
+    // permutes).  Slices entirely inside the vocabulary (all but the last)
+    // take the body without per-column tests; the choice is uniform over the
+    // wave.  max(a, b) is med3(a, b, +inf): one instruction.
+    auto vmax = [](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); };
+    auto vadd = [](float a, float b) { return a + b; };
+    const int nw = n0 + wn * WTN;
+    auto reduce_rows = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
+      auto ok = [&](int j, int e) { return kFull || nw + j * 16 + lg * 4 + e < epi.n_valid; };
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WTM + i * 16 + lr;
+        const int label = m < M ? epi.label(m) : -1;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ok(j, e)) mx = vmax(mx, acc[i][j][e]);
+        mx = combine_xor32(combine_xor16(mx, vmax), vmax);
+        const float b = mx * kLog2e;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ok(j, e)) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][e], kLog2e, -b));
+        s = combine_xor32(combine_xor16(s, vadd), vadd);
+        if (m < M) {
+          if (lg == 0) epi.partial(m, nw / WTN, mx, s);
+          // the label's logit, from the one lane that holds it
+          const int dl = label - nw;
+          if (dl >= 0 && dl < WTN && ((dl >> 2) & 3) == lg && label < epi.n_valid) {
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if ((dl >> 4) == j && (dl & 3) == e) t = acc[i][j][e];
+            epi.target(m, t);
+          }
+        }
+      }
+    };
+    if (nw + WTN <= epi.n_valid) reduce_rows(std::true_type{});
+    else reduce_rows(std::false_type{});
+    return;
   }
 
   // Each wave then stages its WTM x WTN sub-tile through a private slice
@@ -336,19 +413,29 @@ __global__ __launch_bounds__(NWS * 64) void gemm_skinny_split_kernel(const T* __
 
 }  // namespace
 
+int gemm_slice_width(GemmTile tile) {
+  switch (tile) {
+    case kTile256x256: return 256 / 4;
+    case kTile64x64: return 64 / 2;
+    case kTile32x64: return 64 / 2;
+    case kTile128x128:
+    default: return 128 / 2;
+  }
+}
+
 template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,
                        const Epi& epi, hipStream_t stream) {
   switch (tile) {
     case kTile256x256:
-      return launch_tile<T, 256, 256, 2, 4, 2, kSplitIssue>(A, B, M, N, K, lda, ldb, epi, stream);
+      return launch_tile<T, 256, 256, 2, 4, 2, kSplitIssue | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile64x64:
       return launch_tile<T, 64, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile32x64:
       return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x128:
     default:
-      return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kAllFrags>(A, B, M, N, K, lda, ldb, epi, stream);
+      return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
   }
 }
 
@@ -400,5 +487,9 @@ GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
+template hipError_t launch_gemm<float, EpiCE>(GemmTile, const float*, const float*, int, int, int, int, int,
+                                              const EpiCE&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiCE>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,
+                                               const EpiCE&, hipStream_t);
 
 }  // namespace gpt2

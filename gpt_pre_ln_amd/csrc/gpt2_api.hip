@@ -109,8 +109,23 @@ size_t blob_floats(const gpt2_config& c) {
   return V * D + P * D + per_layer * c.n_layer + 2 * D;
 }
 
+// Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
+// 256 CUs many times over (the lm_head); 128x128 otherwise (2 blocks per CU).
+GemmTile pick_tile(int M, int N) {
+  if (M <= 32) return kTile32x64;
+  if (M <= 64) return kTile64x64;
+  const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles256 >= 8 * 256) return kTile256x256;
+  return kTile128x128;
+}
+
 struct WsLayout {
-  size_t x, h, q, k, vt, a, u, part, rpart, total;
+  size_t x, h, q, k, vt, a, u, part, rpart;
+  // next-token loss (lm_head partials, label logits, per-position losses):
+  // placed over q .. rpart, which are dead once ln_f has run
+  size_t ce_part, ce_tgt, ce_loss;
+  int ce_nseg;
+  size_t total;
 };
 
 WsLayout ws_layout(const gpt2_config& c, int B, int T) {
@@ -135,7 +150,13 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   // split-K partials of the decode step's residual projections (at most 32 rows)
   const int ks = std::max(skinny_splits(c.d_model, (int)es), skinny_splits(c.d_ff, (int)es));
   W.rpart = take((size_t)ks * std::min<size_t>(M, 32) * D * 4);
-  W.total = off;
+  const size_t end = off;
+  off = W.q;
+  W.ce_nseg = vocab_pad(c) / gemm_slice_width(pick_tile((int)M, vocab_pad(c)));
+  W.ce_part = take(M * W.ce_nseg * sizeof(float2));
+  W.ce_tgt = take(M * 4);
+  W.ce_loss = take(M * 4);
+  W.total = std::max(end, off);
   return W;
 }
 
@@ -204,16 +225,6 @@ inline int ilog2(int v) {
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
-// 256 CUs many times over (the lm_head); 128x128 otherwise (2 blocks per CU).
-GemmTile pick_tile(int M, int N) {
-  if (M <= 32) return kTile32x64;
-  if (M <= 64) return kTile64x64;
-  const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles256 >= 8 * 256) return kTile256x256;
-  return kTile128x128;
-}
-
 // Block projections: the one-kernel skinny path for at most 32 rows, the tiled
 // MFMA kernel otherwise.
 template <typename T, class Epi>
@@ -248,9 +259,16 @@ hipError_t launch_lm_head(gpt2_model* m, const T* h, void* logits, int M, hipStr
 
 // ------------------------------------------------------------------ forward
 
+// Outputs of the next-token loss (gpt2_forward_loss).
+struct LossOut {
+  const int32_t* labels;  // [B][T]
+  float* token_loss;      // [B][T-1] or null
+  float* mean;            // [1] or null
+};
+
 template <typename T>
 gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, void* logits, float* hidden,
-                        gpt2_kv_view* kv, hipStream_t st) {
+                        gpt2_kv_view* kv, const LossOut* loss, hipStream_t st) {
   const gpt2_config& c = m->cfg;
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
   const int M = B * T_seq;
@@ -334,6 +352,21 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
   if (logits) {
     TimedScope ts(m, kLMHead, st);
     GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
+  }
+  if (loss) {
+    // lm_head with the cross-entropy epilogue: per-slice (max, sum exp) and
+    // the label logits, then one wave per position and one block for the mean
+    float2* part = reinterpret_cast<float2*>(m->ws + W.ce_part);
+    float* tgt = reinterpret_cast<float*>(m->ws + W.ce_tgt);
+    float* per = loss->token_loss ? loss->token_loss : reinterpret_cast<float*>(m->ws + W.ce_loss);
+    {
+      TimedScope ts(m, kLMHead, st);
+      const GemmTile tile = pick_tile(M, vocab_pad(c));
+      EpiCE e{part, W.ce_nseg, loss->labels, FastDiv((uint32_t)T_seq), V, tgt};
+      GPT2_HIP(launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st), "lm_head loss");
+    }
+    GPT2_HIP(launch_ce_rows(part, W.ce_nseg, tgt, loss->labels, B, T_seq, V, per, st), "loss rows");
+    if (loss->mean) GPT2_HIP(launch_ce_mean(per, loss->labels, B, T_seq, loss->mean, st), "loss mean");
   }
   if (kv) kv->past_len = T_seq;
   return GPT2_OK;
@@ -532,8 +565,22 @@ gpt2_status gpt2_forward(gpt2_model* m, const int32_t* tokens, int32_t B, int32_
     if (kv->max_T < T || kv->max_T > m->cfg.n_positions) return GPT2_ERR_CAPACITY;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return m->cfg.dtype == GPT2_BF16 ? run_forward<bf16_t>(m, tokens, B, T, logits, hidden, kv, st)
-                                   : run_forward<float>(m, tokens, B, T, logits, hidden, kv, st);
+  return m->cfg.dtype == GPT2_BF16 ? run_forward<bf16_t>(m, tokens, B, T, logits, hidden, kv, nullptr, st)
+                                   : run_forward<float>(m, tokens, B, T, logits, hidden, kv, nullptr, st);
+}
+
+gpt2_status gpt2_forward_loss(gpt2_model* m, const int32_t* tokens, const int32_t* labels, int32_t B, int32_t T,
+                              float* token_loss, float* mean_loss, void* stream) {
+  if (!m || !tokens || (!token_loss && !mean_loss)) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || T < 2 || T > m->cfg.n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
+  if (!aligned(tokens, 4) || (labels && !aligned(labels, 4)) || (token_loss && !aligned(token_loss, 4)) ||
+      (mean_loss && !aligned(mean_loss, 4)))
+    return GPT2_ERR_INVALID_ARG;
+  if (ws_layout(m->cfg, B, T).total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
+  const LossOut lo{labels ? labels : tokens, token_loss, mean_loss};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return m->cfg.dtype == GPT2_BF16 ? run_forward<bf16_t>(m, tokens, B, T, nullptr, nullptr, nullptr, &lo, st)
+                                   : run_forward<float>(m, tokens, B, T, nullptr, nullptr, nullptr, &lo, st);
 }
 
 gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, void* stream) {

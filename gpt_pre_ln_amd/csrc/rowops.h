@@ -36,4 +36,14 @@ hipError_t launch_transpose_convert(const float* src, T* dst, int K, int N, int 
 template <typename T>
 hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipStream_t stream);
 
+// Next-token cross-entropy (pwwt.cn "逐行拆GPT-2源码", GPT2LMHeadModel: logits
+// of position t scored against the label of position t + 1, mean over the
+// scored pairs).  part / nseg / tgt are the lm_head's EpiCE partials over
+// rows m = b*T + t; loss[b*(T-1) + t] receives each position's loss (0 for a
+// negative label, NaN for a label >= V).
+hipError_t launch_ce_rows(const float2* part, int nseg, const float* tgt, const int32_t* labels, int B, int T, int V,
+                          float* loss, hipStream_t stream);
+// out[0] = mean of loss over the positions whose label is >= 0 (NaN if none).
+hipError_t launch_ce_mean(const float* loss, const int32_t* labels, int B, int T, float* out, hipStream_t stream);
+
 }  // namespace gpt2

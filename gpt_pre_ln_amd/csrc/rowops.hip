@@ -189,7 +189,94 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     dst[i] = Elem<T>::from_f32(i < n ? src[i] : 0.f);
 }
 
+// Per-position next-token loss from the lm_head partials (EpiCE): one wave
+// per scored position p = b*(T-1) + t (row m = b*T + t of the product).
+// Lane l combines slices l, l+64, ... into (max, sum) online -- slices with
+// no valid column carry sum 0 and are skipped -- then the wave takes the
+// maximum M and S = sum of sum_l * exp(max_l - M):
+//   loss = M + log(S) - C[m][label]   (log-sum-exp minus the label's logit).
+// Negative labels give 0 (not scored), labels >= V give NaN.
+__global__ __launch_bounds__(256) void ce_rows_kernel(const float2* __restrict__ part, int nseg,
+                                                       const float* __restrict__ tgt,
+                                                       const int32_t* __restrict__ labels, int B, int T, int V,
+                                                       float* __restrict__ loss) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (p >= B * (T - 1)) return;
+  const int b = p / (T - 1), t = p - b * (T - 1);
+  const int m = b * T + t;
+  const int label = labels[m + 1];
+  const float2* pr = part + (size_t)m * nseg;
+  float mx = -INFINITY, s = 0.f;
+  for (int i = lane; i < nseg; i += 64) {
+    const float2 q = pr[i];
+    if (q.y > 0.f) {
+      if (q.x > mx) {
+        s = s * __builtin_amdgcn_exp2f((mx - q.x) * kLog2e) + q.y;
+        mx = q.x;
+      } else {
+        s += q.y * __builtin_amdgcn_exp2f((q.x - mx) * kLog2e);
+      }
+    }
+  }
+  const float M = wave_max(mx);
+  const float S = wave_sum(s > 0.f ? s * __builtin_amdgcn_exp2f((mx - M) * kLog2e) : 0.f);
+  if (lane == 0) {
+    float v;
+    if (label < 0) v = 0.f;
+    else if (label >= V) v = __builtin_nanf("");
+    else v = M + logf(S) - tgt[m];
+    loss[p] = v;
+  }
+}
+
+// Mean over the scored positions (labels >= 0) of loss[B*(T-1)], one block,
+// fixed summation order; NaN when nothing is scored.
+__global__ __launch_bounds__(1024) void ce_mean_kernel(const float* __restrict__ loss,
+                                                        const int32_t* __restrict__ labels, int B, int T,
+                                                        float* __restrict__ out) {
+  __shared__ float ssum[16], scnt[16];
+  const int n = B * (T - 1);
+  float s = 0.f, c = 0.f;
+  for (int p = threadIdx.x; p < n; p += 1024) {
+    const int b = p / (T - 1), t = p - b * (T - 1);
+    if (labels[b * T + t + 1] >= 0) {
+      s += loss[p];
+      c += 1.f;
+    }
+  }
+  s = wave_sum(s);
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) {
+    ssum[threadIdx.x >> 6] = s;
+    scnt[threadIdx.x >> 6] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float ts = 0.f, tc = 0.f;
+    for (int w = 0; w < 16; ++w) {
+      ts += ssum[w];
+      tc += scnt[w];
+    }
+    out[0] = ts / tc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ce_rows(const float2* part, int nseg, const float* tgt, const int32_t* labels, int B, int T, int V,
+                          float* loss, hipStream_t stream) {
+  const int n = B * (T - 1);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, stream, part, nseg, tgt, labels, B, T, V,
+                     loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_mean(const float* loss, const int32_t* labels, int B, int T, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(1024), 0, stream, loss, labels, B, T, out);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq, int pos0, int D,

@@ -96,6 +96,24 @@ class GPT2:
                        self.stream)
         return lg, hd
 
+    def loss(self, ids: torch.Tensor, labels: torch.Tensor | None = None, token_loss: bool = False,
+             out_mean: torch.Tensor | None = None):
+        """Shifted next-token cross-entropy (gpt2_forward_loss).
+
+        ids, labels: int32 [B, T] on the device (labels default to ids; negative
+        labels are not scored).  Returns (mean fp32 [1], per-position fp32
+        [B, T-1] | None).  No logits are materialised."""
+        assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.device == self.device
+        if labels is not None:
+            assert labels.dtype == torch.int32 and labels.is_contiguous() and labels.shape == ids.shape
+            assert labels.device == self.device
+        Bsz, T = ids.shape
+        mean = out_mean if out_mean is not None else torch.empty(1, dtype=torch.float32, device=self.device)
+        per = torch.empty((Bsz, T - 1), dtype=torch.float32, device=self.device) if token_loss else None
+        B.gpt2_forward_loss(self.handle, ids.data_ptr(), labels.data_ptr() if labels is not None else None, Bsz, T,
+                            per.data_ptr() if per is not None else None, mean.data_ptr(), self.stream)
+        return mean, per
+
     def new_kv_cache(self, batch: int, max_T: int) -> KVCache:
         return KVCache(self.cfg, batch, max_T, self.device)
 

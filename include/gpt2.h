@@ -130,6 +130,23 @@ gpt2_status gpt2_init_params(gpt2_model* model, const float* d_blob, size_t n_fl
 gpt2_status gpt2_forward(gpt2_model* model, const int32_t* d_tokens, int32_t B, int32_t T,
                          void* d_logits, float* d_hidden, gpt2_kv_view* kv, void* stream);
 
+/* Next-token cross-entropy of B sequences of T tokens (2 <= T <= n_positions),
+ * pwwt.cn section GPT2LMHeadModel (its second design): the logits of position
+ * t are scored against the label of position t + 1 -- the shift happens here,
+ * so labels are given per position like the tokens and NULL means "the tokens
+ * themselves" -- and the mean is taken over the scored positions.
+ *   d_labels:     int32 [B, T] or NULL.  A negative label marks a position
+ *                 that is not scored (its loss is 0 and it is left out of the
+ *                 mean); labels >= vocab_size are a caller error and give NaN.
+ *   d_token_loss: fp32 [B, T-1] (position t of sequence b at b*(T-1) + t), or NULL.
+ *   d_mean_loss:  fp32 [1], or NULL (at least one of the two outputs is required).
+ *                 NaN when no position is scored.
+ * Per position: log(sum_v exp(logit[v])) - logit[label], evaluated in fp32
+ * from the lm_head's fp32 accumulators, which never leave the chip (no logits
+ * are written).  Same workspace as gpt2_forward(B, T). */
+gpt2_status gpt2_forward_loss(gpt2_model* model, const int32_t* d_tokens, const int32_t* d_labels, int32_t B,
+                              int32_t T, float* d_token_loss, float* d_mean_loss, void* stream);
+
 /* One decode step: one new token per sequence at position kv->past_len.
  *   d_new_tokens: int32 [kv->B]; d_logits: [kv->B, vocab_size] of cfg.logits_dtype.
  * Requires kv->past_len < kv->max_T (else GPT2_ERR_CAPACITY).  Appends the new

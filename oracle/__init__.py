@@ -8,5 +8,6 @@ See ``oracle.gpt2`` for the functions and the passages each one follows.
 """
 from .gpt2 import (  # noqa: F401
     bf16_round, layer_norm, gelu_new, causal_attention, block_forward,
-    embed, forward_hidden, forward, decode_logits, lm_loss, prepare_params, TRACE_POINTS,
+    embed, forward_hidden, forward, decode_logits, shifted_cross_entropy, lm_loss, prepare_params,
+    TRACE_POINTS,
 )

@@ -233,24 +233,21 @@ def decode_logits(P: dict, prefix: np.ndarray, new_ids: np.ndarray) -> np.ndarra
     return forward(P, full, positions=[T - 1])[:, 0, :]
 
 
-def lm_loss(P: dict, ids: np.ndarray, labels: np.ndarray | None = None):
-    """Shifted next-token cross-entropy of ids [B, T] against labels [B, T].
+def shifted_cross_entropy(logits: np.ndarray, labels: np.ndarray):
+    """Next-token cross-entropy of logits [B, T, V] against labels [B, T].
 
     Returns (mean, per_position [B, T-1]).  [HFsrc] section GPT2LMHeadModel,
     its second design: the shift happens inside the model -- the logits of
     positions 0..T-2 are scored against the labels of positions 1..T-1, the
-    pairs are flattened and averaged by a cross-entropy loss -- so passing the
-    input ids as labels is the ordinary call (labels default to ids here).
-    Per position t: loss_t = log(sum_v exp(logit_t[v])) - logit_t[label_{t+1}],
-    the sum taken after subtracting the row maximum.
+    pairs are flattened and averaged by a cross-entropy loss.  Per position t:
+    loss_t = log(sum_v exp(logit_t[v])) - logit_t[label_{t+1}], the sum taken
+    after subtracting the row maximum.
     Readings: a negative label marks a position that is not scored (loss
     reported as 0, left out of the mean, as the loss's usual ignore index);
     the mean over zero scored positions is NaN.
     """
-    ids = np.atleast_2d(np.asarray(ids))
-    labels = ids if labels is None else np.atleast_2d(np.asarray(labels))
-    logits = forward(P, ids)[:, :-1, :]                      # [B, T-1, V]
-    tgt = labels[:, 1:]                                      # [B, T-1]
+    logits = np.asarray(logits, dtype=np.float64)[:, :-1, :]     # [B, T-1, V]
+    tgt = np.atleast_2d(np.asarray(labels))[:, 1:]                 # [B, T-1]
     mx = logits.max(axis=-1, keepdims=True)
     lse = mx[..., 0] + np.log(np.exp(logits - mx).sum(axis=-1))
     counted = tgt >= 0
@@ -259,3 +256,12 @@ def lm_loss(P: dict, ids: np.ndarray, labels: np.ndarray | None = None):
     n = int(counted.sum())
     mean = per.sum() / n if n else float("nan")
     return float(mean), per
+
+
+def lm_loss(P: dict, ids: np.ndarray, labels: np.ndarray | None = None):
+    """Loss of GPT2LMHeadModel called with labels ([HFsrc] GPT2LMHeadModel):
+    the forward's logits through shifted_cross_entropy; labels default to the
+    input ids, the ordinary call since the shift happens inside."""
+    ids = np.atleast_2d(np.asarray(ids))
+    labels = ids if labels is None else np.atleast_2d(np.asarray(labels))
+    return shifted_cross_entropy(forward(P, ids), labels)

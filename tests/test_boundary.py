@@ -144,6 +144,22 @@ def test_forward_host_checks(B, handle):
     assert fwd(FAKE, 2, 8, kv=kv) == B.GPT2_ERR_INVALID_ARG
 
 
+def test_forward_loss_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    loss = lambda tok, Bz, T, lab=None, per=None, mean=FAKE: lib.gpt2_forward_loss(h, tok, lab, Bz, T, per, mean, None)
+    assert loss(None, 1, 8) == B.GPT2_ERR_INVALID_ARG
+    assert loss(FAKE, 1, 8, mean=None) == B.GPT2_ERR_INVALID_ARG     # no output requested
+    assert loss(FAKE, 1, 1) == B.GPT2_ERR_SHAPE                      # T = 1: nothing to score
+    assert loss(FAKE, 1, 129) == B.GPT2_ERR_SHAPE
+    assert loss(FAKE, 0, 8) == B.GPT2_ERR_SHAPE
+    assert loss(FAKE, 4, 64) == B.GPT2_ERR_WORKSPACE                 # workspace sized for (2, 64)
+    assert loss(FAKE + 2, 1, 8) == B.GPT2_ERR_INVALID_ARG
+    assert loss(FAKE, 1, 8, lab=FAKE + 2) == B.GPT2_ERR_INVALID_ARG
+    assert loss(FAKE, 1, 8, per=FAKE + 1) == B.GPT2_ERR_INVALID_ARG
+    assert loss(FAKE, 1, 8, mean=FAKE + 1) == B.GPT2_ERR_INVALID_ARG
+
+
 def test_decode_host_checks(B, handle):
     h, cfg = handle
     lib = B.load()
