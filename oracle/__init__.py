@@ -8,6 +8,7 @@ See ``oracle.gpt2`` for the functions and the passages each one follows.
 """
 from .gpt2 import (  # noqa: F401
     bf16_round, layer_norm, gelu_new, causal_attention, block_forward,
-    embed, forward_hidden, forward, decode_logits, shifted_cross_entropy, lm_loss, prepare_params,
+    embed, forward_hidden, forward, decode_logits, shifted_cross_entropy, lm_loss, generate_greedy,
+    prepare_params,
     TRACE_POINTS,
 )

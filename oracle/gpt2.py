@@ -265,3 +265,24 @@ def lm_loss(P: dict, ids: np.ndarray, labels: np.ndarray | None = None):
     ids = np.atleast_2d(np.asarray(ids))
     labels = ids if labels is None else np.atleast_2d(np.asarray(labels))
     return shifted_cross_entropy(forward(P, ids), labels)
+
+
+def generate_greedy(P: dict, prompt: np.ndarray, n_steps: int) -> np.ndarray:
+    """Greedy continuation of prompt [B, P]: n_steps new tokens per sequence.
+
+    Token-by-token generation ([HFsrc] closing section: embeddings, positions,
+    the pre-norm stack, causal attention and generation one token at a time)
+    with the token chosen from the head's distribution ([Anatomy] architecture
+    overview: LM head, softmax over the vocabulary, pick a token).  Reading:
+    the pick is the most probable token -- the argmax of the logits, since
+    softmax is monotone -- ties to the lowest index.  Each new token is
+    appended and the next one is read off the last row of the plain forward
+    over the longer sequence (a cache would only avoid recomputation).
+    """
+    seq = np.atleast_2d(np.asarray(prompt)).copy()
+    out = np.empty((seq.shape[0], n_steps), dtype=np.int64)
+    for i in range(n_steps):
+        last = forward(P, seq, positions=[seq.shape[1] - 1])[:, 0, :]
+        out[:, i] = last.argmax(axis=-1)          # numpy: first maximum wins
+        seq = np.concatenate([seq, out[:, i:i + 1]], axis=1)
+    return out

@@ -449,3 +449,51 @@ def test_lm_loss_all_ignored_is_nan():
     ids = np.random.default_rng(38).integers(0, 64, size=(2, 5))
     mean, per = oracle.lm_loss(P, ids, np.full((2, 5), -100))
     assert math.isnan(mean) and (per == 0).all()
+
+
+# ---------------------------------------------------------------- greedy generation
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_generate_greedy_closed_form(dtype):
+    """Identity blocks (zero c_proj weights and biases), ln_f gamma 1 / beta 0,
+    one-hot token embeddings wte[v] = e_v and position embeddings
+    wpe[t] = 3 e_pi(t): the final LayerNorm keeps the order of the components,
+    so the logits of the token at position p peak at pi(p) and the greedy
+    token after position p is pi(p), whatever came before (closed form; the
+    values are exact in bf16 too)."""
+    V, D, NP = 48, 64, 32
+    s = _tiny_shape(n_head=1, d=D, L=2, vocab=V, npos=NP)
+    blob = W.make_params(s, W.Init(w_std=0.2, proj_std=0.2, bias_std=0.1, gamma=(1.0, 0.3), beta=(0.0, 0.3)), 39)
+    view = W.unpack(blob, s)
+    for l in range(s.n_layer):
+        for k in ("attn.c_proj.w", "attn.c_proj.b", "mlp.c_proj.w", "mlp.c_proj.b"):
+            view[f"h.{l}.{k}"][...] = 0.0
+    view["ln_f.w"][...] = 1.0
+    view["ln_f.b"][...] = 0.0
+    view["wte"][...] = 0.0
+    view["wte"][np.arange(V), np.arange(V)] = 1.0
+    pi = lambda t: (5 * t + 3) % V
+    view["wpe"][...] = 0.0
+    view["wpe"][np.arange(NP), [pi(t) for t in range(NP)]] = 3.0
+    P = oracle.prepare_params(blob, s, dtype)
+    prompt = np.random.default_rng(40).integers(0, V, size=(2, 7))
+    out = oracle.generate_greedy(P, prompt, 9)
+    expect = np.array([[pi(7 - 1 + i) for i in range(9)]] * 2)
+    np.testing.assert_array_equal(out, expect)
+
+
+def test_generate_greedy_vs_torch_loop():
+    """Library routine: the torch fp64 reference forward with torch.argmax
+    (first maximum) in a plain loop gives the same tokens; and the first k of
+    n generated tokens are the k-step generation."""
+    s = _tiny_shape(n_head=4, d=64, L=2, vocab=97, npos=40)
+    _, P = _random_params(s, 41)
+    prompt = np.random.default_rng(42).integers(0, 97, size=(3, 5))
+    out = oracle.generate_greedy(P, prompt, 8)
+    seq = prompt.copy()
+    for i in range(8):
+        nxt = torch.from_numpy(_torch_reference_forward(P, seq)[:, -1]).argmax(dim=-1).numpy()
+        assert (nxt == out[:, i]).all(), f"step {i}"
+        seq = np.concatenate([seq, nxt[:, None]], axis=1)
+    np.testing.assert_array_equal(oracle.generate_greedy(P, prompt, 3), out[:, :3])
