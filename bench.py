@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -305,6 +307,27 @@ def bench_decode(args, w):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    # greedy generation (gpt2_generate): the first 960 tokens as the prompt,
+    # 64 steps chained on the device (positions 959 .. 1022), no logits stored
+    gen_prompt, gen_steps = min(960, P), min(64, P + 1 - min(960, P))
+    gen_first = torch.from_numpy(np.ascontiguousarray(prefix[:, gen_prompt - 1])).to(dev)
+    gen_out = torch.empty((B, gen_steps), dtype=torch.int32, device=dev)
+
+    def gen():
+        kv.view.past_len = gen_prompt - 1
+        model.generate(kv, gen_first, gen_steps, out=gen_out)
+
+    gen()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 10)
+    t1 = time.perf_counter()
+    for _ in range(reps):
+        gen()
+    torch.cuda.synchronize()
+    gdt = (time.perf_counter() - t1) / reps
+    generate = {"value": round(B * gen_steps / gdt, 1), "unit": "tokens/s", "batch": B, "prompt": gen_prompt,
+                "steps": gen_steps, "ms_per_step": round(gdt * 1e3 / gen_steps, 4)}
+
     s = w.shape
     D, F, L, V = s.d_model, s.d_ff, s.n_layer, s.vocab
     weights = 2 * (L * (3 * D * D + D * D + 2 * D * F) + V * D)
@@ -318,7 +341,8 @@ def bench_decode(args, w):
            "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "batch": B, "prefix": P, "logits_dtype": logits_dtype},
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                        "kernel": "whole decode step", "algorithmic_bytes": total}}
+                        "kernel": "whole decode step", "algorithmic_bytes": total},
+           "generate": generate}
     print(json.dumps(out), flush=True)
 
 

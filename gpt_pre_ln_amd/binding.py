@@ -70,6 +70,7 @@ _SIG = {
                                     ctypes.POINTER(gpt2_kv_view), _P]),
     "gpt2_forward_loss": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
+    "gpt2_generate": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, ctypes.c_int32, _P, _P]),
     "gpt2_set_trace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "gpt2_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
     "gpt2_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -165,6 +166,10 @@ def gpt2_forward_loss(handle, d_tokens: int, d_labels, B: int, T: int, d_token_l
 
 def gpt2_decode_step(handle, kv, d_new_tokens: int, d_logits: int, stream: int):
     _check(load().gpt2_decode_step(handle, ctypes.byref(kv), d_new_tokens, d_logits, stream), "gpt2_decode_step")
+
+
+def gpt2_generate(handle, kv, d_tokens: int, n_steps: int, d_out_tokens: int, stream: int):
+    _check(load().gpt2_generate(handle, ctypes.byref(kv), d_tokens, n_steps, d_out_tokens, stream), "gpt2_generate")
 
 
 def gpt2_set_trace(handle, d_trace, n_floats: int):

@@ -127,6 +127,29 @@ __device__ __forceinline__ float combine_xor32(float v, Op op) {
   const unsigned r0 = r[0], r1 = r[1];
   return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
+// Arg-max pairs (v, i) over the lanes l and l ^ 16 (X = 16) or l ^ 32 (X = 32):
+// the larger v wins, equal values go to the smaller i, so both lanes of a
+// pair end with the same pair.  The same row-swap permute moves v and i.
+template <int X>
+__device__ __forceinline__ void argmax_xor(float& v, int& i) {
+  const unsigned u = __builtin_bit_cast(unsigned, v), w = (unsigned)i;
+  unsigned a0, a1, b0, b1;
+  if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    a0 = r[0], a1 = r[1], b0 = q[0], b1 = q[1];
+  } else {
+    static_assert(X == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    a0 = r[0], a1 = r[1], b0 = q[0], b1 = q[1];
+  }
+  const float v0 = __builtin_bit_cast(float, a0), v1 = __builtin_bit_cast(float, a1);
+  const int i0 = (int)b0, i1 = (int)b1;
+  const bool first = v0 > v1 || (v0 == v1 && i0 < i1);
+  v = first ? v0 : v1;
+  i = first ? i0 : i1;
+}
 template <class Op>
 __device__ __forceinline__ float wave_reduce(float v, Op op) {
   v = op(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1

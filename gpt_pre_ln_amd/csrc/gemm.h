@@ -45,11 +45,12 @@ namespace gpt2 {
 // kRowReduce epilogues (EpiCE) instead receive, per row m and per column
 // slice s of one wave's width (gemm_slice_width), the maximum and the sum of
 // exp(C - maximum) over the slice's columns below n_valid, and the single
-// entry C[m][label(m)] from the lane that holds it.
+// entry C[m][label(m)] from the lane that holds it; kRowArgmax epilogues
+// (EpiArgmax) the slice maximum and the first column holding it.
 
 template <typename T>
 struct EpiQKV {
-  static constexpr bool kPreload = false, kBias = true, kTransposed = true, kRowReduce = false;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = true, kRowReduce = false, kRowArgmax = false;
   const float* bias;  // [3D]
   T* q;               // [B][H][Tq][hs], scaled by q_scale
   T* k;               // [B][H][kvT][hs], rows t0 + t
@@ -111,7 +112,7 @@ struct EpiQKV {
 };
 
 struct EpiResidual {
-  static constexpr bool kPreload = true, kBias = true, kTransposed = false, kRowReduce = false;
+  static constexpr bool kPreload = true, kBias = true, kTransposed = false, kRowReduce = false, kRowArgmax = false;
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
@@ -128,7 +129,7 @@ struct EpiResidual {
 
 template <typename T>
 struct EpiGelu {
-  static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false;
+  static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false, kRowArgmax = false;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
@@ -148,7 +149,7 @@ typedef float f32x4_u4_t __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_u2_t __attribute__((ext_vector_type(2), aligned(2)));
 template <typename O>
 struct EpiLogits {
-  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false;
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false, kRowArgmax = false;
   O* out;       // [M][ldo], only columns n < n_valid are written
   int ldo;
   int n_valid;
@@ -178,7 +179,7 @@ struct EpiLogits {
 // stored.  Row m = b*T + t of the product has label labels[m + 1] when
 // t < T - 1, none otherwise.
 struct EpiCE {
-  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = true;
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = true, kRowArgmax = false;
   float2* part;            // [M][nseg]: (max, sum of exp(C - max)) per column slice
   int nseg;                // slices per row
   const int32_t* labels;   // [M]
@@ -198,6 +199,25 @@ struct EpiCE {
     part[(size_t)m * nseg + s] = make_float2(mx, sum);
   }
   __device__ __forceinline__ void target(int m, float v) const { tgt[m] = v; }
+};
+
+// Greedy token choice of the tied lm_head (the generation loop): per row m
+// and column slice s, the largest C[m][n] over the slice's columns below
+// n_valid and the first column holding it; the logits are not stored.
+struct EpiArgmax {
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false,
+                        kRowArgmax = true;
+  int2* part;   // [M][nseg]: (bits of the slice maximum, its first column)
+  int nseg;     // slices per row
+  int n_valid;  // vocabulary size
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int, int, const f32x4_t&, const float4&) const {}
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+  __device__ __forceinline__ void partial(int m, int s, float v, int col) const {
+    part[(size_t)m * nseg + s] = make_int2(__builtin_bit_cast(int, v), col);
+  }
 };
 
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),

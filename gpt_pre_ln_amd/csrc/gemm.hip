@@ -235,6 +235,33 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
     return;
   }
 
+  if constexpr (Epi::kRowArgmax) {
+    // Same lane layout as the kRowReduce path: per fragment row, the lane's
+    // columns in increasing order (strictly larger replaces, so the first
+    // maximum stays), then across the four lanes holding the row.
+    const int nw = n0 + wn * WTN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WTM + i * 16 + lr;
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = nw + j * 16 + lg * 4 + e;
+          if (col < epi.n_valid && acc[i][j][e] > best) {
+            best = acc[i][j][e];
+            bi = col;
+          }
+        }
+      argmax_xor<16>(best, bi);
+      argmax_xor<32>(best, bi);
+      if (m < M && lg == 0) epi.partial(m, nw / WTN, best, bi);
+    }
+    return;
+  }
+
   // Each wave then stages its WTM x WTN sub-tile through a private slice
   // of the (now idle) operand LDS, R rows at a time, and reads it back so
   // that 16-byte groups of consecutive lanes cover consecutive columns of one
@@ -487,6 +514,10 @@ GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
+template hipError_t launch_gemm<float, EpiArgmax>(GemmTile, const float*, const float*, int, int, int, int, int,
+                                                  const EpiArgmax&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiArgmax>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,
+                                                   const EpiArgmax&, hipStream_t);
 template hipError_t launch_gemm<float, EpiCE>(GemmTile, const float*, const float*, int, int, int, int, int,
                                               const EpiCE&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiCE>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,

@@ -125,6 +125,8 @@ struct WsLayout {
   // placed over q .. rpart, which are dead once ln_f has run
   size_t ce_part, ce_tgt, ce_loss;
   int ce_nseg;
+  // generation loop: the token chosen at one step, read by the next
+  size_t gen_tok;
   size_t total;
 };
 
@@ -150,6 +152,7 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   // split-K partials of the decode step's residual projections (at most 32 rows)
   const int ks = std::max(skinny_splits(c.d_model, (int)es), skinny_splits(c.d_ff, (int)es));
   W.rpart = take((size_t)ks * std::min<size_t>(M, 32) * D * 4);
+  W.gen_tok = take(M * 4);
   const size_t end = off;
   off = W.q;
   W.ce_nseg = vocab_pad(c) / gemm_slice_width(pick_tile((int)M, vocab_pad(c)));
@@ -372,8 +375,17 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
   return GPT2_OK;
 }
 
+// Output of a generation step (gpt2_generate): the greedy token of row b goes
+// to out[b * stride + col] and to next[b].
+struct GenOut {
+  int32_t* out;
+  int stride, col;
+  int32_t* next;
+};
+
 template <typename T>
-gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, hipStream_t st) {
+gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, const GenOut* gen,
+                       hipStream_t st) {
   const gpt2_config& c = m->cfg;
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
   const int B = kv->B, M = B, pos = kv->past_len;
@@ -384,9 +396,11 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   T* a = reinterpret_cast<T*>(m->ws + W.a);
   T* u = reinterpret_cast<T*>(m->ws + W.u);
   float* part = reinterpret_cast<float*>(m->ws + W.part);
-  // The residual projections (attn.c_proj, mlp.c_proj) write split-K partial
-  // products; the LayerNorm that follows each adds them, the bias and the
-  // residual stream, writes x back and normalises: no reduce launch.
+  // Up to 32 rows the residual projections (attn.c_proj, mlp.c_proj) write
+  // split-K partial products and the LayerNorm that follows each adds them,
+  // the bias and the residual stream, writes x back and normalises: no reduce
+  // launch.  More rows take the tiled GEMM with the residual epilogue.
+  const bool split = M <= 32;
   float* rpart = reinterpret_cast<float*>(m->ws + W.rpart);
   const int ks_o = skinny_splits(D, sizeof(T)), ks_p = skinny_splits(F, sizeof(T));
   const float* pending_bias = nullptr;  // mlp.c_proj bias of the previous layer, when partials are pending
@@ -407,21 +421,40 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
-    GPT2_HIP(launch_gemm_skinny_splitk<T>(a, pp<T>(m, o.w_o), M, D, D, D, D, rpart, st), "attn.c_proj");
-    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0, rpart,
-                                 ks_o, pf(m, o.b_o)),
+    if (split) {
+      GPT2_HIP(launch_gemm_skinny_splitk<T>(a, pp<T>(m, o.w_o), M, D, D, D, D, rpart, st), "attn.c_proj");
+    } else {
+      EpiResidual e{pf(m, o.b_o), x, D};
+      GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
+    }
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
+                                 split ? rpart : nullptr, ks_o, pf(m, o.b_o)),
              "ln_2");
     {
       EpiGelu<T> e{pf(m, o.b_fc), u, F};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
-    GPT2_HIP(launch_gemm_skinny_splitk<T>(u, pp<T>(m, o.w_pr), M, D, F, F, F, rpart, st), "mlp.c_proj");
-    pending_bias = pf(m, o.b_pr);
+    if (split) {
+      GPT2_HIP(launch_gemm_skinny_splitk<T>(u, pp<T>(m, o.w_pr), M, D, F, F, F, rpart, st), "mlp.c_proj");
+      pending_bias = pf(m, o.b_pr);
+    } else {
+      EpiResidual e{pf(m, o.b_pr), x, D};
+      GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
+    }
   }
   GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
                                pending_bias ? rpart : nullptr, ks_p, pending_bias),
            "ln_f");
-  GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
+  if (gen) {
+    // lm_head with the arg-max epilogue (no logits stored), then one wave per row
+    int2* apart = reinterpret_cast<int2*>(m->ws + W.ce_part);
+    EpiArgmax e{apart, W.ce_nseg, V};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
+             "lm_head argmax");
+    GPT2_HIP(launch_argmax_rows(apart, W.ce_nseg, M, V, gen->out + gen->col, gen->stride, gen->next, st), "argmax");
+  } else {
+    GPT2_HIP(launch_lm_head<T>(m, h, logits, M, st), "lm_head");
+  }
   kv->past_len = pos + 1;
   return GPT2_OK;
 }
@@ -592,8 +625,30 @@ gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tok
   if (kv->past_len >= kv->max_T) return GPT2_ERR_CAPACITY;
   if (ws_layout(m->cfg, kv->B, 1).total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, tokens, logits, st)
-                                   : run_decode<float>(m, kv, tokens, logits, st);
+  return m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, tokens, logits, nullptr, st)
+                                   : run_decode<float>(m, kv, tokens, logits, nullptr, st);
+}
+
+gpt2_status gpt2_generate(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, int32_t n_steps, int32_t* out,
+                          void* stream) {
+  if (!m || !kv || !tokens || !out || !kv->d_kv) return GPT2_ERR_INVALID_ARG;
+  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(out, 4)) return GPT2_ERR_INVALID_ARG;
+  if (n_steps < 1) return GPT2_ERR_SHAPE;
+  if (kv->B < 1 || kv->max_T < 1 || kv->max_T > m->cfg.n_positions) return GPT2_ERR_SHAPE;
+  if (kv->past_len < 0) return GPT2_ERR_SHAPE;
+  if ((int64_t)kv->past_len + n_steps > kv->max_T) return GPT2_ERR_CAPACITY;
+  const WsLayout W = ws_layout(m->cfg, kv->B, 1);
+  if (W.total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
+  int32_t* next = reinterpret_cast<int32_t*>(m->ws + W.gen_tok);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n_steps; ++i) {
+    const GenOut g{out, n_steps, i, next};
+    const int32_t* in = i == 0 ? tokens : next;
+    const gpt2_status s = m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, in, nullptr, &g, st)
+                                                    : run_decode<float>(m, kv, in, nullptr, &g, st);
+    if (s != GPT2_OK) return s;
+  }
+  return GPT2_OK;
 }
 
 gpt2_status gpt2_set_trace(gpt2_model* m, float* d_trace, size_t n) {

@@ -46,4 +46,11 @@ hipError_t launch_ce_rows(const float2* part, int nseg, const float* tgt, const 
 // out[0] = mean of loss over the positions whose label is >= 0 (NaN if none).
 hipError_t launch_ce_mean(const float* loss, const int32_t* labels, int B, int T, float* out, hipStream_t stream);
 
+// Greedy token choice (the generation loop): the largest logit of each row,
+// first column on ties, from the lm_head's EpiArgmax partials (part / nseg);
+// written to out[row * out_stride] and next[row] (the next step's input).
+// Rows without an ordered logit (all NaN) give token 0.
+hipError_t launch_argmax_rows(const int2* part, int nseg, int M, int V, int32_t* out, int out_stride, int32_t* next,
+                              hipStream_t stream);
+
 }  // namespace gpt2

@@ -262,7 +262,53 @@ __global__ __launch_bounds__(1024) void ce_mean_kernel(const float* __restrict__
   }
 }
 
+// Greedy token per row from the lm_head's EpiArgmax partials: one wave per
+// row; lane l scans slices l, l+64, ... in increasing order (strictly larger
+// replaces, so the first maximum stays), then the lanes combine pairs
+// (larger value, then smaller column).  A row with no ordered value (all NaN)
+// gets token 0, so the next step's embedding gather stays inside wte.
+__global__ __launch_bounds__(256) void argmax_rows_kernel(const int2* __restrict__ part, int nseg, int M, int V,
+                                                           int32_t* __restrict__ out, int out_stride,
+                                                           int32_t* __restrict__ next) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int2* pr = part + (size_t)row * nseg;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int s = lane; s < nseg; s += 64) {
+    const int2 q = pr[s];
+    const float v = __builtin_bit_cast(float, q.x);
+    if (v > best) {
+      best = v;
+      bi = q.y;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    if (v2 > best || (v2 == best && i2 < bi)) {
+      best = v2;
+      bi = i2;
+    }
+  }
+  if (lane == 0) {
+    const int tok = (bi >= 0 && bi < V) ? bi : 0;
+    out[(size_t)row * out_stride] = tok;
+    next[row] = tok;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_argmax_rows(const int2* part, int nseg, int M, int V, int32_t* out, int out_stride, int32_t* next,
+                              hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, part, nseg, M, V, out, out_stride,
+                     next);
+  return hipGetLastError();
+}
 
 hipError_t launch_ce_rows(const float2* part, int nseg, const float* tgt, const int32_t* labels, int B, int T, int V,
                           float* loss, hipStream_t stream) {

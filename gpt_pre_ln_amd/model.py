@@ -124,6 +124,17 @@ class GPT2:
         B.gpt2_decode_step(self.handle, kv.view, new_ids.data_ptr(), lg.data_ptr(), self.stream)
         return lg
 
+    def generate(self, kv: KVCache, first_ids: torch.Tensor, n_steps: int, out: torch.Tensor | None = None):
+        """Greedy generation (gpt2_generate): first_ids int32 [B] at position
+        kv.past_len; returns int32 [B, n_steps], column i the token chosen at step i."""
+        assert first_ids.dtype == torch.int32 and first_ids.is_contiguous() and first_ids.device == self.device
+        Bsz = kv.view.B
+        if out is None:
+            out = torch.empty((Bsz, n_steps), dtype=torch.int32, device=self.device)
+        assert out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (Bsz, n_steps)
+        B.gpt2_generate(self.handle, kv.view, first_ids.data_ptr(), n_steps, out.data_ptr(), self.stream)
+        return out
+
     def set_trace(self, trace: torch.Tensor | None):
         B.gpt2_set_trace(self.handle, trace.data_ptr() if trace is not None else None,
                          trace.numel() if trace is not None else 0)

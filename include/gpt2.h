@@ -154,6 +154,24 @@ gpt2_status gpt2_forward_loss(gpt2_model* model, const int32_t* d_tokens, const 
 gpt2_status gpt2_decode_step(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_new_tokens,
                              void* d_logits, void* stream);
 
+/* Greedy generation: n_steps decode steps in one call, each feeding the token
+ * it chose to the next, with no host round trip (pwwt.cn closing section:
+ * generation one token at a time over a KV cache; bbs.huaweicloud.com blog
+ * 476445, architecture overview: LM head, softmax over the vocabulary, pick a
+ * token).  The pick is the most probable token -- the largest logit, since
+ * softmax is monotone -- the lowest id on ties, decided in fp32 from the
+ * lm_head's accumulators, which are reduced on chip (no logits are written).
+ *   d_tokens:     int32 [kv->B], the input of the first step, at position
+ *                 kv->past_len (typically the prompt's last token after a
+ *                 prefill of the others).
+ *   d_out_tokens: int32 [kv->B, n_steps]; column i is the token chosen at
+ *                 step i and the input of step i + 1.
+ * Requires n_steps >= 1 and kv->past_len + n_steps <= kv->max_T (else
+ * GPT2_ERR_CAPACITY); kv->past_len grows by n_steps (host side, at enqueue).
+ * A row without any ordered logit (all NaN) yields token 0. */
+gpt2_status gpt2_generate(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_tokens, int32_t n_steps,
+                          int32_t* d_out_tokens, void* stream);
+
 /* Optional per-layer trace for debugging: when d_trace is non-NULL, the next
  * gpt2_forward calls copy the residual stream after every block (X_{l+1},
  * fp32 [n_layer][B*T][d_model]) into d_trace, which must hold that many floats.

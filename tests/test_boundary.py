@@ -173,6 +173,23 @@ def test_decode_host_checks(B, handle):
     assert lib.gpt2_decode_step(h, ctypes.byref(kv), FAKE, None, None) == B.GPT2_ERR_INVALID_ARG
 
 
+def test_generate_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    gen = lambda kv, n, tok=FAKE, out=FAKE: lib.gpt2_generate(h, ctypes.byref(kv), tok, n, out, None)
+    kv = B.gpt2_kv_view(FAKE, 2, 32, 30)
+    assert gen(kv, 3) == B.GPT2_ERR_CAPACITY      # 30 + 3 > 32
+    assert gen(kv, 0) == B.GPT2_ERR_SHAPE
+    assert gen(kv, 2, tok=None) == B.GPT2_ERR_INVALID_ARG
+    assert gen(kv, 2, out=FAKE + 2) == B.GPT2_ERR_INVALID_ARG
+    kv = B.gpt2_kv_view(FAKE, 2, 200, 0)           # max_T > n_positions
+    assert gen(kv, 1) == B.GPT2_ERR_SHAPE
+    kv = B.gpt2_kv_view(FAKE, 2, 32, -1)
+    assert gen(kv, 1) == B.GPT2_ERR_SHAPE
+    kv = B.gpt2_kv_view(None, 2, 32, 0)
+    assert gen(kv, 1) == B.GPT2_ERR_INVALID_ARG
+
+
 def test_init_params_size_check(B, handle):
     h, cfg = handle
     n = B.gpt2_param_blob_floats(cfg)

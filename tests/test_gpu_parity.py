@@ -208,14 +208,15 @@ def test_batch_independence_gpu():
 # ------------------------------------------------------------ decode
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_decode_small_shapes(dtype):
+@pytest.mark.parametrize("dtype,Bsz", [("f32", 3), ("bf16", 3), ("bf16", 40)])
+def test_decode_small_shapes(dtype, Bsz):
     """Prefill P tokens into the cache, then several decode steps; each step must
-    match the oracle's row P+i of the plain forward."""
-    _announce(f"decode small dtype={dtype}")
+    match the oracle's row P+i of the plain forward.  Up to 32 sequences the
+    residual projections take the split-K path, beyond it the tiled GEMM."""
+    _announce(f"decode small dtype={dtype} B={Bsz}")
     s = W.ModelShape(vocab=700, n_positions=300, d_model=128, n_head=2, n_layer=2, d_ff=512)
     blob = W.make_params(s, _init_small(0.08), 12)
-    Bsz, Pn, steps, max_T = 3, 61, 4, 70
+    Pn, steps, max_T = 61, 4, 70
     rng = np.random.default_rng(13)
     ids = rng.integers(0, 700, size=(Bsz, Pn + steps)).astype(np.int32)
     m = _model(s, dtype, Bsz, Pn, blob)
