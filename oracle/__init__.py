@@ -7,7 +7,7 @@ library never calls into it, and nothing here calls the HIP library.
 See ``oracle.gpt2`` for the functions and the passages each one follows.
 """
 from .gpt2 import (  # noqa: F401
-    bf16_round, layer_norm, gelu_new, causal_attention, block_forward,
+    bf16_round, layer_norm, gelu_new, gelu_erf, causal_attention, block_forward,
     embed, forward_hidden, forward, decode_logits, shifted_cross_entropy, lm_loss, generate_greedy,
     prepare_params,
     TRACE_POINTS,

@@ -87,9 +87,17 @@ def gelu_new(x: np.ndarray) -> np.ndarray:
     return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * (x * x * x))))
 
 
+def gelu_erf(x: np.ndarray) -> np.ndarray:
+    """0.5 x (1 + erf(x / sqrt(2))), the standard GELU the pages contrast with
+    gelu_new ([HFsrc] section GPT2MLP).  erf from scipy (a library routine)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
 def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_offset: int = 0,
-                     return_probs: bool = False):
-    """softmax(q k^T / sqrt(hs), keys j <= i) v, per head.
+                     return_probs: bool = False, scale: float | None = None):
+    """softmax(q k^T * scale, keys j <= i) v, per head; scale = 1/sqrt(hs) unless given.
 
     q: [H, Tq, hs] at absolute positions q_offset .. q_offset+Tq-1;
     k, v: [H, Tk, hs] at positions 0 .. Tk-1.
@@ -108,7 +116,7 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_offset: int 
     out = np.empty((H, Tq, v.shape[2]), dtype=np.float64)
     probs = np.empty((H, Tq, Tk), dtype=np.float64) if return_probs else None
     for h in range(H):
-        s = (q[h] @ k[h].T) / np.sqrt(float(hs))
+        s = (q[h] @ k[h].T) / np.sqrt(float(hs)) if scale is None else (q[h] @ k[h].T) * scale
         s = np.where(allowed, s, -np.inf)
         s = s - s.max(axis=-1, keepdims=True)
         e = np.where(allowed, np.exp(s), 0.0)
@@ -134,7 +142,7 @@ def prepare_params(blob: np.ndarray, shape, dtype: str) -> dict:
     raw = unpack(np.asarray(blob, np.float32), shape)
     out = {}
     for key, arr in raw.items():
-        is_matrix = key in ("wte", "wpe") or key.endswith("c_attn.w") or key.endswith("c_proj.w") \
+        is_matrix = key in ("wte", "wpe", "lm_head.w") or key.endswith("c_attn.w") or key.endswith("c_proj.w") \
             or key.endswith("c_fc.w")
         a = bf16_round(arr) if (dtype == "bf16" and is_matrix) else arr
         out[key] = a.astype(np.float64)
@@ -155,31 +163,47 @@ def embed(P: dict, ids: np.ndarray, pos0: int = 0) -> np.ndarray:
 
 
 def block_forward(x: np.ndarray, P: dict, l: int, trace: dict | None = None) -> np.ndarray:
-    """One Pre-LN block on one sequence x [T, D].
+    """One block on one sequence x [T, D].
 
-    H = X + Attn(LN_1(X)),  X' = H + MLP(LN_2(H))
+    Pre-LN (GPT-2):  H = X + Attn(LN_1(X)),  X' = H + MLP(LN_2(H))
     [Hidden] section "GPT-2 Block" (the four-line data flow);
     [HFsrc] GPT2Block.forward (ln_1 -> attn -> residual -> ln_2 -> mlp ->
     residual), GPT2Attention (fused c_attn, split into thirds q|k|v, heads as
     consecutive head_dim-wide column blocks, merge heads, c_proj), GPT2MLP
     (c_fc -> gelu_new -> c_proj).
+    Switches of the model shape (defaults as above):
+      post_ln: H = LN_1(X + Attn(X)),  X' = LN_2(H + MLP(H)) -- the Post-Norm
+        form LN(x + Sublayer(x)) ([Hidden] Pre-Norm section; [llmc] 3.1);
+        the same ln_1 / ln_2 parameters, ln_f and the head unchanged.
+      scale_attn_by_inverse_layer_idx: scores further divided by l + 1
+        ([HFsrc] GPT2Config, the switch of the original TensorFlow code).
+      activation "gelu": the erf GELU instead of gelu_new ([HFsrc] GPT2MLP).
     """
     s = P["_shape"]
     D, H = s.d_model, s.n_head
     hs = D // H
     T = x.shape[0]
     pre = f"h.{l}."
-    h = layer_norm(x, P[pre + "ln_1.w"], P[pre + "ln_1.b"], s.ln_eps)
+    act = gelu_erf if getattr(s, "activation", "gelu_new") == "gelu" else gelu_new
+    post = getattr(s, "post_ln", False)
+    scale = 1.0 / np.sqrt(float(hs))
+    if getattr(s, "scale_attn_by_inverse_layer_idx", False):
+        scale = scale / float(l + 1)
+    ln1 = lambda z: layer_norm(z, P[pre + "ln_1.w"], P[pre + "ln_1.b"], s.ln_eps)
+    ln2 = lambda z: layer_norm(z, P[pre + "ln_2.w"], P[pre + "ln_2.b"], s.ln_eps)
+    h = x if post else ln1(x)
     qkv = h @ P[pre + "attn.c_attn.w"] + P[pre + "attn.c_attn.b"]
     q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
     split = lambda t: t.reshape(T, H, hs).transpose(1, 0, 2)   # [H, T, hs]
-    a = causal_attention(split(q), split(k), split(v))
+    a = causal_attention(split(q), split(k), split(v), scale=scale)
     a = a.transpose(1, 0, 2).reshape(T, D)                      # merge heads in order
     x_h = x + (a @ P[pre + "attn.c_proj.w"] + P[pre + "attn.c_proj.b"])
-    h2 = layer_norm(x_h, P[pre + "ln_2.w"], P[pre + "ln_2.b"], s.ln_eps)
-    u = gelu_new(h2 @ P[pre + "mlp.c_fc.w"] + P[pre + "mlp.c_fc.b"])
+    if post:
+        x_h = ln1(x_h)
+    h2 = x_h if post else ln2(x_h)
+    u = act(h2 @ P[pre + "mlp.c_fc.w"] + P[pre + "mlp.c_fc.b"])
     m = u @ P[pre + "mlp.c_proj.w"] + P[pre + "mlp.c_proj.b"]
-    x_out = x_h + m
+    x_out = ln2(x_h + m) if post else x_h + m
     if trace is not None:
         trace.setdefault("attn_norm", []).append(h)
         trace.setdefault("ffn_inp", []).append(x_h)
@@ -204,17 +228,20 @@ def forward(P: dict, ids: np.ndarray, positions=None, trace: dict | None = None)
     """Logits [B, T, V] (or [B, len(positions), V]) for ids [B, T].
 
     logits = ln_f(X_L) @ wte^T, the tied head without bias ([HFsrc]
-    GPT2LMHeadModel; [Anatomy] LM head; [Stack] final LayerNorm + head).
+    GPT2LMHeadModel; [Anatomy] LM head; [Stack] final LayerNorm + head);
+    with a separate head (tie_word_embeddings False, [Stack]'s nn.Linear
+    head) lm_head.w [V, D] takes wte's place.
     ``positions`` selects which rows of every sequence get logits (all when
     None); rows are independent once h_f is known.
     """
     ids = np.atleast_2d(np.asarray(ids))
+    head = P["lm_head.w"] if "lm_head.w" in P else P["wte"]   # untied head when present
     outs = []
     for b in range(ids.shape[0]):
         hf = forward_hidden(P, ids[b], trace=trace)
         if positions is not None:
             hf = hf[np.asarray(positions)]
-        outs.append(hf @ P["wte"].T)
+        outs.append(hf @ head.T)
     return np.stack(outs)
 
 

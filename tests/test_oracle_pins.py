@@ -211,27 +211,40 @@ def test_param_counts_other_shapes():
 
 
 def _torch_reference_forward(P, ids):
-    """Independent fp64 forward built from torch.nn.functional library routines."""
+    """Independent fp64 forward built from torch.nn.functional library routines,
+    with the model-shape switches (Post-LN wiring, per-layer score scaling, erf
+    GELU, separate head)."""
     s = P["_shape"]
     D, H = s.d_model, s.n_head
     t = lambda key: torch.from_numpy(P[key])
     ids_t = torch.from_numpy(np.asarray(ids, np.int64))
     B, T = ids_t.shape
+    post = getattr(s, "post_ln", False)
+    approx = "none" if getattr(s, "activation", "gelu_new") == "gelu" else "tanh"
     x = F.embedding(ids_t, t("wte")) + t("wpe")[:T]
     for l in range(s.n_layer):
         p = lambda k: t(f"h.{l}.{k}")
-        h = F.layer_norm(x, (D,), p("ln_1.w"), p("ln_1.b"), s.ln_eps)
+        ln1 = lambda z: F.layer_norm(z, (D,), p("ln_1.w"), p("ln_1.b"), s.ln_eps)
+        ln2 = lambda z: F.layer_norm(z, (D,), p("ln_2.w"), p("ln_2.b"), s.ln_eps)
+        h = x if post else ln1(x)
         qkv = F.linear(h, p("attn.c_attn.w").T, p("attn.c_attn.b"))
         q, k, v = qkv.split(D, dim=2)
         heads = lambda z: z.view(B, T, H, D // H).permute(0, 2, 1, 3)
-        a = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True)
+        scale = 1.0 / math.sqrt(D // H)
+        if getattr(s, "scale_attn_by_inverse_layer_idx", False):
+            scale /= l + 1
+        a = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True, scale=scale)
         a = a.permute(0, 2, 1, 3).reshape(B, T, D)
         x = x + F.linear(a, p("attn.c_proj.w").T, p("attn.c_proj.b"))
-        h = F.layer_norm(x, (D,), p("ln_2.w"), p("ln_2.b"), s.ln_eps)
-        u = F.gelu(F.linear(h, p("mlp.c_fc.w").T, p("mlp.c_fc.b")), approximate="tanh")
+        if post:
+            x = ln1(x)
+        h = x if post else ln2(x)
+        u = F.gelu(F.linear(h, p("mlp.c_fc.w").T, p("mlp.c_fc.b")), approximate=approx)
         x = x + F.linear(u, p("mlp.c_proj.w").T, p("mlp.c_proj.b"))
+        if post:
+            x = ln2(x)
     x = F.layer_norm(x, (D,), t("ln_f.w"), t("ln_f.b"), s.ln_eps)
-    return F.linear(x, t("wte")).numpy()
+    return F.linear(x, t("lm_head.w") if "lm_head.w" in P else t("wte")).numpy()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -497,3 +510,84 @@ def test_generate_greedy_vs_torch_loop():
         assert (nxt == out[:, i]).all(), f"step {i}"
         seq = np.concatenate([seq, nxt[:, None]], axis=1)
     np.testing.assert_array_equal(oracle.generate_greedy(P, prompt, 3), out[:, :3])
+
+
+# ---------------------------------------------------------------- model variants (switches)
+
+
+def test_gelu_erf_identities_and_torch():
+    x = np.linspace(-8, 8, 4001)
+    y = oracle.gelu_erf(x)
+    assert oracle.gelu_erf(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(y - oracle.gelu_erf(-x), x, rtol=0, atol=1e-14)
+    ref = F.gelu(torch.from_numpy(x), approximate="none").numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-15)
+    # the two forms differ, by at most ~4.7e-4 (the page's "small difference")
+    d = np.abs(y - oracle.gelu_new(x)).max()
+    assert 4e-4 < d < 5e-4
+
+
+VARIANTS = {
+    "post_ln": dict(post_ln=True),
+    "layer_scale": dict(scale_attn_by_inverse_layer_idx=True),
+    "gelu_erf": dict(activation="gelu"),
+    "untied": dict(tie_word_embeddings=False),
+    "all": dict(post_ln=True, scale_attn_by_inverse_layer_idx=True, activation="gelu", tie_word_embeddings=False),
+}
+
+
+def _variant_shape(name, **kw):
+    import dataclasses
+    return dataclasses.replace(_tiny_shape(n_head=4, d=64, L=3, vocab=97, npos=40), **VARIANTS[name], **kw)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_variant_forward_vs_torch_library_fp64(name, dtype):
+    s = _variant_shape(name)
+    _, P = _random_params(s, 51, dtype)
+    ids = np.random.default_rng(52).integers(0, 97, size=(2, 23))
+    got = oracle.forward(P, ids)
+    np.testing.assert_allclose(got, _torch_reference_forward(P, ids), rtol=1e-11, atol=1e-11)
+    # the switch changes the result
+    import dataclasses
+    base = dataclasses.replace(s, **{k: getattr(_tiny_shape(), k) for k in VARIANTS[name]})
+    Pb = dict(P)
+    Pb["_shape"] = base
+    Pb.pop("lm_head.w", None)
+    assert np.abs(got - oracle.forward(Pb, ids)).max() > 1e-6
+
+
+def test_post_ln_identity_blocks_closed_form():
+    """Post-LN with zero c_proj weights and biases: each block is LN_2(LN_1(X))."""
+    s = _variant_shape("post_ln")
+    _, P = _random_params(s, 53)
+    for l in range(s.n_layer):
+        for k in ("attn.c_proj.w", "attn.c_proj.b", "mlp.c_proj.w", "mlp.c_proj.b"):
+            P[f"h.{l}.{k}"] = np.zeros_like(P[f"h.{l}.{k}"])
+    ids = np.random.default_rng(54).integers(0, s.vocab, size=(1, 11))
+    x = P["wte"][ids[0]] + P["wpe"][:11]
+    for l in range(s.n_layer):
+        x = oracle.layer_norm(oracle.layer_norm(x, P[f"h.{l}.ln_1.w"], P[f"h.{l}.ln_1.b"]),
+                              P[f"h.{l}.ln_2.w"], P[f"h.{l}.ln_2.b"])
+    expect = oracle.layer_norm(x, P["ln_f.w"], P["ln_f.b"]) @ P["wte"].T
+    np.testing.assert_allclose(oracle.forward(P, ids)[0], expect, rtol=1e-12, atol=1e-13)
+
+
+def test_layer_scale_leaves_layer_zero_and_untied_equal_head_is_tied():
+    """Per-layer scaling divides layer l's scores by l + 1, so a one-layer model
+    is unchanged; a separate head equal to wte gives the tied model bitwise."""
+    import dataclasses
+    s1 = dataclasses.replace(_tiny_shape(L=1), scale_attn_by_inverse_layer_idx=True)
+    _, P = _random_params(s1, 55)
+    ids = np.random.default_rng(56).integers(0, s1.vocab, size=(1, 13))
+    Pb = dict(P)
+    Pb["_shape"] = dataclasses.replace(s1, scale_attn_by_inverse_layer_idx=False)
+    np.testing.assert_array_equal(oracle.forward(P, ids), oracle.forward(Pb, ids))
+    su = dataclasses.replace(_tiny_shape(L=2), tie_word_embeddings=False)
+    _, Pu = _random_params(su, 57)
+    Pu["lm_head.w"] = Pu["wte"].copy()
+    Pt = dict(Pu)
+    Pt.pop("lm_head.w")
+    Pt["_shape"] = dataclasses.replace(su, tie_word_embeddings=True)
+    np.testing.assert_array_equal(oracle.forward(Pu, ids), oracle.forward(Pt, ids))

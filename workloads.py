@@ -23,8 +23,10 @@ Parameter blob layout (fp32, one flat array, this exact order):
         ln_2.w[D], ln_2.b[D],
         mlp.c_fc.w[D, F], mlp.c_fc.b[F],
         mlp.c_proj.w[F, D], mlp.c_proj.b[D],
-    ln_f.w[D], ln_f.b[D]
-Matrices are stored [in, out] (the Conv1D orientation: y = x @ W + b).
+    ln_f.w[D], ln_f.b[D],
+    lm_head.w[V, D]          (only when tie_word_embeddings is False)
+Matrices are stored [in, out] (the Conv1D orientation: y = x @ W + b); the
+separate head is stored like wte, [V, D] (nn.Linear's [out, in]).
 
 Random numbers.  Token ids come from numpy's PCG64 (``default_rng``).
 Parameters come from a counter-based generator so that large blobs (GPT-2 XL
@@ -60,6 +62,13 @@ class ModelShape:
     n_layer: int
     d_ff: int
     ln_eps: float = 1e-5
+    # Variants the pages describe as switches; the defaults are GPT-2 as
+    # released (pwwt.cn GPT2Config / GPT2MLP; russellluo.com Pre-Norm;
+    # nano-ai.tech Transformer Stack for the separate head).
+    activation: str = "gelu_new"                   # "gelu_new" (tanh form) or "gelu" (erf form)
+    scale_attn_by_inverse_layer_idx: bool = False  # scores further divided by layer index + 1
+    post_ln: bool = False                          # LN(x + Sublayer(x)) instead of x + Sublayer(LN(x))
+    tie_word_embeddings: bool = True               # False: a separate head lm_head.w [V, D]
 
     @property
     def head_dim(self) -> int:
@@ -144,6 +153,8 @@ def param_specs(s: ModelShape):
         for k in LAYER_TENSORS:
             out.append((f"h.{l}.{k}", shapes[k]))
     out += [("ln_f.w", (D,)), ("ln_f.b", (D,))]
+    if not s.tie_word_embeddings:
+        out.append(("lm_head.w", (s.vocab, D)))
     return out
 
 
@@ -171,7 +182,7 @@ def unpack(blob: np.ndarray, s: ModelShape) -> dict:
 def _init_of(key: str, init: Init):
     """(mean, std) for one tensor key."""
     leaf = key.split(".", 2)[-1] if key.startswith("h.") else key
-    if leaf in ("wte", "wpe", "attn.c_attn.w", "mlp.c_fc.w"):
+    if leaf in ("wte", "wpe", "lm_head.w", "attn.c_attn.w", "mlp.c_fc.w"):
         return 0.0, init.w_std
     if leaf in ("attn.c_proj.w", "mlp.c_proj.w"):
         return 0.0, init.proj_std
