@@ -236,6 +236,25 @@ def main():
     loss_step = {"value": round(B * T / el_loss, 1), "unit": "tokens/s", "ms_per_step": round(el_loss * 1e3, 4),
                  "mean_loss": round(float(loss_mean.item()), 5)}
 
+    # the same workload with every variant switch on (Post-LN wiring, per-layer
+    # score scaling, erf GELU, separate head): its own weights, same ids
+    import dataclasses
+    vshape = dataclasses.replace(w.shape, post_ln=True, scale_attn_by_inverse_layer_idx=True, activation="gelu",
+                                 tie_word_embeddings=False)
+    vmodel = GPT2.from_shape(vshape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
+    vmodel.load_blob(W.make_params(vshape, w.init, w.param_seed))
+    for _ in range(args.warmup):
+        vmodel.forward(ids, out_logits=logits)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for _ in range(args.steps):
+        vmodel.forward(ids, out_logits=logits)
+    torch.cuda.synchronize()
+    el_v = (time.perf_counter() - t3) / args.steps
+    variant_step = {"switches": ["post_ln", "scale_attn_by_inverse_layer_idx", "gelu_erf", "separate_head"],
+                    "value": round(B * T / el_v, 1), "unit": "tokens/s", "ms_per_step": round(el_v * 1e3, 4)}
+    del vmodel
+
     # the same forward storing fp32 logits (reported beside the headline value)
     alt = None
     if logits_dtype != "f32":
@@ -276,6 +295,7 @@ def main():
         "per_class_ms": {c: round(v["ms_per_step"], 4) for c, v in per_class.items()},
     }
     out["loss_step"] = loss_step
+    out["variant_step"] = variant_step
     if alt is not None:
         out["fp32_logits"] = alt
     if not args.no_cpu_baseline:

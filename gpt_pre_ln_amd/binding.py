@@ -35,7 +35,9 @@ class gpt2_config(ctypes.Structure):
     _fields_ = [("vocab_size", ctypes.c_int32), ("n_positions", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("n_head", ctypes.c_int32),
                 ("n_layer", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("logits_dtype", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("logits_dtype", ctypes.c_int32),
+                ("activation", ctypes.c_int32), ("scale_attn_by_inverse_layer_idx", ctypes.c_int32),
+                ("post_ln", ctypes.c_int32), ("separate_head", ctypes.c_int32)]
 
 
 class gpt2_kv_view(ctypes.Structure):
@@ -105,11 +107,17 @@ def _dtype_code(dtype) -> int:
 
 
 def make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps=1e-5, dtype="bf16",
-                logits_dtype=None):
-    """logits_dtype defaults to the arithmetic dtype (bf16 logits for a bf16 model)."""
+                logits_dtype=None, activation="gelu_new", scale_attn_by_inverse_layer_idx=False, post_ln=False,
+                tie_word_embeddings=True):
+    """logits_dtype defaults to the arithmetic dtype (bf16 logits for a bf16 model).
+    activation: "gelu_new" (tanh form) or "gelu" (erf form)."""
     dt = _dtype_code(dtype)
     ldt = dt if logits_dtype is None else _dtype_code(logits_dtype)
-    return gpt2_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dt, ldt)
+    if activation not in ("gelu_new", "gelu"):
+        raise ValueError(f"activation {activation!r}")
+    return gpt2_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dt, ldt,
+                       int(activation == "gelu"), int(bool(scale_attn_by_inverse_layer_idx)), int(bool(post_ln)),
+                       int(not tie_word_embeddings))
 
 
 # ------------------------------------------------------------ thin wrappers

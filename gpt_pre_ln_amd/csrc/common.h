@@ -195,6 +195,9 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// The erf GELU, 0.5 x (1 + erf(x / sqrt(2))), with the device library's erff.
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
 // Division by a runtime-invariant positive divisor through a precomputed
 // multiplier (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI 1994): for 0 <= n < 2^31 and 1 <= d < 2^31,

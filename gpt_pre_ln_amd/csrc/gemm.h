@@ -6,7 +6,7 @@
 //            column blocks)                        -> EpiQKV (bias, head scatter)
 //   c_proj  (GPT2Attention c_proj, then the first residual of GPT2Block.forward)
 //                                                   -> EpiResidual (bias, x += .)
-//   c_fc    (GPT2MLP c_fc followed by gelu_new)     -> EpiGelu
+//   c_fc    (GPT2MLP c_fc followed by gelu_new, or the erf GELU)  -> EpiGelu
 //   mlp.c_proj (GPT2MLP c_proj, second residual)    -> EpiResidual
 //   lm_head (GPT2LMHeadModel: tied to wte, no bias) -> EpiLogits
 //
@@ -133,11 +133,15 @@ struct EpiGelu {
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
+  int erf_form;       // 0: gelu_new (tanh form), 1: the erf GELU
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
-    Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
+    if (erf_form)
+      Elem<T>::store4(u + (size_t)m * ldu + n, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3]));
+    else
+      Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
   }
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };

@@ -46,6 +46,8 @@ gpt2_status check_config(const gpt2_config* c) {
     return GPT2_ERR_SHAPE;
   if (c->dtype != GPT2_F32 && c->dtype != GPT2_BF16) return GPT2_ERR_UNSUPPORTED;
   if (c->logits_dtype != GPT2_F32 && c->logits_dtype != GPT2_BF16) return GPT2_ERR_UNSUPPORTED;
+  if ((c->activation | c->scale_attn_by_inverse_layer_idx | c->post_ln | c->separate_head) & ~1)
+    return GPT2_ERR_UNSUPPORTED;
   if (!(c->ln_eps >= 0.f) || !std::isfinite(c->ln_eps)) return GPT2_ERR_INVALID_ARG;
   if (c->d_model % c->n_head != 0) return GPT2_ERR_SHAPE;
   const int hs = c->d_model / c->n_head;
@@ -67,6 +69,7 @@ struct LayerOff {
 
 struct ParamLayout {
   size_t wte = 0, wpe = 0, lnf_g = 0, lnf_b = 0, total = 0;
+  size_t head = 0;  // [V_pad][D]: wte itself, or the separate head
   std::vector<LayerOff> layers;
 };
 
@@ -99,6 +102,7 @@ ParamLayout param_layout(const gpt2_config& c) {
   }
   L.lnf_g = take(D * 4);
   L.lnf_b = take(D * 4);
+  L.head = c.separate_head ? take((size_t)vocab_pad(c) * D * es) : L.wte;
   L.total = off;
   return L;
 }
@@ -106,7 +110,7 @@ ParamLayout param_layout(const gpt2_config& c) {
 size_t blob_floats(const gpt2_config& c) {
   const size_t V = c.vocab_size, P = c.n_positions, D = c.d_model, F = c.d_ff;
   const size_t per_layer = 2 * D + (3 * D * D + 3 * D) + (D * D + D) + 2 * D + (D * F + F) + (F * D + D);
-  return V * D + P * D + per_layer * c.n_layer + 2 * D;
+  return V * D + P * D + per_layer * c.n_layer + 2 * D + (c.separate_head ? V * D : 0);
 }
 
 // Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
@@ -254,10 +258,10 @@ hipError_t launch_lm_head(gpt2_model* m, const T* h, void* logits, int M, hipStr
   const GemmTile tile = pick_tile(M, vocab_pad(c));
   if (c.logits_dtype == GPT2_BF16) {
     EpiLogits<bf16_t> e{static_cast<bf16_t*>(logits), V, V};
-    return launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st);
+    return launch_gemm<T>(tile, h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st);
   }
   EpiLogits<float> e{static_cast<float*>(logits), V, V};
-  return launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st);
+  return launch_gemm<T>(tile, h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st);
 }
 
 // ------------------------------------------------------------------ forward
@@ -295,6 +299,10 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     TimedScope ts(m, kEmbed, st);
     GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, st), "embed");
   }
+  // Post-LN: the first block's attention reads the embeddings themselves (an
+  // operand copy of x); later blocks read the output of the previous ln_2.
+  const bool post = c.post_ln != 0;
+  if (post) GPT2_HIP(launch_convert<T>(x, h, (size_t)M * D, (size_t)M * D, st), "post-ln input");
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& o = m->lay.layers[l];
     T* kl;
@@ -307,7 +315,8 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
       kl = reinterpret_cast<T*>(m->ws + W.k);
       vtl = reinterpret_cast<T*>(m->ws + W.vt);
     }
-    {
+    const float q_scale_l = c.scale_attn_by_inverse_layer_idx ? q_scale / (float)(l + 1) : q_scale;
+    if (!post) {
       TimedScope ts(m, kLN, st);
       GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st,
                                    pre ? m->params + o.w_qkv : nullptr, span(o.w_qkv, o.w_o, (size_t)D * D)),
@@ -315,7 +324,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kQKV, st);
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale, M};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(T_seq), FastDiv(D), 0, kvT, H, ilog2(hs), q_scale_l, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     {
@@ -328,20 +337,32 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
       GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
     }
     {
+      // Pre-LN: h = ln_2(x).  Post-LN: x = ln_1(x) in place, h its operand copy.
       TimedScope ts(m, kLN, st);
-      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st,
-                                   pre ? m->params + o.w_fc : nullptr, span(o.w_fc, o.w_pr, (size_t)D * F)),
-               "ln_2");
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, post ? o.ln1_g : o.ln2_g), pf(m, post ? o.ln1_b : o.ln2_b), h,
+                                   post ? x : nullptr, M, D, c.ln_eps, st, pre ? m->params + o.w_fc : nullptr,
+                                   span(o.w_fc, o.w_pr, (size_t)D * F)),
+               post ? "ln_1" : "ln_2");
     }
     {
       TimedScope ts(m, kFC, st);
-      EpiGelu<T> e{pf(m, o.b_fc), u, F};
+      EpiGelu<T> e{pf(m, o.b_fc), u, F, c.activation};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
     {
       TimedScope ts(m, kMLPProj, st);
       EpiResidual e{pf(m, o.b_pr), x, D};
       GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
+    }
+    if (post) {
+      // x = ln_2(x) in place, h the next block's attention input
+      const bool next = l + 1 < c.n_layer;
+      const LayerOff& on = m->lay.layers[next ? l + 1 : l];
+      TimedScope ts(m, kLN, st);
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, x, M, D, c.ln_eps, st,
+                                   pre && next ? m->params + on.w_qkv : nullptr,
+                                   span(on.w_qkv, on.w_o, (size_t)D * D)),
+               "ln_2");
     }
     if (m->trace && (size_t)(l + 1) * M * D <= m->trace_floats) {
       GPT2_HIP(hipMemcpyAsync(m->trace + (size_t)l * M * D, x, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st),
@@ -366,7 +387,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
       TimedScope ts(m, kLMHead, st);
       const GemmTile tile = pick_tile(M, vocab_pad(c));
       EpiCE e{part, W.ce_nseg, loss->labels, FastDiv((uint32_t)T_seq), V, tgt};
-      GPT2_HIP(launch_gemm<T>(tile, h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st), "lm_head loss");
+      GPT2_HIP(launch_gemm<T>(tile, h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st), "lm_head loss");
     }
     GPT2_HIP(launch_ce_rows(part, W.ce_nseg, tgt, loss->labels, B, T_seq, V, per, st), "loss rows");
     if (loss->mean) GPT2_HIP(launch_ce_mean(per, loss->labels, B, T_seq, loss->mean, st), "loss mean");
@@ -408,16 +429,23 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   const float q_scale = 1.0f / std::sqrt((float)hs);
 
   GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, st), "embed");
+  // Post-LN: each LayerNorm follows a residual add (ln_1 after attn.c_proj,
+  // ln_2 after mlp.c_proj) and also writes the normalised row back to x; the
+  // first block's attention reads an operand copy of the embeddings.
+  const bool post = c.post_ln != 0;
+  if (post) GPT2_HIP(launch_convert<T>(x, h, (size_t)M * D, (size_t)M * D, st), "post-ln input");
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& o = m->lay.layers[l];
     char* base = reinterpret_cast<char*>(kv->d_kv) + (size_t)l * kv_layer_bytes(c, B, kv->max_T);
     T* kl = reinterpret_cast<T*>(base);
     T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
-    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
-                                 pending_bias ? rpart : nullptr, ks_p, pending_bias),
-             "ln_1");
+    const float q_scale_l = c.scale_attn_by_inverse_layer_idx ? q_scale / (float)(l + 1) : q_scale;
+    if (!post)
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
+                                   pending_bias ? rpart : nullptr, ks_p, pending_bias),
+               "ln_1");
     {
-      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale, M};
+      EpiQKV<T> e{pf(m, o.b_qkv), q, kl, vtl, FastDiv(1), FastDiv(D), pos, kvT, H, ilog2(hs), q_scale_l, M};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_qkv), M, 3 * D, D, e, st), "c_attn");
     }
     GPT2_HIP(launch_attention_decode<T>(q, kl, vtl, a, part, B, H, pos + 1, kvT, hs, st), "attention decode");
@@ -427,11 +455,13 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
       EpiResidual e{pf(m, o.b_o), x, D};
       GPT2_HIP(proj_gemm<T>(a, pp<T>(m, o.w_o), M, D, D, e, st), "attn.c_proj");
     }
-    GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
-                                 split ? rpart : nullptr, ks_o, pf(m, o.b_o)),
-             "ln_2");
+    // Pre-LN: h = ln_2(x + partials).  Post-LN: x = ln_1(x + partials), h its copy.
+    GPT2_HIP(launch_layernorm<T>(x, pf(m, post ? o.ln1_g : o.ln2_g), pf(m, post ? o.ln1_b : o.ln2_b), h,
+                                 post ? x : nullptr, M, D, c.ln_eps, st, nullptr, 0, split ? rpart : nullptr, ks_o,
+                                 pf(m, o.b_o)),
+             post ? "ln_1" : "ln_2");
     {
-      EpiGelu<T> e{pf(m, o.b_fc), u, F};
+      EpiGelu<T> e{pf(m, o.b_fc), u, F, c.activation};
       GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
     }
     if (split) {
@@ -441,6 +471,13 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
       EpiResidual e{pf(m, o.b_pr), x, D};
       GPT2_HIP(proj_gemm<T>(u, pp<T>(m, o.w_pr), M, D, F, e, st), "mlp.c_proj");
     }
+    if (post) {
+      // x = ln_2(x + partials) in place; h is the next block's attention input
+      GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln2_g), pf(m, o.ln2_b), h, x, M, D, c.ln_eps, st, nullptr, 0,
+                                   pending_bias ? rpart : nullptr, ks_p, pending_bias),
+               "ln_2");
+      pending_bias = nullptr;
+    }
   }
   GPT2_HIP(launch_layernorm<T>(x, pf(m, m->lay.lnf_g), pf(m, m->lay.lnf_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
                                pending_bias ? rpart : nullptr, ks_p, pending_bias),
@@ -449,7 +486,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
     // lm_head with the arg-max epilogue (no logits stored), then one wave per row
     int2* apart = reinterpret_cast<int2*>(m->ws + W.ce_part);
     EpiArgmax e{apart, W.ce_nseg, V};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.wte), M, vocab_pad(c), D, D, D, e, st),
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st),
              "lm_head argmax");
     GPT2_HIP(launch_argmax_rows(apart, W.ce_nseg, M, V, gen->out + gen->col, gen->stride, gen->next, st), "argmax");
   } else {
@@ -492,6 +529,12 @@ gpt2_status run_init(gpt2_model* m, const float* blob, hipStream_t st) {
       return s;
   }
   if ((s = vec(m->lay.lnf_g, D)) || (s = vec(m->lay.lnf_b, D))) return s;
+  if (c.separate_head) {
+    GPT2_HIP(launch_convert<T>(blob + src, reinterpret_cast<T*>(m->params + m->lay.head), V * D,
+                               (size_t)vocab_pad(c) * D, st),
+             "init lm_head");
+    src += V * D;
+  }
   return GPT2_OK;
 }
 

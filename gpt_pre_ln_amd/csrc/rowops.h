@@ -13,7 +13,8 @@ hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x
                         int pos0, int D, hipStream_t stream);
 
 // y[m, :] = gamma * (x - mean) / sqrt(var + eps) + beta over D (biased
-// variance, two passes over the row held in registers); optional fp32 copy.
+// variance, two passes over the row held in registers); optional fp32 copy
+// y32, which may be x itself (in-place normalisation, the Post-LN wiring).
 // russellluo.com "Hidden State 如何流过 GPT-2 Block", Pre-Norm; dpshk.com 3.2.
 // prefetch / prefetch_bytes (optional; 16-byte aligned, a multiple of 16): a
 // region the kernel also reads and discards, so that the GEMMs that follow

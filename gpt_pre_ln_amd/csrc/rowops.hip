@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 template <typename T, int NV, int NMAX>
 __device__ __forceinline__ void layernorm_row(float4 (&v)[NMAX], const float4 (&gv)[NMAX], const float4 (&bv)[NMAX],
                                               int lane, int row, int D, float eps, T* __restrict__ y,
-                                              float* __restrict__ y32) {
+                                              float* y32) {
   auto valid = [&](int i) { return NV > 0 || lane * 4 + i * 256 < D; };
   float sum = 0.f;
 #pragma unroll
@@ -67,13 +67,15 @@ __device__ __forceinline__ void layernorm_row(float4 (&v)[NMAX], const float4 (&
     }
 }
 
+// y32 may be x itself (in-place normalisation): a wave loads its whole row
+// before it stores anything, and rows are disjoint between waves.
 // One wave per row; lane holds float4 groups c = lane*4 + i*256.  NV > 0:
 // exactly NV groups per lane (d_model = 256*NV, no bounds tests); NV == 0:
 // up to kMaxV4 groups with tests.
 template <typename T, int NV>
-__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* x, const float* __restrict__ gamma,
                                                          const float* __restrict__ beta, T* __restrict__ y,
-                                                         float* __restrict__ y32, int M, int D, float eps,
+                                                         float* y32, int M, int D, float eps,
                                                          const u32x4_t* __restrict__ pf, size_t pf16) {
   constexpr int NMAX = NV > 0 ? NV : kMaxV4;
   // Optional read-ahead of the next GEMMs' weights (pf16 16-byte chunks),
@@ -104,10 +106,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 // [w*q, min((w+1)*q, rks)), q = ceil(rks/4), in increasing s; wave 0 adds the
 // four wave sums in order w = 0..3 (so the result does not depend on timing).
 template <typename T, int NV>
-__global__ __launch_bounds__(256) void layernorm_residual_kernel(float* __restrict__ x,
+__global__ __launch_bounds__(256) void layernorm_residual_kernel(float* x,
                                                                   const float* __restrict__ gamma,
                                                                   const float* __restrict__ beta, T* __restrict__ y,
-                                                                  float* __restrict__ y32, int M, int D, float eps,
+                                                                  float* y32, int M, int D, float eps,
                                                                   const float* __restrict__ rpart, int rks,
                                                                   const float* __restrict__ rbias) {
   constexpr int NMAX = NV > 0 ? NV : kMaxV4;

@@ -26,11 +26,15 @@ class KVCache:
 
 class GPT2:
     def __init__(self, vocab_size, n_positions, d_model, n_head, n_layer, d_ff, dtype="bf16",
-                 max_batch=1, max_seq=None, ln_eps=1e-5, device="cuda:0", logits_dtype=None):
-        """logits_dtype: "f32" or "bf16" element type of the logits (default: dtype)."""
+                 max_batch=1, max_seq=None, ln_eps=1e-5, device="cuda:0", logits_dtype=None,
+                 activation="gelu_new", scale_attn_by_inverse_layer_idx=False, post_ln=False,
+                 tie_word_embeddings=True):
+        """logits_dtype: "f32" or "bf16" element type of the logits (default: dtype).
+        The remaining switches select the model variants (defaults: GPT-2)."""
         self.device = torch.device(device)
         self.cfg = B.make_config(vocab_size, n_positions, d_model, n_head, n_layer, d_ff, ln_eps, dtype,
-                                 logits_dtype)
+                                 logits_dtype, activation, scale_attn_by_inverse_layer_idx, post_ln,
+                                 tie_word_embeddings)
         self.dtype = dtype
         self.logits_torch_dtype = torch.bfloat16 if self.cfg.logits_dtype == B.GPT2_BF16 else torch.float32
         max_seq = max_seq or n_positions
@@ -46,7 +50,9 @@ class GPT2:
     @classmethod
     def from_shape(cls, shape, dtype, **kw):
         return cls(shape.vocab, shape.n_positions, shape.d_model, shape.n_head, shape.n_layer,
-                   shape.d_ff, dtype=dtype, ln_eps=shape.ln_eps, **kw)
+                   shape.d_ff, dtype=dtype, ln_eps=shape.ln_eps, activation=shape.activation,
+                   scale_attn_by_inverse_layer_idx=shape.scale_attn_by_inverse_layer_idx,
+                   post_ln=shape.post_ln, tie_word_embeddings=shape.tie_word_embeddings, **kw)
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -60,7 +60,18 @@ typedef enum { GPT2_F32 = 0, GPT2_BF16 = 1 } gpt2_dtype;
  * LayerNorm statistics, softmax and GELU are fp32.
  * logits_dtype: element type of the logits the forward and decode calls write
  * (GPT2_F32 or GPT2_BF16; the lm_head accumulates in fp32 either way and
- * GPT2_BF16 rounds each logit to nearest even on the store). */
+ * GPT2_BF16 rounds each logit to nearest even on the store).
+ * Variant switches (all 0 = GPT-2 as released):
+ *   activation: 0 gelu_new, the tanh form (pwwt.cn GPT2MLP); 1 the erf GELU
+ *     0.5x(1 + erf(x/sqrt 2)) the same section contrasts it with.
+ *   scale_attn_by_inverse_layer_idx: 1 divides layer l's attention scores by
+ *     l + 1 as well (pwwt.cn GPT2Config: on in the original TensorFlow code).
+ *   post_ln: 1 wires each block as H = LN_1(X + Attn(X)), X' = LN_2(H + MLP(H))
+ *     (the Post-Norm form, russellluo.com Pre-Norm section; dpshk.com 3.1);
+ *     ln_f and the head are unchanged.
+ *   separate_head: 1 gives the head its own weight lm_head.w [V, D]
+ *     (nano-ai.tech Transformer Stack: an nn.Linear head), appended to the
+ *     blob after ln_f; 0 ties it to wte. */
 typedef struct {
   int32_t vocab_size;
   int32_t n_positions;
@@ -71,6 +82,10 @@ typedef struct {
   float ln_eps;
   int32_t dtype;        /* gpt2_dtype of the arithmetic */
   int32_t logits_dtype; /* gpt2_dtype of d_logits */
+  int32_t activation;   /* 0 gelu_new, 1 erf GELU */
+  int32_t scale_attn_by_inverse_layer_idx;
+  int32_t post_ln;
+  int32_t separate_head;
 } gpt2_config;
 
 typedef struct gpt2_model gpt2_model;
@@ -91,7 +106,8 @@ typedef struct {
  * ln_1.{w,b}, attn.c_attn.{w[D,3D],b}, attn.c_proj.{w[D,D],b}, ln_2.{w,b},
  * mlp.c_fc.{w[D,F],b}, mlp.c_proj.{w[F,D],b}, then ln_f.{w,b} -- the order of
  * the safetensors key list (pwwt.cn, section on weights and architecture),
- * matrices [in, out] as Conv1D stores them. */
+ * matrices [in, out] as Conv1D stores them -- and, with separate_head, the
+ * head lm_head.w [V, D]. */
 gpt2_status gpt2_param_blob_floats(const gpt2_config* cfg, size_t* n_floats);
 
 /* Bytes of the device parameter region (converted layout, see gpt2_init_params). */

@@ -48,7 +48,25 @@ def test_exports_every_declared_symbol(B):
 
 def _cfg(B, shape, dtype):
     return B.make_config(shape.vocab, shape.n_positions, shape.d_model, shape.n_head, shape.n_layer,
-                         shape.d_ff, shape.ln_eps, dtype)
+                         shape.d_ff, shape.ln_eps, dtype, None, shape.activation,
+                         shape.scale_attn_by_inverse_layer_idx, shape.post_ln, shape.tie_word_embeddings)
+
+
+def test_variant_blob_and_region_sizes(B):
+    """A separate head adds V*D floats to the blob and V_pad*D elements to the
+    device region; the other switches change no size."""
+    import dataclasses
+    s = W.ModelShape(vocab=1000, n_positions=128, d_model=128, n_head=2, n_layer=2, d_ff=512)
+    base = _cfg(B, s, "bf16")
+    for kw in (dict(post_ln=True), dict(activation="gelu"), dict(scale_attn_by_inverse_layer_idx=True)):
+        v = _cfg(B, dataclasses.replace(s, **kw), "bf16")
+        assert B.gpt2_param_blob_floats(v) == B.gpt2_param_blob_floats(base) == W.param_count(s)
+        assert B.gpt2_param_bytes(v) == B.gpt2_param_bytes(base)
+    su = dataclasses.replace(s, tie_word_embeddings=False)
+    u = _cfg(B, su, "bf16")
+    assert B.gpt2_param_blob_floats(u) == W.param_count(su) == W.param_count(s) + 1000 * 128
+    assert B.gpt2_param_bytes(u) == B.gpt2_param_bytes(base) + 1024 * 128 * 2
+    assert list(W.unpack(W.make_params(su, W.Init(0.02, 0.02, 0.0, (1.0, 0.0), (0.0, 0.0)), 1), su))[-1] == "lm_head.w"
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
@@ -78,6 +96,10 @@ def test_kv_cache_bytes(B):
     (dict(n_layer=0), "GPT2_ERR_SHAPE"),
     (dict(d_ff=100), "GPT2_ERR_UNSUPPORTED"),
     (dict(n_positions=5000), "GPT2_ERR_UNSUPPORTED"),
+    (dict(activation=2), "GPT2_ERR_UNSUPPORTED"),
+    (dict(post_ln=-1), "GPT2_ERR_UNSUPPORTED"),
+    (dict(separate_head=3), "GPT2_ERR_UNSUPPORTED"),
+    (dict(scale_attn_by_inverse_layer_idx=2), "GPT2_ERR_UNSUPPORTED"),
 ])
 def test_config_validation(B, change, status):
     base = dict(vocab_size=1000, n_positions=128, d_model=128, n_head=2, n_layer=2, d_ff=512, ln_eps=1e-5,
