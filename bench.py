@@ -70,11 +70,11 @@ def class_work(shape, B, T, cls):
 
 
 # kernel class -> kernel name as rocprofv3 reports it (short form)
-# kernel of each class in the traffic summary (the schedule-knob field of the
-# GEMM template may vary)
+# kernel of each class in the traffic summary (the tile and schedule-knob
+# fields of the GEMM template may vary)
 TRAFFIC_KERNELS = {"lm_head_gemm": r"void gemm_kernel<bf16_t, 256, 256, 2, 4, 2, \d+, EpiLogits<bf16_t> >",
-                   "fc_gemm": r"void gemm_kernel<bf16_t, 128, 128, 2, 2, 2, \d+, EpiGelu<bf16_t> >",
-                   "qkv_gemm": r"void gemm_kernel<bf16_t, 128, 128, 2, 2, 2, \d+, EpiQKV<bf16_t> >",
+                   "fc_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, 2, 2, 2, \d+, EpiGelu<bf16_t> >",
+                   "qkv_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, 2, 2, 2, \d+, EpiQKV<bf16_t> >",
                    "attention": r"void attn_prefill_kernel<bf16_t, 64>",
                    "layernorm": r"void layernorm_kernel<bf16_t, 3>"}
 

@@ -445,6 +445,7 @@ int gemm_slice_width(GemmTile tile) {
     case kTile256x256: return 256 / 4;
     case kTile64x64: return 64 / 2;
     case kTile32x64: return 64 / 2;
+    case kTile64x128: return 128 / 2;
     case kTile128x128:
     default: return 128 / 2;
   }
@@ -460,6 +461,8 @@ hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int 
       return launch_tile<T, 64, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile32x64:
       return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
+    case kTile64x128:
+      return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x128:
     default:
       return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);

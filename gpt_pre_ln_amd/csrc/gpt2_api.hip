@@ -114,12 +114,26 @@ size_t blob_floats(const gpt2_config& c) {
 }
 
 // Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
-// 256 CUs many times over (the lm_head); 128x128 otherwise (2 blocks per CU).
-GemmTile pick_tile(int M, int N) {
+// 256 CUs many times over (the lm_head); 128x128 (2 blocks per CU) or 64x128
+// (3 blocks per CU) otherwise.
+GemmTile pick_tile(int M, int N, int K) {
   if (M <= 32) return kTile32x64;
   if (M <= 64) return kTile64x64;
   const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 8 * 256) return kTile256x256;
+  // Short k loops (K <= 1024): 64x128 tiles run 3 blocks per CU against 2 for
+  // 128x128; take the one whose busiest CU computes fewer output elements
+  // (ties to the larger tile).  GPT-2 small: qkv and attn.c_proj take 64x128
+  // (the 128x128 grids leave the last round a quarter or half full); with
+  // K = 3072 the smaller tile's extra operand traffic outweighs the balance
+  // (mlp.c_proj measured 6 % slower), so long k loops keep 128x128.
+  if (K <= 1024) {
+    constexpr long kCUs = 256;
+    const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+    const long t64 = (long)((M + 63) / 64) * ((N + 127) / 128);
+    const long w128 = (t128 + kCUs - 1) / kCUs * 128 * 128, w64 = (t64 + kCUs - 1) / kCUs * 64 * 128;
+    if (w64 < w128) return kTile64x128;
+  }
   return kTile128x128;
 }
 
@@ -159,7 +173,7 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   W.gen_tok = take(M * 4);
   const size_t end = off;
   off = W.q;
-  W.ce_nseg = vocab_pad(c) / gemm_slice_width(pick_tile((int)M, vocab_pad(c)));
+  W.ce_nseg = vocab_pad(c) / gemm_slice_width(pick_tile((int)M, vocab_pad(c), c.d_model));
   W.ce_part = take(M * W.ce_nseg * sizeof(float2));
   W.ce_tgt = take(M * 4);
   W.ce_loss = take(M * 4);
@@ -237,7 +251,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 template <typename T, class Epi>
 hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& epi, hipStream_t st) {
   if (M <= 32) return launch_gemm_skinny<T>(A, Bw, M, N, K, K, K, epi, st);
-  return launch_gemm<T>(pick_tile(M, N), A, Bw, M, N, K, K, K, epi, st);
+  return launch_gemm<T>(pick_tile(M, N, K), A, Bw, M, N, K, K, K, epi, st);
 }
 
 // Weight read-ahead.  Inside a forward a layer's weight matrices have dropped
@@ -255,7 +269,7 @@ template <typename T>
 hipError_t launch_lm_head(gpt2_model* m, const T* h, void* logits, int M, hipStream_t st) {
   const gpt2_config& c = m->cfg;
   const int V = c.vocab_size, D = c.d_model;
-  const GemmTile tile = pick_tile(M, vocab_pad(c));
+  const GemmTile tile = pick_tile(M, vocab_pad(c), D);
   if (c.logits_dtype == GPT2_BF16) {
     EpiLogits<bf16_t> e{static_cast<bf16_t*>(logits), V, V};
     return launch_gemm<T>(tile, h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st);
@@ -385,7 +399,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     float* per = loss->token_loss ? loss->token_loss : reinterpret_cast<float*>(m->ws + W.ce_loss);
     {
       TimedScope ts(m, kLMHead, st);
-      const GemmTile tile = pick_tile(M, vocab_pad(c));
+      const GemmTile tile = pick_tile(M, vocab_pad(c), D);
       EpiCE e{part, W.ce_nseg, loss->labels, FastDiv((uint32_t)T_seq), V, tgt};
       GPT2_HIP(launch_gemm<T>(tile, h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st), "lm_head loss");
     }
@@ -486,7 +500,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
     // lm_head with the arg-max epilogue (no logits stored), then one wave per row
     int2* apart = reinterpret_cast<int2*>(m->ws + W.ce_part);
     EpiArgmax e{apart, W.ce_nseg, V};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c)), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st),
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c), D), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st),
              "lm_head argmax");
     GPT2_HIP(launch_argmax_rows(apart, W.ce_nseg, M, V, gen->out + gen->col, gen->stride, gen->next, st), "argmax");
   } else {
