@@ -313,3 +313,129 @@ def generate_greedy(P: dict, prompt: np.ndarray, n_steps: int) -> np.ndarray:
         out[:, i] = last.argmax(axis=-1)          # numpy: first maximum wins
         seq = np.concatenate([seq, out[:, i:i + 1]], axis=1)
     return out
+
+
+# --------------------------------------------------------------------------
+# Backward of one block
+# --------------------------------------------------------------------------
+
+
+def gelu_new_grad(x: np.ndarray) -> np.ndarray:
+    """d/dx gelu_new(x) = 0.5 (1 + t) + 0.5 x (1 - t^2) sqrt(2/pi) (1 + 3 c x^2),
+    t = tanh(sqrt(2/pi) (x + c x^3)), c = 0.044715 (the derivative of [HFsrc]
+    GPT2MLP's NewGELUActivation)."""
+    x = np.asarray(x, dtype=np.float64)
+    k = np.sqrt(2.0 / np.pi)
+    t = np.tanh(k * (x + 0.044715 * x * x * x))
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * k * (1.0 + 3.0 * 0.044715 * x * x)
+
+
+def gelu_erf_grad(x: np.ndarray) -> np.ndarray:
+    """d/dx 0.5 x (1 + erf(x/sqrt 2)) = Phi(x) + x phi(x) (standard normal cdf / pdf)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + erf(x / np.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / np.sqrt(2.0 * np.pi)
+
+
+def layer_norm_backward(dh: np.ndarray, x: np.ndarray, gamma: np.ndarray, eps: float = 1e-5):
+    """Gradients of h = gamma * xhat + beta, xhat = (x - mu) / sqrt(var + eps),
+    over the last axis: returns (dx, dgamma, dbeta) with dgamma, dbeta summed
+    over every leading axis.  [llmc] 5.3: the mean, the variance and the
+    normalised value are coupled --
+      dxhat = dh * gamma,
+      dx = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)),
+    dgamma = sum dh * xhat, dbeta = sum dh."""
+    x = np.asarray(x, np.float64)
+    dh = np.asarray(dh, np.float64)
+    d = x.shape[-1]
+    mu = x.sum(axis=-1, keepdims=True) / d
+    xc = x - mu
+    rstd = 1.0 / np.sqrt((xc * xc).sum(axis=-1, keepdims=True) / d + eps)
+    xhat = xc * rstd
+    dxhat = dh * np.asarray(gamma, np.float64)
+    dx = rstd * (dxhat - dxhat.mean(axis=-1, keepdims=True) - xhat * (dxhat * xhat).mean(axis=-1, keepdims=True))
+    lead = tuple(range(dh.ndim - 1))
+    return dx, (dh * xhat).sum(axis=lead), dh.sum(axis=lead)
+
+
+def block_backward(x: np.ndarray, dy: np.ndarray, P: dict, l: int):
+    """Backward of Pre-LN block l on one sequence: x [T, D] is the block input,
+    dy [T, D] the gradient of a loss with respect to the block output.
+    Returns (dx [T, D], grads) with grads keyed like the parameters
+    ("h.{l}.ln_1.w", ...), matrices in the blob's [in, out] orientation.
+
+    The forward of block_forward taken in reverse, one step at a time ([llmc]
+    5.3 on the two delicate steps):
+      MLP:        y = x_h + u W_pr + b_pr,  u = act(g),  g = h2 W_fc + b_fc,
+                  h2 = LN_2(x_h)
+      attention:  x_h = x + a W_o + b_o,  a = merge_heads(p v),
+                  p = softmax(s) over keys j <= i (masked entries exactly 0,
+                  so their gradient is exactly 0), s = q k^T * scale,
+                  [q | k | v] = h1 W_qkv + b_qkv,  h1 = LN_1(x)
+    Softmax backward: ds = p * (dp - sum_j dp * p).
+    """
+    s = P["_shape"]
+    if getattr(s, "post_ln", False):
+        raise NotImplementedError("backward of the Post-LN wiring is not built")
+    D, H = s.d_model, s.n_head
+    hs = D // H
+    T = x.shape[0]
+    pre = f"h.{l}."
+    g_ = lambda k: P[pre + k]
+    erf_form = getattr(s, "activation", "gelu_new") == "gelu"
+    act = gelu_erf if erf_form else gelu_new
+    act_grad = gelu_erf_grad if erf_form else gelu_new_grad
+    scale = 1.0 / np.sqrt(float(hs))
+    if getattr(s, "scale_attn_by_inverse_layer_idx", False):
+        scale = scale / float(l + 1)
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    # forward, keeping what the backward needs
+    h1 = layer_norm(x, g_("ln_1.w"), g_("ln_1.b"), s.ln_eps)
+    qkv = h1 @ g_("attn.c_attn.w") + g_("attn.c_attn.b")
+    split = lambda t: t.reshape(T, H, hs).transpose(1, 0, 2)    # [H, T, hs]
+    q, k, v = split(qkv[:, :D]), split(qkv[:, D:2 * D]), split(qkv[:, 2 * D:])
+    o, p = causal_attention(q, k, v, scale=scale, return_probs=True)
+    a = o.transpose(1, 0, 2).reshape(T, D)
+    x_h = x + a @ g_("attn.c_proj.w") + g_("attn.c_proj.b")
+    h2 = layer_norm(x_h, g_("ln_2.w"), g_("ln_2.b"), s.ln_eps)
+    gpre = h2 @ g_("mlp.c_fc.w") + g_("mlp.c_fc.b")
+    u = act(gpre)
+    grads = {}
+    # MLP
+    grads[pre + "mlp.c_proj.b"] = dy.sum(axis=0)
+    grads[pre + "mlp.c_proj.w"] = u.T @ dy
+    dgpre = (dy @ g_("mlp.c_proj.w").T) * act_grad(gpre)
+    grads[pre + "mlp.c_fc.b"] = dgpre.sum(axis=0)
+    grads[pre + "mlp.c_fc.w"] = h2.T @ dgpre
+    dh2 = dgpre @ g_("mlp.c_fc.w").T
+    dxh_ln, grads[pre + "ln_2.w"], grads[pre + "ln_2.b"] = layer_norm_backward(dh2, x_h, g_("ln_2.w"), s.ln_eps)
+    dx_h = dy + dxh_ln
+    # attention
+    grads[pre + "attn.c_proj.b"] = dx_h.sum(axis=0)
+    grads[pre + "attn.c_proj.w"] = a.T @ dx_h
+    do = split(dx_h @ g_("attn.c_proj.w").T)                      # [H, T, hs]
+    dv = np.einsum("hij,hid->hjd", p, do)
+    dp = np.einsum("hid,hjd->hij", do, v)
+    ds = p * (dp - (dp * p).sum(axis=-1, keepdims=True))           # 0 wherever p is masked
+    dq = np.einsum("hij,hjd->hid", ds, k) * scale
+    dk = np.einsum("hij,hid->hjd", ds, q) * scale
+    merge = lambda t: t.transpose(1, 0, 2).reshape(T, D)
+    dqkv = np.concatenate([merge(dq), merge(dk), merge(dv)], axis=1)
+    grads[pre + "attn.c_attn.b"] = dqkv.sum(axis=0)
+    grads[pre + "attn.c_attn.w"] = h1.T @ dqkv
+    dh1 = dqkv @ g_("attn.c_attn.w").T
+    dx_ln, grads[pre + "ln_1.w"], grads[pre + "ln_1.b"] = layer_norm_backward(dh1, x, g_("ln_1.w"), s.ln_eps)
+    return dx_h + dx_ln, grads
+
+
+def block_backward_batch(x: np.ndarray, dy: np.ndarray, P: dict, l: int):
+    """block_backward over a batch x, dy [B, T, D]: dx [B, T, D] and parameter
+    gradients summed over the sequences (sequences are independent)."""
+    dxs, total = [], {}
+    for b in range(x.shape[0]):
+        dx, g = block_backward(x[b], dy[b], P, l)
+        dxs.append(dx)
+        for k2, v2 in g.items():
+            total[k2] = total[k2] + v2 if k2 in total else v2
+    return np.stack(dxs), total

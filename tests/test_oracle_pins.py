@@ -591,3 +591,98 @@ def test_layer_scale_leaves_layer_zero_and_untied_equal_head_is_tied():
     Pt.pop("lm_head.w")
     Pt["_shape"] = dataclasses.replace(su, tie_word_embeddings=True)
     np.testing.assert_array_equal(oracle.forward(Pu, ids), oracle.forward(Pt, ids))
+
+
+# ---------------------------------------------------------------- block backward
+
+
+def _bwd_shape(**kw):
+    import dataclasses
+    s = W.ModelShape(vocab=11, n_positions=8, d_model=8, n_head=2, n_layer=2, d_ff=16)
+    return dataclasses.replace(s, **kw)
+
+
+def _bwd_case(seed, **kw):
+    s = _bwd_shape(**kw)
+    init = W.Init(w_std=0.5, proj_std=0.5, bias_std=0.2, gamma=(1.0, 0.3), beta=(0.0, 0.3))
+    blob = W.make_params(s, init, seed)
+    P = oracle.prepare_params(blob, s, "f32")
+    rng = np.random.default_rng(seed + 1)
+    x = rng.normal(0.0, 1.0, size=(5, s.d_model))
+    r = rng.normal(0.0, 1.0, size=(5, s.d_model))
+    return s, P, x, r
+
+
+@pytest.mark.parametrize("layer,kw", [(0, {}), (1, dict(activation="gelu", scale_attn_by_inverse_layer_idx=True))])
+def test_block_backward_finite_differences(layer, kw):
+    """Central differences (fp64, eps 1e-5) of L = sum(block(x) * r) against
+    every entry of dx and of every parameter gradient of the block."""
+    s, P, x, r = _bwd_case(61 + layer, **kw)
+    dx, grads = oracle.block_backward(x, r, P, layer)
+    L = lambda PP, xx: float((oracle.block_forward(xx, PP, layer) * r).sum())
+    eps = 1e-5
+    fd = np.empty_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += eps
+        xm[idx] -= eps
+        fd[idx] = (L(P, xp) - L(P, xm)) / (2 * eps)
+    np.testing.assert_allclose(dx, fd, rtol=1e-6, atol=1e-8)
+    assert len(grads) == 12
+    for key, g in grads.items():
+        fdp = np.empty_like(P[key])
+        for idx in np.ndindex(P[key].shape):
+            Pp, Pm = dict(P), dict(P)
+            Pp[key] = P[key].copy()
+            Pm[key] = P[key].copy()
+            Pp[key][idx] += eps
+            Pm[key][idx] -= eps
+            fdp[idx] = (L(Pp, x) - L(Pm, x)) / (2 * eps)
+        np.testing.assert_allclose(g, fdp, rtol=1e-6, atol=1e-8, err_msg=key)
+
+
+def test_block_backward_vs_torch_autograd():
+    """Library routine: torch autograd (fp64) through the functional block."""
+    s = _tiny_shape(n_head=4, d=64, L=2, vocab=97, npos=40)
+    _, P = _random_params(s, 63)
+    rng = np.random.default_rng(64)
+    x = rng.normal(0, 1, size=(2, 19, 64))
+    dy = rng.normal(0, 1, size=(2, 19, 64))
+    l = 1
+    dx, grads = oracle.block_backward_batch(x, dy, P, l)
+    D, H = 64, 4
+    pt = {k: torch.tensor(P[f"h.{l}.{k}"], requires_grad=True) for k in W.LAYER_TENSORS}
+    xt = torch.tensor(x, requires_grad=True)
+    h = F.layer_norm(xt, (D,), pt["ln_1.w"], pt["ln_1.b"], s.ln_eps)
+    qkv = F.linear(h, pt["attn.c_attn.w"].T, pt["attn.c_attn.b"])
+    q, k, v = qkv.split(D, dim=2)
+    heads = lambda z: z.view(2, 19, H, D // H).permute(0, 2, 1, 3)
+    a = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True)
+    a = a.permute(0, 2, 1, 3).reshape(2, 19, D)
+    xh = xt + F.linear(a, pt["attn.c_proj.w"].T, pt["attn.c_proj.b"])
+    h2 = F.layer_norm(xh, (D,), pt["ln_2.w"], pt["ln_2.b"], s.ln_eps)
+    u = F.gelu(F.linear(h2, pt["mlp.c_fc.w"].T, pt["mlp.c_fc.b"]), approximate="tanh")
+    y = xh + F.linear(u, pt["mlp.c_proj.w"].T, pt["mlp.c_proj.b"])
+    y.backward(torch.tensor(dy))
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    for k in W.LAYER_TENSORS:
+        np.testing.assert_allclose(grads[f"h.{l}.{k}"], pt[k].grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=k)
+
+
+def test_block_backward_causal_zeros_and_ln_invariant():
+    """A gradient only at position 0 reaches position 0 only (masked keys carry
+    exactly zero gradient); LayerNorm's input gradient sums to zero per row."""
+    s, P, x, r = _bwd_case(65)
+    dy = np.zeros_like(r)
+    dy[0] = r[0]
+    dx, _ = oracle.block_backward(x, dy, P, 0)
+    assert (dx[1:] == 0).all() and np.abs(dx[0]).max() > 0
+    dxl, _, _ = oracle.layer_norm_backward(r, x, P["h.0.ln_1.w"])
+    np.testing.assert_allclose(dxl.sum(axis=-1), 0.0, atol=1e-13)
+
+
+def test_gelu_grads_vs_torch_autograd():
+    x = torch.linspace(-7, 7, 2001, dtype=torch.float64, requires_grad=True)
+    for approx, fn in (("tanh", oracle.gelu_new_grad), ("none", oracle.gelu_erf_grad)):
+        g, = torch.autograd.grad(F.gelu(x, approximate=approx).sum(), x)
+        np.testing.assert_allclose(fn(x.detach().numpy()), g.numpy(), rtol=1e-13, atol=1e-14)
