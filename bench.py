@@ -45,6 +45,19 @@ def forward_flops(shape, B, T):
     return L * (per_layer + attn) + 2 * M * D * V
 
 
+def backward_block_flops(shape, B, T):
+    """Algorithmic FLOPs of one block's backward: the input- and weight-gradient
+    products of the four projections (twice their forward FLOPs) and the four
+    causal attention products dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q
+    (keys j <= i only)."""
+    D, F, H = shape.d_model, shape.d_ff, shape.n_head
+    hs = D // H
+    M = B * T
+    proj = 2 * M * D * (3 * D + D + F + F)
+    attn = 4 * 2 * hs * (T * (T + 1) // 2) * B * H
+    return 2 * proj + attn
+
+
 def class_work(shape, B, T, cls):
     """(algorithmic units per launch, unit, bound) for one kernel class."""
     D, F, H, V = shape.d_model, shape.d_ff, shape.n_head, shape.vocab
@@ -255,6 +268,29 @@ def main():
                     "value": round(B * T / el_v, 1), "unit": "tokens/s", "ms_per_step": round(el_v * 1e3, 4)}
     del vmodel
 
+    # backward of one block (gpt2_block_backward, layer 0) on the same batch:
+    # seeded fp32 block input and output gradient
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    xb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
+    dyb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
+    dxb, gb = model.block_backward(0, xb, dyb)
+    for _ in range(max(1, args.warmup // 2)):
+        model.block_backward(0, xb, dyb, out_dx=dxb, out_grads=gb)
+    torch.cuda.synchronize()
+    nb = max(2, args.steps // 4)
+    t4 = time.perf_counter()
+    for _ in range(nb):
+        model.block_backward(0, xb, dyb, out_dx=dxb, out_grads=gb)
+    torch.cuda.synchronize()
+    el_b = (time.perf_counter() - t4) / nb
+    bflop = backward_block_flops(w.shape, B, T)
+    block_backward = {"layer": 0, "ms_per_call": round(el_b * 1e3, 4), "algorithmic_tflop": round(bflop / 1e12, 4),
+                      "achieved_tflops": round(bflop / el_b / 1e12, 2),
+                      "note": "includes the recomputed forward of the block"}
+    del xb, dyb, dxb, gb
+    model._bwd_ws = None
+
     # the same forward storing fp32 logits (reported beside the headline value)
     alt = None
     if logits_dtype != "f32":
@@ -296,6 +332,7 @@ def main():
     }
     out["loss_step"] = loss_step
     out["variant_step"] = variant_step
+    out["block_backward"] = block_backward
     if alt is not None:
         out["fp32_logits"] = alt
     if not args.no_cpu_baseline:

@@ -73,6 +73,10 @@ _SIG = {
     "gpt2_forward_loss": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
     "gpt2_generate": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, ctypes.c_int32, _P, _P]),
+    "gpt2_block_backward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32,
+                                                           ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt2_block_backward": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
     "gpt2_set_trace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "gpt2_timing_enable": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
     "gpt2_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -178,6 +182,19 @@ def gpt2_decode_step(handle, kv, d_new_tokens: int, d_logits: int, stream: int):
 
 def gpt2_generate(handle, kv, d_tokens: int, n_steps: int, d_out_tokens: int, stream: int):
     _check(load().gpt2_generate(handle, ctypes.byref(kv), d_tokens, n_steps, d_out_tokens, stream), "gpt2_generate")
+
+
+def gpt2_block_backward_workspace_bytes(cfg, B: int, T: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().gpt2_block_backward_workspace_bytes(ctypes.byref(cfg), B, T, ctypes.byref(n)),
+           "gpt2_block_backward_workspace_bytes")
+    return n.value
+
+
+def gpt2_block_backward(handle, layer: int, B: int, T: int, d_x: int, d_dy: int, d_dx: int, d_grads: int,
+                        d_ws: int, ws_bytes: int, stream: int):
+    _check(load().gpt2_block_backward(handle, layer, B, T, d_x, d_dy, d_dx, d_grads, d_ws, ws_bytes, stream),
+           "gpt2_block_backward")
 
 
 def gpt2_set_trace(handle, d_trace, n_floats: int):

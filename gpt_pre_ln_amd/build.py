@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgpt2.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["gpt2_api.hip", "gemm.hip", "attention.hip", "rowops.hip"]
+SOURCES = ["gpt2_api.hip", "gemm.hip", "attention.hip", "rowops.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [

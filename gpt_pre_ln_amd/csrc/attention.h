@@ -15,9 +15,11 @@ namespace gpt2 {
 
 // Prefill / full forward.  q: [B*H][Tq][hs] at positions 0..Tq-1; k: [B*H][kvT][hs];
 // vt: [B*H][hs][kvT]; out: [B*Tq][D] with head h in columns h*hs .. h*hs+hs-1.
+// lse (optional): [B*H][Tq], log(sum_j exp(s_ij)) of each query's scores
+// s = q k^T (q pre-scaled), for the backward pass.
 template <typename T>
 hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out, int B, int H, int Tq,
-                                    int kvT, int hs, hipStream_t stream);
+                                    int kvT, int hs, hipStream_t stream, float* lse = nullptr);
 
 // Decode: one query per (b, h) at position pos = n_keys - 1, attending keys
 // 0..n_keys-1 of the cache.  q: [B*H][hs]; k: [B*H][kvT][hs]; vt: [B*H][hs][kvT];

@@ -48,7 +48,7 @@ __device__ __forceinline__ void barrier_nofence() {
 template <typename T, int HS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, T* __restrict__ out, int BH, int H,
-    int Tq, int kvT, int n_qtiles) {
+    int Tq, int kvT, int n_qtiles, float* __restrict__ lse) {
   constexpr int QW = 32, NW = 4, BQ = QW * NW, BKEYS = 64;
   constexpr int ESZ = (int)sizeof(T);
   constexpr int KROWB = HS * ESZ, KCH = KROWB / 16;     // K tile rows (keys)
@@ -298,6 +298,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   for (int qf = 0; qf < QF; ++qf) {
     const float inv = 1.0f / lsum[qf][0];
     const int qi = q0w + qf * 16 + lr;
+    // optional log-sum-exp of the query's scores (for the backward pass)
+    if (lse && lg == 0 && qi < Tq) lse[((size_t)b * H + h) * Tq + qi] = m_run[qf] + logf(lsum[qf][0]);
     if (qi < Tq) {
       T* dst = out + ((size_t)b * Tq + qi) * D + h * HS;
 #pragma unroll
@@ -455,15 +457,15 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const float* __re
 
 template <typename T>
 hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out, int B, int H, int Tq,
-                                    int kvT, int hs, hipStream_t stream) {
+                                    int kvT, int hs, hipStream_t stream, float* lse) {
   const int n_qtiles = (Tq + 127) / 128;
   dim3 grid(B * H * n_qtiles), block(256);
   if (hs == 64) {
     hipLaunchKernelGGL((attn_prefill_kernel<T, 64>), grid, block, 0, stream, q, k, vt, out, B * H, H, Tq, kvT,
-                       n_qtiles);
+                       n_qtiles, lse);
   } else if (hs == 16 && sizeof(T) == 4) {
     hipLaunchKernelGGL((attn_prefill_kernel<T, (sizeof(T) == 4 ? 16 : 64)>), grid, block, 0, stream, q, k,
-                       vt, out, B * H, H, Tq, kvT, n_qtiles);
+                       vt, out, B * H, H, Tq, kvT, n_qtiles, lse);
   } else {
     return hipErrorInvalidValue;
   }
@@ -494,9 +496,9 @@ hipError_t launch_attention_decode(const T* q, const T* k, const T* vt, T* out, 
 }
 
 template hipError_t launch_attention_prefill<float>(const float*, const float*, const float*, float*, int, int,
-                                                    int, int, int, hipStream_t);
+                                                    int, int, int, hipStream_t, float*);
 template hipError_t launch_attention_prefill<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*, int,
-                                                     int, int, int, int, hipStream_t);
+                                                     int, int, int, int, hipStream_t, float*);
 template hipError_t launch_attention_decode<float>(const float*, const float*, const float*, float*, float*, int,
                                                    int, int, int, int, hipStream_t);
 template hipError_t launch_attention_decode<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*,

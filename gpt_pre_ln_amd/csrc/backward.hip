@@ -1,0 +1,429 @@
+// Block backward kernels (see backward.h).
+#include "backward.h"
+
+namespace gpt2 {
+
+namespace {
+
+constexpr int kColChunks = 64;  // row chunks of the first column-sum pass
+
+// 32x32 tile transpose through LDS; 256 threads = 32 x 8.  Tiles cover dst
+// rows c and dst columns r < ld_dst (the padding columns are written as 0).
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void transpose_kernel(const Tin* __restrict__ src, int R, int C,
+                                                         Tout* __restrict__ dst, int ld_dst) {
+  __shared__ float tile[32][33];
+  const int r0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? Elem<Tin>::to_f32(src[(size_t)r * C + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < ld_dst) dst[(size_t)c * ld_dst + r] = Elem<Tout>::from_f32(tile[tx][i]);
+  }
+}
+
+// First pass: block (column block nb, row chunk rc); 256 threads = 4 row
+// lanes x 64 columns; lane ry adds rows ry, ry+4, ... of the chunk in order,
+// then the four lane sums are added in order.
+template <typename Tin, bool kXhat>
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restrict__ src, int M, int N,
+                                                              float* __restrict__ part, const float* __restrict__ x,
+                                                              const float* __restrict__ mu,
+                                                              const float* __restrict__ rstd) {
+  __shared__ float red[4][64];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + cx, rc = blockIdx.y;
+  const int rows = (M + kColChunks - 1) / kColChunks;
+  const int m0 = rc * rows, m1 = min(M, m0 + rows);
+  float s = 0.f;
+  if (n < N) {
+    for (int m = m0 + ry; m < m1; m += 4) {
+      float v = Elem<Tin>::to_f32(src[(size_t)m * N + n]);
+      if constexpr (kXhat) v *= (x[(size_t)m * N + n] - mu[m]) * rstd[m];
+      s += v;
+    }
+  }
+  red[ry][cx] = s;
+  __syncthreads();
+  if (ry == 0 && n < N) part[(size_t)rc * N + n] = ((red[0][cx] + red[1][cx]) + red[2][cx]) + red[3][cx];
+}
+
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int N,
+                                                            float* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int rc = 0; rc < kColChunks; ++rc) s += part[(size_t)rc * N + n];
+  out[n] = s;
+}
+
+// One wave per row; lane holds float4 groups c = lane*4 + i*256 (as the
+// forward LayerNorm).
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void layernorm_backward_kernel(
+    const float* __restrict__ x, const float* __restrict__ dh, const float* __restrict__ gamma,
+    const float* __restrict__ resid, float* __restrict__ out, T* __restrict__ out_t, float* __restrict__ mu_out,
+    float* __restrict__ rstd_out, int M, int D, float eps) {
+  constexpr int kMax = 8;
+  constexpr int NMAX = NV > 0 ? NV : kMax;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  auto valid = [&](int i) { return NV > 0 || lane * 4 + i * 256 < D; };
+  const size_t base = (size_t)row * D;
+  float4 xv[NMAX], gv[NMAX];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      xv[i] = *reinterpret_cast<const float4*>(x + base + lane * 4 + i * 256);
+      sum += (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+    }
+  const float mu = wave_sum(sum) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      xv[i] = make_float4(xv[i].x - mu, xv[i].y - mu, xv[i].z - mu, xv[i].w - mu);
+      sq += (xv[i].x * xv[i].x + xv[i].y * xv[i].y) + (xv[i].z * xv[i].z + xv[i].w * xv[i].w);
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + eps);
+  // g = dh * gamma; a = mean(g), b = mean(g * xhat)
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      const int c = lane * 4 + i * 256;
+      const float4 d = *reinterpret_cast<const float4*>(dh + base + c);
+      const float4 gm = *reinterpret_cast<const float4*>(gamma + c);
+      gv[i] = make_float4(d.x * gm.x, d.y * gm.y, d.z * gm.z, d.w * gm.w);
+      xv[i] = make_float4(xv[i].x * rstd, xv[i].y * rstd, xv[i].z * rstd, xv[i].w * rstd);  // xhat
+      sa += (gv[i].x + gv[i].y) + (gv[i].z + gv[i].w);
+      sb += (gv[i].x * xv[i].x + gv[i].y * xv[i].y) + (gv[i].z * xv[i].z + gv[i].w * xv[i].w);
+    }
+  const float a = wave_sum(sa) / (float)D, bm = wave_sum(sb) / (float)D;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i)
+    if (valid(i)) {
+      const int c = lane * 4 + i * 256;
+      const float4 r = *reinterpret_cast<const float4*>(resid + base + c);
+      const float4 o = make_float4(r.x + rstd * (gv[i].x - a - xv[i].x * bm), r.y + rstd * (gv[i].y - a - xv[i].y * bm),
+                                   r.z + rstd * (gv[i].z - a - xv[i].z * bm), r.w + rstd * (gv[i].w - a - xv[i].w * bm));
+      *reinterpret_cast<float4*>(out + base + c) = o;
+      if (out_t) Elem<T>::store4(out_t + base + c, o.x, o.y, o.z, o.w);
+    }
+  if (lane == 0) {
+    if (mu_out) mu_out[row] = mu;
+    if (rstd_out) rstd_out[row] = rstd;
+  }
+}
+
+// dvec[bh][i] = sum_d dout[b*T + i][h*HS + d] * o[b*T + i][h*HS + d]: one wave per (bh, i).
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dvec_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                             float* __restrict__ dvec, int B, int H, int T_seq) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= B * H * T_seq) return;
+  const int bh = r / T_seq, i = r - bh * T_seq;
+  const int b = bh / H, h = bh - b * H;
+  const size_t off = ((size_t)b * T_seq + i) * (H * HS) + h * HS + lane;
+  const float v = lane < HS ? Elem<T>::to_f32(dout[off]) * Elem<T>::to_f32(o[off]) : 0.f;
+  const float s = wave_sum(v);
+  if (lane == 0) dvec[r] = s;
+}
+
+constexpr int kBT = 64;  // keys per key tile, queries per query tile
+
+// Shared pieces of the two attention-backward kernels: 256 threads,
+// ty = tid / 16 owns rows ty*4 .. +3 of a 64 x 64 score tile, tx = tid % 16
+// its columns tx*4 .. +3.
+template <int HS>
+struct AttnBwdSmem {
+  float Ks[kBT][HS + 1];
+  float Vs[kBT][HS + 1];
+  float Qs[kBT][HS + 1];
+  float dOs[kBT][HS + 1];
+  float Ps[kBT][kBT + 1];
+  float dSs[kBT][kBT + 1];
+  float lse[kBT];
+  float dv[kBT];
+};
+
+template <typename T, int HS>
+__device__ __forceinline__ void load_kv_tile(AttnBwdSmem<HS>& sm, const T* k, const T* vt, int bh, int kvT, int j0,
+                                             int T_seq) {
+  for (int e = threadIdx.x; e < kBT * HS; e += 256) {
+    const int j = e / HS, d = e - j * HS;  // K rows are HS-contiguous
+    sm.Ks[j][d] = j0 + j < T_seq ? Elem<T>::to_f32(k[((size_t)bh * kvT + j0 + j) * HS + d]) : 0.f;
+  }
+  for (int e = threadIdx.x; e < kBT * HS; e += 256) {
+    const int d = e / kBT, j = e - d * kBT;  // V^T rows are key-contiguous
+    sm.Vs[j][d] = j0 + j < T_seq ? Elem<T>::to_f32(vt[((size_t)bh * HS + d) * kvT + j0 + j]) : 0.f;
+  }
+}
+
+template <typename T, int HS>
+__device__ __forceinline__ void load_q_tile(AttnBwdSmem<HS>& sm, const T* q, const T* dout, const float* lse,
+                                            const float* dvec, int bh, int b, int h, int H, int i0, int T_seq) {
+  for (int e = threadIdx.x; e < kBT * HS; e += 256) {
+    const int i = e / HS, d = e - i * HS;
+    const bool ok = i0 + i < T_seq;
+    sm.Qs[i][d] = ok ? Elem<T>::to_f32(q[((size_t)bh * T_seq + i0 + i) * HS + d]) : 0.f;
+    sm.dOs[i][d] = ok ? Elem<T>::to_f32(dout[((size_t)b * T_seq + i0 + i) * (H * HS) + h * HS + d]) : 0.f;
+  }
+  if (threadIdx.x < kBT) {
+    const int i = threadIdx.x;
+    const bool ok = i0 + i < T_seq;
+    sm.lse[i] = ok ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
+    sm.dv[i] = ok ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+  }
+}
+
+// P and dS of the (query tile i0, key tile j0) pair into Ps / dSs: entries
+// with key j > query i, or outside the sequence, are exactly 0.
+template <int HS>
+__device__ __forceinline__ void score_tiles(AttnBwdSmem<HS>& sm, int i0, int j0, int T_seq) {
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  float s[4][4] = {}, dp[4][4] = {};
+#pragma unroll 4
+  for (int d = 0; d < HS; ++d) {
+    float qa[4], oa[4], kb[4], vb[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      qa[a] = sm.Qs[ty * 4 + a][d];
+      oa[a] = sm.dOs[ty * 4 + a][d];
+      kb[a] = sm.Ks[tx * 4 + a][d];
+      vb[a] = sm.Vs[tx * 4 + a][d];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s[a][c] += qa[a] * kb[c];
+        dp[a][c] += oa[a] * vb[c];
+      }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ii = ty * 4 + a, jj = tx * 4 + c;
+      const int i = i0 + ii, j = j0 + jj;
+      const bool ok = j <= i && i < T_seq;
+      const float p = ok ? __builtin_amdgcn_exp2f((s[a][c] - sm.lse[ii]) * kLog2e) : 0.f;
+      sm.Ps[ii][jj] = p;
+      sm.dSs[ii][jj] = ok ? p * (dp[a][c] - sm.dv[ii]) : 0.f;
+    }
+}
+
+// dK and dV of one key tile: loops over the query tiles at or after it.
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                             const T* __restrict__ vt, const T* __restrict__ dout,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ dvec, float* __restrict__ dqkv,
+                                                             int H, int T_seq, int kvT, int n_tiles) {
+  constexpr int DPT = HS / 16;
+  __shared__ AttnBwdSmem<HS> sm;
+  const int bh = blockIdx.x / n_tiles, kt = blockIdx.x - bh * n_tiles;
+  const int b = bh / H, h = bh - b * H;
+  const int j0 = kt * kBT;
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  load_kv_tile<T, HS>(sm, k, vt, bh, kvT, j0, T_seq);
+  float dk[4][DPT] = {}, dv[4][DPT] = {};
+  for (int qt = kt; qt < n_tiles; ++qt) {
+    const int i0 = qt * kBT;
+    __syncthreads();  // previous tile's readers are done
+    load_q_tile<T, HS>(sm, q, dout, lse, dvec, bh, b, h, H, i0, T_seq);
+    __syncthreads();
+    score_tiles<HS>(sm, i0, j0, T_seq);
+    __syncthreads();
+    // dV[j][d] += sum_i P[i][j] dO[i][d];  dK[j][d] += sum_i dS[i][j] Q[i][d]
+#pragma unroll 4
+    for (int i = 0; i < kBT; ++i) {
+      float pj[4], sj[4], od[DPT], qd[DPT];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        pj[a] = sm.Ps[i][ty * 4 + a];
+        sj[a] = sm.dSs[i][ty * 4 + a];
+      }
+#pragma unroll
+      for (int c = 0; c < DPT; ++c) {
+        od[c] = sm.dOs[i][tx * DPT + c];
+        qd[c] = sm.Qs[i][tx * DPT + c];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) {
+          dv[a][c] += pj[a] * od[c];
+          dk[a][c] += sj[a] * qd[c];
+        }
+    }
+  }
+  const int Dm = H * HS;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int j = j0 + ty * 4 + a;
+    if (j < T_seq) {
+      float* row = dqkv + ((size_t)b * T_seq + j) * (3 * Dm) + h * HS + tx * DPT;
+#pragma unroll
+      for (int c = 0; c < DPT; ++c) {
+        row[Dm + c] = dk[a][c];
+        row[2 * Dm + c] = dv[a][c];
+      }
+    }
+  }
+}
+
+// dQ of one query tile: loops over the key tiles at or before it.
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ vt, const T* __restrict__ dout,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ dvec, float* __restrict__ dqkv,
+                                                           int H, int T_seq, int kvT, int n_tiles, float scale) {
+  constexpr int DPT = HS / 16;
+  __shared__ AttnBwdSmem<HS> sm;
+  const int bh = blockIdx.x / n_tiles, qt = blockIdx.x - bh * n_tiles;
+  const int b = bh / H, h = bh - b * H;
+  const int i0 = qt * kBT;
+  const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+  load_q_tile<T, HS>(sm, q, dout, lse, dvec, bh, b, h, H, i0, T_seq);
+  float dq[4][DPT] = {};
+  for (int kt = 0; kt <= qt; ++kt) {
+    const int j0 = kt * kBT;
+    __syncthreads();
+    load_kv_tile<T, HS>(sm, k, vt, bh, kvT, j0, T_seq);
+    __syncthreads();
+    score_tiles<HS>(sm, i0, j0, T_seq);
+    __syncthreads();
+    // dQ[i][d] += sum_j dS[i][j] K[j][d]
+#pragma unroll 4
+    for (int j = 0; j < kBT; ++j) {
+      float sj[4], kd[DPT];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) sj[a] = sm.dSs[ty * 4 + a][j];
+#pragma unroll
+      for (int c = 0; c < DPT; ++c) kd[c] = sm.Ks[j][tx * DPT + c];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) dq[a][c] += sj[a] * kd[c];
+    }
+  }
+  const int Dm = H * HS;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty * 4 + a;
+    if (i < T_seq) {
+      float* row = dqkv + ((size_t)b * T_seq + i) * (3 * Dm) + h * HS + tx * DPT;
+#pragma unroll
+      for (int c = 0; c < DPT; ++c) row[c] = scale * dq[a][c];
+    }
+  }
+}
+
+}  // namespace
+
+template <typename Tin, typename Tout>
+hipError_t launch_transpose(const Tin* src, int R, int C, Tout* dst, int ld_dst, hipStream_t stream) {
+  if (ld_dst < R) return hipErrorInvalidValue;
+  const dim3 grid((ld_dst + 31) / 32, (C + 31) / 32);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((transpose_kernel<Tin, Tout>), grid, dim3(256), 0, stream, src, R, C, dst, ld_dst);
+  return hipGetLastError();
+}
+
+size_t colsum_partial_floats(int N) { return (size_t)kColChunks * N; }
+
+template <typename Tin>
+hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, hipStream_t stream, const float* x,
+                         const float* mu, const float* rstd) {
+  if (N <= 0) return hipSuccess;
+  const dim3 grid1((N + 63) / 64, kColChunks);
+  if (x)
+    hipLaunchKernelGGL((colsum_partial_kernel<Tin, true>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu, rstd);
+  else
+    hipLaunchKernelGGL((colsum_partial_kernel<Tin, false>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu,
+                       rstd);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_layernorm_backward(const float* x, const float* dh, const float* gamma, const float* resid,
+                                     float* out, T* out_t, float* mu, float* rstd, int M, int D, float eps,
+                                     hipStream_t stream) {
+  if (D > 2048 || D % 4 != 0) return hipErrorInvalidValue;
+  if (M <= 0) return hipSuccess;
+  const dim3 grid((M + 3) / 4), block(256);
+  switch (D) {
+    case 768:
+      hipLaunchKernelGGL((layernorm_backward_kernel<T, 3>), grid, block, 0, stream, x, dh, gamma, resid, out, out_t,
+                         mu, rstd, M, D, eps);
+      break;
+    case 1024:
+      hipLaunchKernelGGL((layernorm_backward_kernel<T, 4>), grid, block, 0, stream, x, dh, gamma, resid, out, out_t,
+                         mu, rstd, M, D, eps);
+      break;
+    default:
+      hipLaunchKernelGGL((layernorm_backward_kernel<T, 0>), grid, block, 0, stream, x, dh, gamma, resid, out, out_t,
+                         mu, rstd, M, D, eps);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_attention_backward(const T* q, const T* k, const T* vt, const T* o, const T* dout,
+                                     const float* lse, float* dvec, float* dqkv, int B, int H, int T_seq, int kvT,
+                                     int hs, float scale, hipStream_t stream) {
+  if (T_seq <= 0) return hipSuccess;
+  const int n_tiles = (T_seq + kBT - 1) / kBT;
+  if (kvT < T_seq) return hipErrorInvalidValue;
+  const int rows = B * H * T_seq;
+  const dim3 grid(B * H * n_tiles), block(256);
+  if (hs == 64) {
+    hipLaunchKernelGGL((attn_bwd_dvec_kernel<T, 64>), dim3((rows + 3) / 4), block, 0, stream, o, dout, dvec, B, H,
+                       T_seq);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 64>), grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, H,
+                       T_seq, kvT, n_tiles);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 64>), grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, H, T_seq,
+                       kvT, n_tiles, scale);
+  } else if (hs == 16) {
+    hipLaunchKernelGGL((attn_bwd_dvec_kernel<T, 16>), dim3((rows + 3) / 4), block, 0, stream, o, dout, dvec, B, H,
+                       T_seq);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, 16>), grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, H,
+                       T_seq, kvT, n_tiles);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, 16>), grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, H, T_seq,
+                       kvT, n_tiles, scale);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_transpose<float, float>(const float*, int, int, float*, int, hipStream_t);
+template hipError_t launch_transpose<float, bf16_t>(const float*, int, int, bf16_t*, int, hipStream_t);
+template hipError_t launch_transpose<bf16_t, bf16_t>(const bf16_t*, int, int, bf16_t*, int, hipStream_t);
+template hipError_t launch_colsum<float>(const float*, int, int, float*, float*, hipStream_t, const float*,
+                                         const float*, const float*);
+template hipError_t launch_colsum<bf16_t>(const bf16_t*, int, int, float*, float*, hipStream_t, const float*,
+                                          const float*, const float*);
+template hipError_t launch_layernorm_backward<float>(const float*, const float*, const float*, const float*, float*,
+                                                     float*, float*, float*, int, int, float, hipStream_t);
+template hipError_t launch_layernorm_backward<bf16_t>(const float*, const float*, const float*, const float*, float*,
+                                                      bf16_t*, float*, float*, int, int, float, hipStream_t);
+template hipError_t launch_attention_backward<float>(const float*, const float*, const float*, const float*,
+                                                     const float*, const float*, float*, float*, int, int, int, int,
+                                                     int, float, hipStream_t);
+template hipError_t launch_attention_backward<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*,
+                                                      const bf16_t*, const float*, float*, float*, int, int, int, int,
+                                                      int, float, hipStream_t);
+
+}  // namespace gpt2

@@ -198,6 +198,19 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 // The erf GELU, 0.5 x (1 + erf(x / sqrt(2))), with the device library's erff.
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+// Derivatives for the backward pass (device library tanhf / erff / expf):
+// gelu_new'(x) = 0.5 (1 + t) + 0.5 x (1 - t^2) k (1 + 3 c x^2),
+//   t = tanh(k (x + c x^3)), k = sqrt(2/pi), c = 0.044715;
+// gelu'(x) = Phi(x) + x phi(x) for the erf form.
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+  const float k = 0.7978845608028654f, c = 0.044715f;
+  const float t = tanhf(k * (x + c * x * x * x));
+  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * c * x * x);
+}
+__device__ __forceinline__ float gelu_erf_grad(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * expf(-0.5f * x * x) * 0.3989422804014327f;
+}
+
 // Division by a runtime-invariant positive divisor through a precomputed
 // multiplier (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI 1994): for 0 <= n < 2^31 and 1 <= d < 2^31,

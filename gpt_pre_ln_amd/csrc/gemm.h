@@ -177,6 +177,73 @@ struct EpiLogits {
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
+// Backward-pass epilogues (block backward).
+// Plain store of C (fp32 or T) into out[M][ldo].
+template <typename O>
+struct EpiStore {
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false,
+                        kRowArgmax = false;
+  O* out;
+  int ldo;
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
+    Elem<O>::store4(out + (size_t)m * ldo + n, v[0], v[1], v[2], v[3]);
+  }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+};
+
+// c_fc of the recomputed forward: as EpiGelu, and the pre-activation (with
+// bias) kept in fp32 for the derivative.
+template <typename T>
+struct EpiGeluSave {
+  static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false,
+                        kRowArgmax = false;
+  const float* bias;  // [N]
+  T* u;               // [M][ld]
+  float* g;           // [M][ld]
+  int ld;
+  int erf_form;
+  __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
+    *reinterpret_cast<float4*>(g + (size_t)m * ld + n) = make_float4(v[0], v[1], v[2], v[3]);
+    if (erf_form)
+      Elem<T>::store4(u + (size_t)m * ld + n, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3]));
+    else
+      Elem<T>::store4(u + (size_t)m * ld + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
+  }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+};
+
+// dG = dU * act'(G): C is dU = dY W_pr^T, G the kept pre-activation.
+template <typename T>
+struct EpiGeluBwd {
+  static constexpr bool kPreload = true, kBias = false, kTransposed = false, kRowReduce = false,
+                        kRowArgmax = false;
+  const float* g;  // [M][ld]
+  T* dg;           // [M][ld]
+  int ld;
+  int erf_form;
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
+  __device__ __forceinline__ float4 preload(int m, int n) const {
+    return *reinterpret_cast<const float4*>(g + (size_t)m * ld + n);
+  }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4& x) const {
+    float d0, d1, d2, d3;
+    if (erf_form) {
+      d0 = gelu_erf_grad(x.x), d1 = gelu_erf_grad(x.y), d2 = gelu_erf_grad(x.z), d3 = gelu_erf_grad(x.w);
+    } else {
+      d0 = gelu_tanh_grad(x.x), d1 = gelu_tanh_grad(x.y), d2 = gelu_tanh_grad(x.z), d3 = gelu_tanh_grad(x.w);
+    }
+    Elem<T>::store4(dg + (size_t)m * ld + n, v[0] * d0, v[1] * d1, v[2] * d2, v[3] * d3);
+  }
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+};
+
 // Next-token cross-entropy partials of the tied lm_head (pwwt.cn
 // "逐行拆GPT-2源码", GPT2LMHeadModel: logits of position t are scored against
 // the label of position t + 1): the logits are reduced in registers and never

@@ -517,6 +517,20 @@ GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
+template hipError_t launch_gemm<float, EpiStore<float>>(GemmTile, const float*, const float*, int, int, int, int,
+                                                        int, const EpiStore<float>&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiStore<float>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int,
+                                                         int, const EpiStore<float>&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiStore<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
+                                                          int, int, const EpiStore<bf16_t>&, hipStream_t);
+template hipError_t launch_gemm<float, EpiGeluSave<float>>(GemmTile, const float*, const float*, int, int, int, int,
+                                                           int, const EpiGeluSave<float>&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiGeluSave<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
+                                                             int, int, const EpiGeluSave<bf16_t>&, hipStream_t);
+template hipError_t launch_gemm<float, EpiGeluBwd<float>>(GemmTile, const float*, const float*, int, int, int, int,
+                                                          int, const EpiGeluBwd<float>&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiGeluBwd<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
+                                                            int, int, const EpiGeluBwd<bf16_t>&, hipStream_t);
 template hipError_t launch_gemm<float, EpiArgmax>(GemmTile, const float*, const float*, int, int, int, int, int,
                                                   const EpiArgmax&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiArgmax>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,

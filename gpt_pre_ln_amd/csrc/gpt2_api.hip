@@ -13,6 +13,7 @@
 
 #include "../../include/gpt2.h"
 #include "attention.h"
+#include "backward.h"
 #include "gemm.h"
 #include "rowops.h"
 
@@ -510,6 +511,165 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   return GPT2_OK;
 }
 
+// ------------------------------------------------------------------ block backward
+
+// Backward workspace (caller-owned, gpt2_block_backward_workspace_bytes):
+// the recomputed forward of the block and the gradient temporaries.
+struct BwdLayout {
+  size_t h1, q, k, vt, lse, dvec, a, xh, h2, g, u, dyt, wt_qkv, wt_o, wt_fc, wt_pr, dg, dh, dxh, dxht, da, dqkv,
+      dqkvt, ta, tb, mu, rstd, part, total;
+};
+
+BwdLayout bwd_layout(const gpt2_config& c, int B, int T) {
+  BwdLayout L;
+  const size_t es = esize(c), D = c.d_model, F = c.d_ff, M = (size_t)B * T, Mp = round_up_int((int)M, 64);
+  const size_t Tp = kv_stride(T), BH = (size_t)B * c.n_head, hs = D / c.n_head;
+  const size_t wide = std::max(F, 3 * D);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.h1 = take(M * D * es);
+  L.q = take(M * D * es);
+  L.k = take(BH * Tp * hs * es);
+  L.vt = take(BH * Tp * hs * es);
+  L.lse = take(BH * T * 4);
+  L.dvec = take(BH * T * 4);
+  L.a = take(M * D * es);
+  L.xh = take(M * D * 4);
+  L.h2 = take(M * D * es);
+  L.g = take(M * F * 4);
+  L.u = take(M * F * es);
+  L.dyt = take(M * D * es);
+  L.wt_qkv = take(3 * D * D * es);
+  L.wt_o = take(D * D * es);
+  L.wt_fc = take(D * F * es);
+  L.wt_pr = take(F * D * es);
+  L.dg = take(M * F * es);
+  L.dh = take(M * D * 4);
+  L.dxh = take(M * D * 4);
+  L.dxht = take(M * D * es);
+  L.da = take(M * D * es);
+  L.dqkv = take(M * 3 * D * 4);
+  L.dqkvt = take(M * 3 * D * es);
+  L.ta = take(wide * Mp * es);
+  L.tb = take(wide * Mp * es);
+  L.mu = take(M * 4);
+  L.rstd = take(M * 4);
+  L.part = take(colsum_partial_floats((int)wide) * 4);
+  L.total = off;
+  return L;
+}
+
+// Backward of Pre-LN block l (dpshk.com llm.c notes 5.3; the block's forward
+// as in russellluo.com "GPT-2 Block" and pwwt.cn GPT2Block / GPT2Attention /
+// GPT2MLP), taken in reverse:
+//   forward recomputed from x: h1 = LN_1(x), q|k|v, attention (keeping each
+//   query's log-sum-exp), x_h = x + a W_o + b_o, h2 = LN_2(x_h),
+//   g = h2 W_fc + b_fc (kept in fp32), u = act(g);
+//   MLP: dg = (dy W_pr^T) act'(g), dW_pr = u^T dy, dW_fc = h2^T dg,
+//        dh2 = dg W_fc^T;  x_h gradient = dy + LN_2 backward(dh2);
+//   attention: dW_o = a^T dx_h, da = dx_h W_o^T, attention backward -> dq|dk|dv,
+//        dW_qkv = h1^T dqkv, dh1 = dqkv W_qkv^T;  dx = dx_h + LN_1 backward(dh1).
+// Products run on the GEMM kernel (C = A B^T, both operands contiguous in
+// the contraction): weight-side operands from transposed copies of this
+// layer's weights, the weight gradients from transposed activations padded
+// to a multiple of 64 rows.  Bias, gamma and beta gradients are column sums.
+template <typename T>
+gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const float* x, const float* dy, float* dx,
+                               float* grads, char* ws, hipStream_t st) {
+  const gpt2_config& c = m->cfg;
+  const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff;
+  const int M = B * T_seq, Mp = round_up_int(M, 64), Tp = kv_stride(T_seq);
+  const BwdLayout L = bwd_layout(c, B, T_seq);
+  const LayerOff& o = m->lay.layers[l];
+  auto wp = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  T *h1 = wp(L.h1), *q = wp(L.q), *kk = wp(L.k), *vt = wp(L.vt), *a = wp(L.a), *h2 = wp(L.h2), *u = wp(L.u);
+  T *dyt = wp(L.dyt), *dg = wp(L.dg), *dxht = wp(L.dxht), *da = wp(L.da), *dqkvt = wp(L.dqkvt);
+  T *ta = wp(L.ta), *tb = wp(L.tb);
+  T *wt_qkv = wp(L.wt_qkv), *wt_o = wp(L.wt_o), *wt_fc = wp(L.wt_fc), *wt_pr = wp(L.wt_pr);
+  float *lse = fp(L.lse), *dvec = fp(L.dvec), *xh = fp(L.xh), *gpre = fp(L.g), *dh = fp(L.dh), *dxh = fp(L.dxh);
+  float *dqkv = fp(L.dqkv), *mu = fp(L.mu), *rstd = fp(L.rstd), *part = fp(L.part);
+  float q_scale = 1.0f / std::sqrt((float)hs);
+  if (c.scale_attn_by_inverse_layer_idx) q_scale /= (float)(l + 1);
+  // gradient slices of this layer, in the blob's order
+  const size_t G_ln1w = 0, G_ln1b = D, G_qkvw = 2 * (size_t)D, G_qkvb = G_qkvw + 3 * (size_t)D * D,
+               G_ow = G_qkvb + 3 * D, G_ob = G_ow + (size_t)D * D, G_ln2w = G_ob + D, G_ln2b = G_ln2w + D,
+               G_fcw = G_ln2b + D, G_fcb = G_fcw + (size_t)D * F, G_prw = G_fcb + F, G_prb = G_prw + (size_t)F * D;
+  auto gemm_f32 = [&](const T* A, const T* Bm, int Mr, int N, int K, float* out, int ldo) {
+    return launch_gemm<T>(pick_tile(Mr, N, K), A, Bm, Mr, N, K, K, K, EpiStore<float>{out, ldo}, st);
+  };
+
+  // transposed copies of this layer's weights ([out][in] -> [in][out])
+  GPT2_HIP((launch_transpose<T, T>(pp<T>(m, o.w_qkv), 3 * D, D, wt_qkv, 3 * D, st)), "bwd transpose w_qkv");
+  GPT2_HIP((launch_transpose<T, T>(pp<T>(m, o.w_o), D, D, wt_o, D, st)), "bwd transpose w_o");
+  GPT2_HIP((launch_transpose<T, T>(pp<T>(m, o.w_fc), F, D, wt_fc, F, st)), "bwd transpose w_fc");
+  GPT2_HIP((launch_transpose<T, T>(pp<T>(m, o.w_pr), D, F, wt_pr, D, st)), "bwd transpose w_pr");
+
+  // forward of the block, keeping what the backward reads
+  GPT2_HIP(launch_layernorm<T>(const_cast<float*>(x), pf(m, o.ln1_g), pf(m, o.ln1_b), h1, nullptr, M, D, c.ln_eps, st),
+           "bwd ln_1");
+  {
+    EpiQKV<T> e{pf(m, o.b_qkv), q, kk, vt, FastDiv(T_seq), FastDiv(D), 0, Tp, H, ilog2(hs), q_scale, M};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D, D), h1, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "bwd c_attn");
+  }
+  GPT2_HIP(launch_attention_prefill<T>(q, kk, vt, a, B, H, T_seq, Tp, hs, st, lse), "bwd attention");
+  GPT2_HIP(hipMemcpyAsync(xh, x, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st), "bwd residual copy");
+  {
+    EpiResidual e{pf(m, o.b_o), xh, D};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, D, D), a, pp<T>(m, o.w_o), M, D, D, D, D, e, st), "bwd attn.c_proj");
+  }
+  GPT2_HIP(launch_layernorm<T>(xh, pf(m, o.ln2_g), pf(m, o.ln2_b), h2, nullptr, M, D, c.ln_eps, st), "bwd ln_2");
+  {
+    EpiGeluSave<T> e{pf(m, o.b_fc), u, gpre, F, c.activation};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, F, D), h2, pp<T>(m, o.w_fc), M, F, D, D, D, e, st), "bwd c_fc");
+  }
+
+  // MLP
+  GPT2_HIP(launch_convert<T>(dy, dyt, (size_t)M * D, (size_t)M * D, st), "bwd dy");
+  {
+    EpiGeluBwd<T> e{gpre, dg, F, c.activation};
+    GPT2_HIP(launch_gemm<T>(pick_tile(M, F, D), dyt, wt_pr, M, F, D, D, D, e, st), "bwd du");
+  }
+  GPT2_HIP(launch_colsum<float>(dy, M, D, grads + G_prb, part, st), "bwd db_pr");
+  GPT2_HIP((launch_transpose<T, T>(u, M, F, ta, Mp, st)), "bwd u^T");
+  GPT2_HIP((launch_transpose<T, T>(dyt, M, D, tb, Mp, st)), "bwd dy^T");
+  GPT2_HIP(gemm_f32(ta, tb, F, D, Mp, grads + G_prw, D), "bwd dW_pr");
+  GPT2_HIP(launch_colsum<T>(dg, M, F, grads + G_fcb, part, st), "bwd db_fc");
+  GPT2_HIP((launch_transpose<T, T>(h2, M, D, ta, Mp, st)), "bwd h2^T");
+  GPT2_HIP((launch_transpose<T, T>(dg, M, F, tb, Mp, st)), "bwd dg^T");
+  GPT2_HIP(gemm_f32(ta, tb, D, F, Mp, grads + G_fcw, F), "bwd dW_fc");
+  GPT2_HIP(gemm_f32(dg, wt_fc, M, D, F, dh, D), "bwd dh2");
+  GPT2_HIP(launch_layernorm_backward<T>(xh, dh, pf(m, o.ln2_g), dy, dxh, dxht, mu, rstd, M, D, c.ln_eps, st),
+           "bwd ln_2 backward");
+  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln2w, part, st, xh, mu, rstd), "bwd dgamma_2");
+  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln2b, part, st), "bwd dbeta_2");
+
+  // attention
+  GPT2_HIP(launch_colsum<float>(dxh, M, D, grads + G_ob, part, st), "bwd db_o");
+  GPT2_HIP((launch_transpose<T, T>(a, M, D, ta, Mp, st)), "bwd a^T");
+  GPT2_HIP((launch_transpose<T, T>(dxht, M, D, tb, Mp, st)), "bwd dx_h^T");
+  GPT2_HIP(gemm_f32(ta, tb, D, D, Mp, grads + G_ow, D), "bwd dW_o");
+  GPT2_HIP(launch_gemm<T>(pick_tile(M, D, D), dxht, wt_o, M, D, D, D, D, EpiStore<T>{da, D}, st), "bwd da");
+  GPT2_HIP(launch_attention_backward<T>(q, kk, vt, a, da, lse, dvec, dqkv, B, H, T_seq, Tp, hs, q_scale, st),
+           "bwd attention backward");
+  GPT2_HIP(launch_colsum<float>(dqkv, M, 3 * D, grads + G_qkvb, part, st), "bwd db_qkv");
+  GPT2_HIP(launch_convert<T>(dqkv, dqkvt, (size_t)M * 3 * D, (size_t)M * 3 * D, st), "bwd dqkv");
+  GPT2_HIP((launch_transpose<T, T>(h1, M, D, ta, Mp, st)), "bwd h1^T");
+  GPT2_HIP((launch_transpose<T, T>(dqkvt, M, 3 * D, tb, Mp, st)), "bwd dqkv^T");
+  GPT2_HIP(gemm_f32(ta, tb, D, 3 * D, Mp, grads + G_qkvw, 3 * D), "bwd dW_qkv");
+  GPT2_HIP(gemm_f32(dqkvt, wt_qkv, M, D, 3 * D, dh, D), "bwd dh1");
+  GPT2_HIP(launch_layernorm_backward<T>(x, dh, pf(m, o.ln1_g), dxh, dx, static_cast<T*>(nullptr), mu, rstd, M, D,
+                                        c.ln_eps, st),
+           "bwd ln_1 backward");
+  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln1w, part, st, x, mu, rstd), "bwd dgamma_1");
+  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln1b, part, st), "bwd dbeta_1");
+  return GPT2_OK;
+}
+
 template <typename T>
 gpt2_status run_init(gpt2_model* m, const float* blob, hipStream_t st) {
   const gpt2_config& c = m->cfg;
@@ -706,6 +866,31 @@ gpt2_status gpt2_generate(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens
     if (s != GPT2_OK) return s;
   }
   return GPT2_OK;
+}
+
+gpt2_status gpt2_block_backward_workspace_bytes(const gpt2_config* cfg, int32_t B, int32_t T, size_t* bytes) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || T > cfg->n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
+  *bytes = bwd_layout(*cfg, B, T).total;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_block_backward(gpt2_model* m, int32_t layer, int32_t B, int32_t T, const float* x, const float* dy,
+                                float* dx, float* grads, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !x || !dy || !dx || !grads || !ws) return GPT2_ERR_INVALID_ARG;
+  if (m->cfg.post_ln) return GPT2_ERR_UNSUPPORTED;
+  if (layer < 0 || layer >= m->cfg.n_layer) return GPT2_ERR_SHAPE;
+  if (B < 1 || T < 1 || T > m->cfg.n_positions || (int64_t)B * T > (1 << 24)) return GPT2_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(grads, 16) || !aligned(ws, kAlign))
+    return GPT2_ERR_INVALID_ARG;
+  if (dx == x || dx == dy) return GPT2_ERR_INVALID_ARG;
+  if (bwd_layout(m->cfg, B, T).total > ws_bytes) return GPT2_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  return m->cfg.dtype == GPT2_BF16 ? run_block_backward<bf16_t>(m, layer, B, T, x, dy, dx, grads, w, st)
+                                   : run_block_backward<float>(m, layer, B, T, x, dy, dx, grads, w, st);
 }
 
 gpt2_status gpt2_set_trace(gpt2_model* m, float* d_trace, size_t n) {

@@ -141,6 +141,29 @@ class GPT2:
         B.gpt2_generate(self.handle, kv.view, first_ids.data_ptr(), n_steps, out.data_ptr(), self.stream)
         return out
 
+    def layer_param_count(self) -> int:
+        D, F = self.cfg.d_model, self.cfg.d_ff
+        return 2 * D + (3 * D * D + 3 * D) + (D * D + D) + 2 * D + (D * F + F) + (F * D + D)
+
+    def block_backward(self, layer: int, x: torch.Tensor, dy: torch.Tensor, out_dx: torch.Tensor | None = None,
+                       out_grads: torch.Tensor | None = None):
+        """Backward of block `layer` (gpt2_block_backward): x, dy fp32 [B, T, D]
+        on the device.  Returns (dx fp32 [B, T, D], grads fp32 [layer parameters]
+        in blob order).  The backward workspace is allocated here, outside the
+        library, and kept for calls of the same or a smaller size."""
+        assert x.dtype == torch.float32 and dy.dtype == torch.float32 and x.shape == dy.shape
+        assert x.is_contiguous() and dy.is_contiguous()
+        Bsz, T, _ = x.shape
+        need = B.gpt2_block_backward_workspace_bytes(self.cfg, Bsz, T)
+        if getattr(self, "_bwd_ws", None) is None or self._bwd_ws.numel() < need:
+            self._bwd_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        dx = out_dx if out_dx is not None else torch.empty_like(x)
+        grads = out_grads if out_grads is not None else torch.empty(self.layer_param_count(), dtype=torch.float32,
+                                                                   device=self.device)
+        B.gpt2_block_backward(self.handle, layer, Bsz, T, x.data_ptr(), dy.data_ptr(), dx.data_ptr(), grads.data_ptr(),
+                              self._bwd_ws.data_ptr(), self._bwd_ws.numel(), self.stream)
+        return dx, grads
+
     def set_trace(self, trace: torch.Tensor | None):
         B.gpt2_set_trace(self.handle, trace.data_ptr() if trace is not None else None,
                          trace.numel() if trace is not None else 0)

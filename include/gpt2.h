@@ -188,6 +188,32 @@ gpt2_status gpt2_decode_step(gpt2_model* model, gpt2_kv_view* kv, const int32_t*
 gpt2_status gpt2_generate(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_tokens, int32_t n_steps,
                           int32_t* d_out_tokens, void* stream);
 
+/* Bytes of the backward workspace for gpt2_block_backward at batch B, length T. */
+gpt2_status gpt2_block_backward_workspace_bytes(const gpt2_config* cfg, int32_t B, int32_t T, size_t* bytes);
+
+/* Backward of block `layer` (Pre-LN wiring; post_ln gives GPT2_ERR_UNSUPPORTED)
+ * for B sequences of T tokens -- the gradients the llm.c notes of dpshk.com
+ * (5.3) single out: LayerNorm with its coupled mean/variance terms, the
+ * masked softmax (masked entries carry exactly zero gradient) and GELU.
+ *   d_x:     fp32 [B, T, D], the block input X_l (the residual stream before
+ *            the block, e.g. from gpt2_set_trace of the previous block).
+ *   d_dy:    fp32 [B, T, D], gradient of the loss w.r.t. the block output.
+ *   d_dx:    fp32 [B, T, D] out: gradient w.r.t. X_l (must not alias d_x, d_dy).
+ *   d_grads: fp32 out, the layer's parameters in blob order (ln_1.w, ln_1.b,
+ *            attn.c_attn.w [D, 3D], attn.c_attn.b, attn.c_proj.w [D, D],
+ *            attn.c_proj.b, ln_2.w, ln_2.b, mlp.c_fc.w [D, F], mlp.c_fc.b,
+ *            mlp.c_proj.w [F, D], mlp.c_proj.b), overwritten, summed over
+ *            all B*T positions.
+ *   d_ws / ws_bytes: caller-owned scratch of at least
+ *            gpt2_block_backward_workspace_bytes(cfg, B, T) bytes, 256-byte
+ *            aligned.  All data pointers 16-byte aligned.
+ * The block's forward is recomputed from d_x (nothing from an earlier
+ * forward call is reused).  bf16 models take bf16 matrix operands with fp32
+ * accumulation; gradients are fp32.  The model workspace is not touched. */
+gpt2_status gpt2_block_backward(gpt2_model* model, int32_t layer, int32_t B, int32_t T, const float* d_x,
+                                const float* d_dy, float* d_dx, float* d_grads, void* d_ws, size_t ws_bytes,
+                                void* stream);
+
 /* Optional per-layer trace for debugging: when d_trace is non-NULL, the next
  * gpt2_forward calls copy the residual stream after every block (X_{l+1},
  * fp32 [n_layer][B*T][d_model]) into d_trace, which must hold that many floats.

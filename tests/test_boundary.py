@@ -212,6 +212,32 @@ def test_generate_host_checks(B, handle):
     assert gen(kv, 1) == B.GPT2_ERR_INVALID_ARG
 
 
+def test_block_backward_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    wb = B.gpt2_block_backward_workspace_bytes(cfg, 2, 64)
+    assert wb > B.gpt2_workspace_bytes(cfg, 2, 64)
+    bwd = lambda layer=0, Bz=2, T=64, x=FAKE, dy=FAKE + 4096, dx=FAKE + 8192, g=FAKE + 16384, ws=FAKE, n=wb: \
+        lib.gpt2_block_backward(h, layer, Bz, T, x, dy, dx, g, ws, n, None)
+    assert bwd(layer=2) == B.GPT2_ERR_SHAPE          # 2 layers
+    assert bwd(layer=-1) == B.GPT2_ERR_SHAPE
+    assert bwd(T=0) == B.GPT2_ERR_SHAPE
+    assert bwd(T=129) == B.GPT2_ERR_SHAPE
+    assert bwd(n=wb - 1) == B.GPT2_ERR_WORKSPACE
+    assert bwd(x=None) == B.GPT2_ERR_INVALID_ARG
+    assert bwd(dx=FAKE) == B.GPT2_ERR_INVALID_ARG     # dx aliases x
+    assert bwd(g=FAKE + 16388) == B.GPT2_ERR_INVALID_ARG
+    assert bwd(ws=FAKE + 16) == B.GPT2_ERR_INVALID_ARG
+    post = B.make_config(1000, 128, 128, 2, 2, 512, 1e-5, "bf16", post_ln=True)
+    pb = B.gpt2_param_bytes(post)
+    hp = B.gpt2_create(post, FAKE, pb, FAKE + (1 << 28), B.gpt2_workspace_bytes(post, 2, 64))
+    try:
+        assert lib.gpt2_block_backward(hp, 0, 2, 64, FAKE, FAKE + 4096, FAKE + 8192, FAKE + 16384, FAKE, wb,
+                                       None) == B.GPT2_ERR_UNSUPPORTED
+    finally:
+        B.gpt2_destroy(hp)
+
+
 def test_init_params_size_check(B, handle):
     h, cfg = handle
     n = B.gpt2_param_blob_floats(cfg)
