@@ -329,6 +329,253 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
   }
 }
 
+// ----------------------------------------------------------- bf16, matrix cores
+// Head size 64, 64 x 64 tiles, 4 waves.  R = X Y^T on 16 x 16 blocks with
+// v_mfma_f32_16x16x32_bf16 (Mma<bf16_t>::run(acc, X, Y)): lane l supplies
+// X[l % 16][8 (l / 16) .. +7] and Y[l % 16][8 (l / 16) .. +7] (16 bytes of a
+// row whose contraction index is contiguous) and receives
+// R[4 (l / 16) + e][l % 16], e = 0..3.  Every operand therefore lives in LDS
+// with its contraction index contiguous: Q, dO, K, V as [row][d] and the
+// transposed copies Q^T, dO^T, K^T as [d][row]; P and dS are written by the
+// wave that computed them in the layout of the product that reads them.
+constexpr int kLdsRow = 64 + 8;  // bf16 per LDS row (16 bytes of padding)
+
+struct alignas(16) MmaTile {
+  bf16_t a[kBT][kLdsRow];
+};
+
+__device__ __forceinline__ u32x4_t frag(const MmaTile& t, int row, int k8) {
+  return *reinterpret_cast<const u32x4_t*>(&t.a[row][k8]);
+}
+
+// Row-major copy ([row][d], 16-byte chunks) and, optionally, the transposed
+// copy ([d][row]) of 64 rows of 64 bf16 from global rows src + r * ld, rows
+// past `valid` zero.
+__device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf16_t* src, size_t ld, int valid) {
+  for (int c = threadIdx.x; c < kBT * 8; c += 256) {
+    const int r = c >> 3, d8 = (c & 7) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < valid) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * ld + d8);
+    *reinterpret_cast<u32x4_t*>(&t.a[r][d8]) = v;
+    if (tt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tt->a[d8 + 2 * e][r].bits = (uint16_t)(v[e] & 0xFFFF);
+        tt->a[d8 + 2 * e + 1][r].bits = (uint16_t)(v[e] >> 16);
+      }
+    }
+  }
+}
+
+// V^T rows (global [d][kvT], keys contiguous) into V as [key][d].
+__device__ __forceinline__ void load_vt_bf16(MmaTile& t, const bf16_t* vt, int kvT, int j0, int valid) {
+  for (int c = threadIdx.x; c < kBT * 8; c += 256) {
+    const int d = c >> 3, k8 = (c & 7) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (k8 < valid) v = *reinterpret_cast<const u32x4_t*>(vt + (size_t)d * kvT + j0 + k8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool lo = k8 + 2 * e < valid, hi = k8 + 2 * e + 1 < valid;
+      t.a[k8 + 2 * e][d].bits = lo ? (uint16_t)(v[e] & 0xFFFF) : (uint16_t)0;
+      t.a[k8 + 2 * e + 1][d].bits = hi ? (uint16_t)(v[e] >> 16) : (uint16_t)0;
+    }
+  }
+}
+
+// S and dP of one 16-row block (rows `r16` of X-side tiles Qs / dOs) against
+// the 64 keys of Ks / Vs, or (keys_by_wave) of 64 query rows against one
+// 16-key block: acc[b] covers the b-th 16 x 16 block.
+__device__ __forceinline__ void mma_sp(f32x4_t (&s)[4], f32x4_t (&dp)[4], const MmaTile& X1, const MmaTile& Y1,
+                                       const MmaTile& X2, const MmaTile& Y2, int xrow0, int yrow0, bool x_varies) {
+  const int lr = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dp[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int k8 = ks * 32 + lg * 8;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int xr = x_varies ? b * 16 + lr : xrow0 + lr;
+      const int yr = x_varies ? yrow0 + lr : b * 16 + lr;
+      Mma<bf16_t>::run(s[b], frag(X1, xr, k8), frag(Y1, yr, k8));
+      Mma<bf16_t>::run(dp[b], frag(X2, xr, k8), frag(Y2, yr, k8));
+    }
+  }
+}
+
+struct AttnBwdMmaKV {
+  MmaTile K, V, Q, Qt, dO, dOt, Pt, dSt;
+  float lse[kBT];
+  float dv[kBT];
+};
+
+// dK and dV of one key tile (64 keys): wave w owns keys 16w .. 16w+15.  Per
+// query tile at or after it: S and dP of all 64 queries against the wave's
+// keys; P = exp(S - lse), dS = P (dP - rowsum(dO o)) (exactly 0 where the key
+// follows the query or the query is past the end), written as P^T, dS^T
+// rows of the wave's keys; then dV += P^T dO and dK += dS^T Q.
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_mma_kernel(const bf16_t* __restrict__ q,
+                                                                const bf16_t* __restrict__ k,
+                                                                const bf16_t* __restrict__ vt,
+                                                                const bf16_t* __restrict__ dout,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ dvec,
+                                                                float* __restrict__ dqkv, int BH, int H, int T_seq,
+                                                                int kvT, int n_tiles) {
+  __shared__ AttnBwdMmaKV sm;
+  const int kt = blockIdx.x / BH, bh = blockIdx.x - kt * BH;  // key tile 0 (the longest) first
+  const int b = bh / H, h = bh - b * H;
+  const int j0 = kt * kBT;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int Dm = H * 64;
+  load_rows_bf16(sm.K, nullptr, k + ((size_t)bh * kvT + j0) * 64, 64, min(kBT, T_seq - j0));
+  load_vt_bf16(sm.V, vt + (size_t)bh * 64 * kvT, kvT, j0, min(kBT, T_seq - j0));
+  f32x4_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qt = kt; qt < n_tiles; ++qt) {
+    const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
+    __syncthreads();
+    load_rows_bf16(sm.Q, &sm.Qt, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
+    load_rows_bf16(sm.dO, &sm.dOt, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
+    if (threadIdx.x < kBT) {
+      const int i = threadIdx.x;
+      sm.lse[i] = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
+      sm.dv[i] = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+    }
+    __syncthreads();
+    // R[q][key] for the 4 query blocks (x varies) against this wave's keys
+    f32x4_t s[4], dp[4];
+    mma_sp(s, dp, sm.Q, sm.K, sm.dO, sm.V, 0, w * 16, true);
+    const int key = w * 16 + lr;  // local key of this lane's column
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      uint32_t pw[2], sw[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        float pv[2], sv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = e2 * 2 + u;
+          const int ql = qb * 16 + lg * 4 + e;
+          const bool ok = j0 + key <= i0 + ql && ql < nq;
+          const float p = ok ? __builtin_amdgcn_exp2f((s[qb][e] - sm.lse[ql]) * kLog2e) : 0.f;
+          pv[u] = p;
+          sv[u] = ok ? p * (dp[qb][e] - sm.dv[ql]) : 0.f;
+        }
+        pw[e2] = pack2_bf16(pv[0], pv[1]);
+        sw[e2] = pack2_bf16(sv[0], sv[1]);
+      }
+      // P^T[key][q .. q+3], dS^T likewise: one 8-byte store each
+      *reinterpret_cast<u32x2_t*>(&sm.Pt.a[key][qb * 16 + lg * 4]) = u32x2_t{pw[0], pw[1]};
+      *reinterpret_cast<u32x2_t*>(&sm.dSt.a[key][qb * 16 + lg * 4]) = u32x2_t{sw[0], sw[1]};
+    }
+    __syncthreads();
+    // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (contraction over the 64 queries)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k8 = ks * 32 + lg * 8;
+      const u32x4_t pf = frag(sm.Pt, w * 16 + lr, k8), sf = frag(sm.dSt, w * 16 + lr, k8);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        Mma<bf16_t>::run(dv[db], pf, frag(sm.dOt, db * 16 + lr, k8));
+        Mma<bf16_t>::run(dk[db], sf, frag(sm.Qt, db * 16 + lr, k8));
+      }
+    }
+  }
+  // lane holds R[key = 16w + 4 lg + e][d = 16 db + lr]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = j0 + w * 16 + lg * 4 + e;
+    if (j < T_seq) {
+      float* row = dqkv + ((size_t)b * T_seq + j) * (3 * Dm) + h * 64 + lr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        row[Dm + db * 16] = dk[db][e];
+        row[2 * Dm + db * 16] = dv[db][e];
+      }
+    }
+  }
+}
+
+struct AttnBwdMmaQ {
+  MmaTile Q, dO, K, Kt, V, dS;
+  float lse[kBT];
+  float dv[kBT];
+};
+
+// dQ of one query tile: wave w owns queries 16w .. 16w+15.  Per key tile at
+// or before it: S, dP of the wave's queries against the 64 keys, dS written
+// as rows of the wave's queries, then dQ += dS K (against K^T).
+__global__ __launch_bounds__(256) void attn_bwd_dq_mma_kernel(const bf16_t* __restrict__ q,
+                                                              const bf16_t* __restrict__ k,
+                                                              const bf16_t* __restrict__ vt,
+                                                              const bf16_t* __restrict__ dout,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ dvec,
+                                                              float* __restrict__ dqkv, int BH, int H, int T_seq,
+                                                              int kvT, int n_tiles, float scale) {
+  __shared__ AttnBwdMmaQ sm;
+  const int r = blockIdx.x / BH, bh = blockIdx.x - r * BH;
+  const int qt = n_tiles - 1 - r;  // the last query tile (the longest) first
+  const int b = bh / H, h = bh - b * H;
+  const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int Dm = H * 64;
+  load_rows_bf16(sm.Q, nullptr, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
+  load_rows_bf16(sm.dO, nullptr, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
+  if (threadIdx.x < kBT) {
+    const int i = threadIdx.x;
+    sm.lse[i] = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
+    sm.dv[i] = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+  }
+  f32x4_t dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt <= qt; ++kt) {
+    const int j0 = kt * kBT, nk = min(kBT, T_seq - j0);
+    __syncthreads();
+    load_rows_bf16(sm.K, &sm.Kt, k + ((size_t)bh * kvT + j0) * 64, 64, nk);
+    load_vt_bf16(sm.V, vt + (size_t)bh * 64 * kvT, kvT, j0, nk);
+    __syncthreads();
+    // R[q][key] for this wave's queries (y varies over the 4 key blocks)
+    f32x4_t s[4], dp[4];
+    mma_sp(s, dp, sm.Q, sm.K, sm.dO, sm.V, w * 16, 0, false);
+    // lane holds R[q = 16w + 4 lg + e][key = 16 kb + lr]
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ql = w * 16 + lg * 4 + e, key = kb * 16 + lr;
+        const bool ok = j0 + key <= i0 + ql && ql < nq;
+        const float p = ok ? __builtin_amdgcn_exp2f((s[kb][e] - sm.lse[ql]) * kLog2e) : 0.f;
+        sm.dS.a[ql][key].bits = f32_to_bf16(ok ? p * (dp[kb][e] - sm.dv[ql]) : 0.f);
+      }
+    __syncthreads();
+    // dQ[q][d] += dS K  (contraction over the 64 keys; K^T rows are d)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int k8 = ks * 32 + lg * 8;
+      const u32x4_t sf = frag(sm.dS, w * 16 + lr, k8);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) Mma<bf16_t>::run(dq[db], sf, frag(sm.Kt, db * 16 + lr, k8));
+    }
+  }
+  // lane holds R[q = 16w + 4 lg + e][d = 16 db + lr]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + w * 16 + lg * 4 + e;
+    if (i < T_seq) {
+      float* row = dqkv + ((size_t)b * T_seq + i) * (3 * Dm) + h * 64 + lr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) row[db * 16] = scale * dq[db][e];
+    }
+  }
+}
+
 }  // namespace
 
 template <typename Tin, typename Tout>
@@ -388,6 +635,17 @@ hipError_t launch_attention_backward(const T* q, const T* k, const T* vt, const 
   if (kvT < T_seq) return hipErrorInvalidValue;
   const int rows = B * H * T_seq;
   const dim3 grid(B * H * n_tiles), block(256);
+  if constexpr (sizeof(T) == 2) {
+    if (hs == 64) {
+      hipLaunchKernelGGL((attn_bwd_dvec_kernel<T, 64>), dim3((rows + 3) / 4), block, 0, stream, o, dout, dvec, B, H,
+                         T_seq);
+      hipLaunchKernelGGL(attn_bwd_dkdv_mma_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
+                         T_seq, kvT, n_tiles);
+      hipLaunchKernelGGL(attn_bwd_dq_mma_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
+                         T_seq, kvT, n_tiles, scale);
+      return hipGetLastError();
+    }
+  }
   if (hs == 64) {
     hipLaunchKernelGGL((attn_bwd_dvec_kernel<T, 64>), dim3((rows + 3) / 4), block, 0, stream, o, dout, dvec, B, H,
                        T_seq);
