@@ -23,6 +23,10 @@ template <typename Tin>
 hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, hipStream_t stream,
                          const float* x = nullptr, const float* mu = nullptr, const float* rstd = nullptr);
 
+// out[i] = sum_{s < splits} part[s * n + i] in increasing s (the split-K
+// partial products of the weight gradients).
+hipError_t launch_sum_splits(const float* part, int splits, size_t n, float* out, hipStream_t stream);
+
 // LayerNorm backward (dpshk.com llm.c notes 5.3: mean, variance and the
 // normalised value are coupled).  Per row of x [M][D] (the LayerNorm input):
 //   xhat = (x - mu) * rstd, g = dh * gamma,

@@ -576,7 +576,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mma_kernel(const bf16_t* __re
   }
 }
 
+// out[i] = sum over s < splits of part[s * n + i], s in increasing order.
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int splits, size_t n,
+                                                          float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float s = part[i];
+    for (int k = 1; k < splits; ++k) s += part[(size_t)k * n + i];
+    out[i] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sum_splits(const float* part, int splits, size_t n, float* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, n, out);
+  return hipGetLastError();
+}
 
 template <typename Tin, typename Tout>
 hipError_t launch_transpose(const Tin* src, int R, int C, Tout* dst, int ld_dst, hipStream_t stream) {

@@ -178,18 +178,20 @@ struct EpiLogits {
 };
 
 // Backward-pass epilogues (block backward).
-// Plain store of C (fp32 or T) into out[M][ldo].
+// Plain store of C (fp32 or T) into out[M][ldo]; in a split-K launch slice y
+// stores its partial sum at out + y * split_stride.
 template <typename O>
 struct EpiStore {
   static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false,
                         kRowArgmax = false;
   O* out;
   int ldo;
+  size_t split_stride = 0;
   __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
-    Elem<O>::store4(out + (size_t)m * ldo + n, v[0], v[1], v[2], v[3]);
+    Elem<O>::store4(out + blockIdx.y * split_stride + (size_t)m * ldo + n, v[0], v[1], v[2], v[3]);
   }
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
@@ -302,6 +304,13 @@ int gemm_slice_width(GemmTile tile);
 template <typename T, class Epi>
 hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int K, int lda, int ldb,
                        const Epi& epi, hipStream_t stream);
+
+// Split-K: `splits` slices of K_split each (A and B advance by K_split per
+// slice; lda, ldb >= splits * K_split); slice y writes its partial product to
+// epi.out + y * epi.split_stride (the caller adds the slices).
+template <typename T>
+hipError_t launch_gemm_splitk(GemmTile tile, const T* A, const T* B, int M, int N, int K_split, int lda, int ldb,
+                              int splits, const EpiStore<float>& epi, hipStream_t stream);
 
 // M <= 32 (decode): one kernel for the product and the fused epilogue `epi`;
 // K % 32 == 0 (bf16) or K % 16 == 0 (fp32), no workspace.

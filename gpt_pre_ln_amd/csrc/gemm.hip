@@ -61,6 +61,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 
   extern __shared__ u32x4_t smem[];
 
+  // Split-K launches (gridDim.y > 1): slice blockIdx.y covers k in
+  // [y*K, (y+1)*K) of both operands; the epilogue places its partial sum.
+  A += (size_t)blockIdx.y * K;
+  B += (size_t)blockIdx.y * K;
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 
 template <typename T, int BM, int BN, int WGM, int WGN, int S, int KNOB, class Epi>
 hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int ldb, const Epi& epi,
-                       hipStream_t stream) {
+                       hipStream_t stream, int splits = 1) {
   constexpr int NT = WGM * WGN * 64;
   const size_t lds = (size_t)S * (BM + BN) * kStepBytes;
   auto kern = gemm_kernel<T, BM, BN, WGM, WGN, S, KNOB, Epi>;
@@ -350,7 +355,7 @@ hipError_t launch_tile(const T* A, const T* B, int M, int N, int K, int lda, int
     attr_set = true;
   }
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(NT), lds, stream, A, B, M, N, K, lda, ldb, epi);
+  hipLaunchKernelGGL(kern, dim3(ntm * ntn, splits), dim3(NT), lds, stream, A, B, M, N, K, lda, ldb, epi);
   return hipGetLastError();
 }
 
@@ -517,6 +522,30 @@ GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
+template <typename T>
+hipError_t launch_gemm_splitk(GemmTile tile, const T* A, const T* B, int M, int N, int K_split, int lda, int ldb,
+                              int splits, const EpiStore<float>& epi, hipStream_t stream) {
+  if (splits < 1 || splits > 65535) return hipErrorInvalidValue;
+  switch (tile) {
+    case kTile256x256:
+      return launch_tile<T, 256, 256, 2, 4, 2, kSplitIssue | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream,
+                                                                           splits);
+    case kTile64x64:
+      return launch_tile<T, 64, 64, 2, 2, 2, 0>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
+    case kTile32x64:
+      return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
+    case kTile64x128:
+      return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
+    case kTile128x128:
+    default:
+      return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream,
+                                                                    splits);
+  }
+}
+template hipError_t launch_gemm_splitk<float>(GemmTile, const float*, const float*, int, int, int, int, int, int,
+                                              const EpiStore<float>&, hipStream_t);
+template hipError_t launch_gemm_splitk<bf16_t>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int, int,
+                                               const EpiStore<float>&, hipStream_t);
 template hipError_t launch_gemm<float, EpiStore<float>>(GemmTile, const float*, const float*, int, int, int, int,
                                                         int, const EpiStore<float>&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiStore<float>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int,

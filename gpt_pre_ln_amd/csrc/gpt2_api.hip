@@ -517,8 +517,28 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
 // the recomputed forward of the block and the gradient temporaries.
 struct BwdLayout {
   size_t h1, q, k, vt, lse, dvec, a, xh, h2, g, u, dyt, wt_qkv, wt_o, wt_fc, wt_pr, dg, dh, dxh, dxht, da, dqkv,
-      dqkvt, ta, tb, mu, rstd, part, total;
+      dqkvt, ta, tb, mu, rstd, part, wpart, total;
 };
+
+// Weight-gradient products [Mr][N] contract over the Mp = B*T (padded)
+// positions: few output tiles, a long k loop.  Split K into the smallest
+// power of two of slices that gives at least 512 blocks (at most 16 slices,
+// each at least 512 deep and a multiple of 64).
+int wgrad_splits(int Mr, int N, int Mp) {
+  int bm = 128, bn = 128;
+  switch (pick_tile(Mr, N, Mp)) {
+    case kTile256x256: bm = bn = 256; break;
+    case kTile64x64: bm = bn = 64; break;
+    case kTile32x64: bm = 32, bn = 64; break;
+    case kTile64x128: bm = 64, bn = 128; break;
+    default: break;
+  }
+  const long tiles = (long)((Mr + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int n64 = Mp / 64;
+  int s = 1;
+  while (s < 16 && tiles * s < 512 && n64 % (2 * s) == 0 && Mp / (2 * s) >= 512) s *= 2;
+  return s;
+}
 
 BwdLayout bwd_layout(const gpt2_config& c, int B, int T) {
   BwdLayout L;
@@ -559,6 +579,13 @@ BwdLayout bwd_layout(const gpt2_config& c, int B, int T) {
   L.mu = take(M * 4);
   L.rstd = take(M * 4);
   L.part = take(colsum_partial_floats((int)wide) * 4);
+  size_t wp = 0;
+  const int Di = (int)D, Fi = (int)F, Mpi = (int)Mp;
+  for (const auto& mn : {std::pair<int, int>{Fi, Di}, {Di, Fi}, {Di, Di}, {Di, 3 * Di}}) {
+    const int s = wgrad_splits(mn.first, mn.second, Mpi);
+    if (s > 1) wp = std::max(wp, (size_t)s * mn.first * mn.second);
+  }
+  L.wpart = take(wp * 4);
   L.total = off;
   return L;
 }
@@ -602,6 +629,16 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   auto gemm_f32 = [&](const T* A, const T* Bm, int Mr, int N, int K, float* out, int ldo) {
     return launch_gemm<T>(pick_tile(Mr, N, K), A, Bm, Mr, N, K, K, K, EpiStore<float>{out, ldo}, st);
   };
+  // weight gradient [Mr][N] = A[Mr][Mp] B[N][Mp]^T, split over K when it has few tiles
+  float* wpart = fp(L.wpart);
+  auto wgrad = [&](const T* A, const T* Bm, int Mr, int N, float* out) -> hipError_t {
+    const int s = wgrad_splits(Mr, N, Mp);
+    if (s == 1) return gemm_f32(A, Bm, Mr, N, Mp, out, N);
+    hipError_t e = launch_gemm_splitk<T>(pick_tile(Mr, N, Mp), A, Bm, Mr, N, Mp / s, Mp, Mp, s,
+                                         EpiStore<float>{wpart, N, (size_t)Mr * N}, st);
+    if (e != hipSuccess) return e;
+    return launch_sum_splits(wpart, s, (size_t)Mr * N, out, st);
+  };
 
   // transposed copies of this layer's weights ([out][in] -> [in][out])
   GPT2_HIP((launch_transpose<T, T>(pp<T>(m, o.w_qkv), 3 * D, D, wt_qkv, 3 * D, st)), "bwd transpose w_qkv");
@@ -637,11 +674,11 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   GPT2_HIP(launch_colsum<float>(dy, M, D, grads + G_prb, part, st), "bwd db_pr");
   GPT2_HIP((launch_transpose<T, T>(u, M, F, ta, Mp, st)), "bwd u^T");
   GPT2_HIP((launch_transpose<T, T>(dyt, M, D, tb, Mp, st)), "bwd dy^T");
-  GPT2_HIP(gemm_f32(ta, tb, F, D, Mp, grads + G_prw, D), "bwd dW_pr");
+  GPT2_HIP(wgrad(ta, tb, F, D, grads + G_prw), "bwd dW_pr");
   GPT2_HIP(launch_colsum<T>(dg, M, F, grads + G_fcb, part, st), "bwd db_fc");
   GPT2_HIP((launch_transpose<T, T>(h2, M, D, ta, Mp, st)), "bwd h2^T");
   GPT2_HIP((launch_transpose<T, T>(dg, M, F, tb, Mp, st)), "bwd dg^T");
-  GPT2_HIP(gemm_f32(ta, tb, D, F, Mp, grads + G_fcw, F), "bwd dW_fc");
+  GPT2_HIP(wgrad(ta, tb, D, F, grads + G_fcw), "bwd dW_fc");
   GPT2_HIP(gemm_f32(dg, wt_fc, M, D, F, dh, D), "bwd dh2");
   GPT2_HIP(launch_layernorm_backward<T>(xh, dh, pf(m, o.ln2_g), dy, dxh, dxht, mu, rstd, M, D, c.ln_eps, st),
            "bwd ln_2 backward");
@@ -652,7 +689,7 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   GPT2_HIP(launch_colsum<float>(dxh, M, D, grads + G_ob, part, st), "bwd db_o");
   GPT2_HIP((launch_transpose<T, T>(a, M, D, ta, Mp, st)), "bwd a^T");
   GPT2_HIP((launch_transpose<T, T>(dxht, M, D, tb, Mp, st)), "bwd dx_h^T");
-  GPT2_HIP(gemm_f32(ta, tb, D, D, Mp, grads + G_ow, D), "bwd dW_o");
+  GPT2_HIP(wgrad(ta, tb, D, D, grads + G_ow), "bwd dW_o");
   GPT2_HIP(launch_gemm<T>(pick_tile(M, D, D), dxht, wt_o, M, D, D, D, D, EpiStore<T>{da, D}, st), "bwd da");
   GPT2_HIP(launch_attention_backward<T>(q, kk, vt, a, da, lse, dvec, dqkv, B, H, T_seq, Tp, hs, q_scale, st),
            "bwd attention backward");
@@ -660,7 +697,7 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   GPT2_HIP(launch_convert<T>(dqkv, dqkvt, (size_t)M * 3 * D, (size_t)M * 3 * D, st), "bwd dqkv");
   GPT2_HIP((launch_transpose<T, T>(h1, M, D, ta, Mp, st)), "bwd h1^T");
   GPT2_HIP((launch_transpose<T, T>(dqkvt, M, 3 * D, tb, Mp, st)), "bwd dqkv^T");
-  GPT2_HIP(gemm_f32(ta, tb, D, 3 * D, Mp, grads + G_qkvw, 3 * D), "bwd dW_qkv");
+  GPT2_HIP(wgrad(ta, tb, D, 3 * D, grads + G_qkvw), "bwd dW_qkv");
   GPT2_HIP(gemm_f32(dqkvt, wt_qkv, M, D, 3 * D, dh, D), "bwd dh1");
   GPT2_HIP(launch_layernorm_backward<T>(x, dh, pf(m, o.ln1_g), dxh, dx, static_cast<T*>(nullptr), mu, rstd, M, D,
                                         c.ln_eps, st),

@@ -111,13 +111,14 @@ def test_block_backward_matches_oracle(case):
 
 
 def test_block_backward_gpt2_small():
-    """GPT-2 small shapes: B=8 T=1024 (the benchmark batch), dx of sequences 0
-    and 7 against the oracle (sequences are independent); B=1 T=1024, every
-    gradient against the oracle."""
+    """GPT-2 small shapes: B=8 T=1024 (the benchmark batch; the weight
+    gradients take the split-K products, 4 to 16 slices), dx and every
+    gradient against the oracle over all 8 sequences; B=1 T=1024 (2 slices)
+    likewise."""
     w = W.WORKLOADS["gpt2-small-b8t1024"]
     s = w.shape
-    _announce(f"{w.name} block backward layer 5, B=8 T=1024 (dx) and B=1 (all gradients)")
+    _announce(f"{w.name} block backward layer 5, B=8 T=1024 and B=1")
     blob, x, dy, dx, g = _run(s, w.dtype, 8, 1024, 5, 901, w.init)
-    _compare(s, w.dtype, blob, x, dy, dx, g, 5, "gpt2-small B=8 seqs 0,7", seqs=[0, 7])
+    _compare(s, w.dtype, blob, x, dy, dx, g, 5, "gpt2-small B=8")
     blob, x, dy, dx, g = _run(s, w.dtype, 1, 1024, 5, 903, w.init)
     _compare(s, w.dtype, blob, x, dy, dx, g, 5, "gpt2-small B=1")
