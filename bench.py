@@ -186,10 +186,13 @@ def main():
     model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
     model.load_blob(blob)
     ids = torch.from_numpy(W.make_ids(w)).to(dev)
-    logits = torch.empty((B, T, w.shape.vocab), dtype=model.logits_torch_dtype, device=dev)
+    # logits in the padded layout (rows of logits_padded_ld elements; the
+    # caller sees the [B, T, vocab] view): the fast layout of gpt2_forward_strided
+    ld = model.logits_padded_ld
+    logits = torch.empty((B, T, ld), dtype=model.logits_torch_dtype, device=dev)
 
     def step():
-        model.forward(ids, out_logits=logits)
+        model.forward(ids, out_logits=logits, padded_logits=True)
 
     for _ in range(args.warmup):
         step()
@@ -257,11 +260,11 @@ def main():
     vmodel = GPT2.from_shape(vshape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
     vmodel.load_blob(W.make_params(vshape, w.init, w.param_seed))
     for _ in range(args.warmup):
-        vmodel.forward(ids, out_logits=logits)
+        vmodel.forward(ids, out_logits=logits, padded_logits=True)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     for _ in range(args.steps):
-        vmodel.forward(ids, out_logits=logits)
+        vmodel.forward(ids, out_logits=logits, padded_logits=True)
     torch.cuda.synchronize()
     el_v = (time.perf_counter() - t3) / args.steps
     variant_step = {"switches": ["post_ln", "scale_attn_by_inverse_layer_idx", "gelu_erf", "separate_head"],
@@ -297,13 +300,13 @@ def main():
         del logits
         model32 = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype="f32")
         model32.load_blob(blob)
-        logits32 = torch.empty((B, T, w.shape.vocab), dtype=torch.float32, device=dev)
+        logits32 = torch.empty((B, T, ld), dtype=torch.float32, device=dev)
         for _ in range(args.warmup):
-            model32.forward(ids, out_logits=logits32)
+            model32.forward(ids, out_logits=logits32, padded_logits=True)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(args.steps):
-            model32.forward(ids, out_logits=logits32)
+            model32.forward(ids, out_logits=logits32, padded_logits=True)
         torch.cuda.synchronize()
         el32 = (time.perf_counter() - t1) / args.steps
         alt = {"value": round(B * T / el32, 1), "ms_per_step": round(el32 * 1e3, 4)}
@@ -324,7 +327,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "d_model": w.shape.d_model,
                    "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": w.shape.vocab,
-                   "logits_dtype": logits_dtype},
+                   "logits_dtype": logits_dtype, "logits_row_stride": ld},
         "frac_of_peak": round(flops / (elapsed / args.steps) / (peak * 1e12), 4),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "roofline": roof,

@@ -70,6 +70,9 @@ _SIG = {
     "gpt2_init_params": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "gpt2_forward": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                     ctypes.POINTER(gpt2_kv_view), _P]),
+    "gpt2_logits_padded_ld": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.POINTER(ctypes.c_int64)]),
+    "gpt2_forward_strided": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P,
+                                            ctypes.POINTER(gpt2_kv_view), _P]),
     "gpt2_forward_loss": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
     "gpt2_generate": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, ctypes.c_int32, _P, _P]),
@@ -169,6 +172,19 @@ def gpt2_init_params(handle, d_blob: int, n_floats: int, stream: int):
 def gpt2_forward(handle, d_tokens: int, B: int, T: int, d_logits, d_hidden, kv, stream: int):
     _check(load().gpt2_forward(handle, d_tokens, B, T, d_logits, d_hidden,
                                ctypes.byref(kv) if kv is not None else None, stream), "gpt2_forward")
+
+
+def gpt2_logits_padded_ld(cfg) -> int:
+    ld = ctypes.c_int64()
+    _check(load().gpt2_logits_padded_ld(ctypes.byref(cfg), ctypes.byref(ld)), "gpt2_logits_padded_ld")
+    return ld.value
+
+
+def gpt2_forward_strided(handle, d_tokens: int, B: int, T: int, d_logits, logits_ld: int, d_hidden, kv,
+                         stream: int):
+    _check(load().gpt2_forward_strided(handle, d_tokens, B, T, d_logits, logits_ld, d_hidden,
+                                       ctypes.byref(kv) if kv is not None else None, stream),
+           "gpt2_forward_strided")
 
 
 def gpt2_forward_loss(handle, d_tokens: int, d_labels, B: int, T: int, d_token_loss, d_mean_loss, stream: int):

@@ -41,7 +41,7 @@ namespace gpt2 {
 //   apply(m, n, v, pre)  v = C[m][n .. n+3]; pre = preload(m, n) when kPreload
 //                        (the residual), fetched before the group's stores;
 //   apply_t(m, n, v)     v = C[m .. m+3][n], only when kTransposed and
-//                        transposed(n) holds for the (64-aligned) column block.
+//                        transposed(n) holds for the column block of the wave.
 // kRowReduce epilogues (EpiCE) instead receive, per row m and per column
 // slice s of one wave's width (gemm_slice_width), the maximum and the sum of
 // exp(C - maximum) over the slice's columns below n_valid, and the single
@@ -296,7 +296,7 @@ struct EpiArgmax {
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),
 // K % (128 / sizeof(T)) == 0, N % 4 == 0.  `tile` picks the tile shape
 // (see gemm.hip); returns hipSuccess or the launch error.
-enum GemmTile { kTile128x128 = 0, kTile256x256 = 1, kTile64x64 = 2, kTile32x64 = 3, kTile64x128 = 4 };
+enum GemmTile { kTile128x128 = 0, kTile256x256 = 1, kTile64x64 = 2, kTile32x64 = 3, kTile64x128 = 4, kTile128x96 = 5 };
 
 // Width of the column slice one wave owns in `tile` (the kRowReduce slice).
 int gemm_slice_width(GemmTile tile);

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
     else p = reinterpret_cast<const char*>(B + (size_t)min(n0 + row - BM, N - 1) * ldb);
     gsrc[j] = p + c * 16;
   }
+  const int KT = K / KE;
   auto issue = [&](int kt, int j0, int j1) {
     const size_t off = (size_t)kt * kStepBytes;
     u32x4_t* base = smem + (kt % S) * STAGE;
@@ -103,7 +104,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = K / KE;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < KT) issue(s, 0, RBW);
@@ -275,11 +275,22 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
   // row segments instead of 16 rows x 16 columns.
   constexpr int LDS_F = S * (BM + BN) * kStepBytes / 4;  // floats of LDS
   constexpr int PER_WAVE = LDS_F / NW;
-  constexpr int R = WTM < PER_WAVE / WTN ? WTM : PER_WAVE / WTN;  // rows staged per round
-  static_assert(R % 16 == 0 && WTM % R == 0, "staging rounds must hold whole fragments");
   constexpr int CPR = WTN / 4;  // 16-byte chunks per staged row (row mode)
+  // Rows of a power-of-two number of chunks are XOR-swizzled; other widths
+  // (48-column waves of the 128x96 tile) are padded by one chunk instead,
+  // which puts 8 consecutive rows in distinct bank groups as well.
+  constexpr bool kPow2Row = (CPR & (CPR - 1)) == 0;
+  constexpr int RS = kPow2Row ? WTN : WTN + 4;  // staged row stride, floats
+  constexpr int R = [] {  // rows staged per round: whole fragments that divide WTM
+    int r = WTM < PER_WAVE / RS ? WTM : PER_WAVE / RS;
+    r -= r % 16;
+    while (r > 16 && WTM % r) r -= 16;
+    return r;
+  }();
+  static_assert(R % 16 == 0 && WTM % R == 0, "staging rounds must hold whole fragments");
   constexpr int CPT = R / 4;    // 16-byte chunks per staged column (transposed mode)
-  static_assert(CPR <= 16 && CPT <= 16 && 64 % CPR == 0 && 64 % CPT == 0, "lane mapping");
+  static_assert(CPR <= 16 && CPT <= 16 && (64 % CPR == 0 || !kPow2Row) && 64 % CPT == 0, "lane mapping");
+  auto slot = [](int r, int c) { return kPow2Row ? (c ^ (r & (CPR - 1))) : c; };
 
   // every wave is past its last operand read (its MFMAs consumed them) and
   // the last stage's loads have landed (vmcnt(0) in the last step)
@@ -293,27 +304,30 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
   for (int rd = 0; rd < WTM / R; ++rd) {
     const int mr = mw + rd * R;  // first row of this round
     if (!tr) {
-      // row-major [R][WTN] with chunk c of row r at slot c ^ (r % CPR)
+      // row-major [R][RS] with chunk c of row r at slot(r, c)
 #pragma unroll
       for (int i = 0; i < R / 16; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int r = i * 16 + lr, c = j * 4 + lg;
-          *reinterpret_cast<f32x4_t*>(stg + r * WTN + ((c ^ (r & (CPR - 1))) << 2)) = acc[rd * (R / 16) + i][j];
+          *reinterpret_cast<f32x4_t*>(stg + r * RS + (slot(r, c) << 2)) = acc[rd * (R / 16) + i][j];
         }
-      constexpr int RPI = 64 / CPR;  // rows per read instruction
+      constexpr int RPI = 64 / CPR;            // rows per read instruction
+      constexpr int NQ = (R + RPI - 1) / RPI;  // read instructions per round
       const int c = lane % CPR;
       const int n = nw + c * 4;
-      float4 pre[R / RPI];
+      const bool lane_on = lane < RPI * CPR;   // every lane when CPR divides 64
+      float4 pre[NQ];
       if constexpr (Epi::kPreload) {
 #pragma unroll
-        for (int q = 0; q < R / RPI; ++q)
-          pre[q] = epi.preload(min(mr + q * RPI + lane / CPR, M - 1), min(n, N - 4));
+        for (int q = 0; q < NQ; ++q)
+          pre[q] = epi.preload(min(mr + min(q * RPI + lane / CPR, R - 1), M - 1), min(n, N - 4));
       }
 #pragma unroll
-      for (int q = 0; q < R / RPI; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const int r = q * RPI + lane / CPR;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * WTN + ((c ^ (r & (CPR - 1))) << 2));
+        if (!lane_on || r >= R) continue;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c) << 2));
         const int m = mr + r;
         if (m < M && n < N) epi.apply(m, n, v, pre[q]);
       }
@@ -451,6 +465,7 @@ int gemm_slice_width(GemmTile tile) {
     case kTile64x64: return 64 / 2;
     case kTile32x64: return 64 / 2;
     case kTile64x128: return 128 / 2;
+    case kTile128x96: return 96 / 2;
     case kTile128x128:
     default: return 128 / 2;
   }
@@ -468,6 +483,8 @@ hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int 
       return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile64x128:
       return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
+    case kTile128x96:
+      return launch_tile<T, 128, 96, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x128:
     default:
       return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
@@ -536,6 +553,8 @@ hipError_t launch_gemm_splitk(GemmTile tile, const T* A, const T* B, int M, int 
       return launch_tile<T, 32, 64, 2, 2, 2, 0>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
     case kTile64x128:
       return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
+    case kTile128x96:
+      return launch_tile<T, 128, 96, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
     case kTile128x128:
     default:
       return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream,

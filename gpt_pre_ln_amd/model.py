@@ -87,19 +87,31 @@ class GPT2:
                              f"on {self.device}")
         return out
 
+    @property
+    def logits_padded_ld(self) -> int:
+        """Row stride of the padded logits layout (gpt2_logits_padded_ld)."""
+        return B.gpt2_logits_padded_ld(self.cfg)
+
     def forward(self, ids: torch.Tensor, logits: bool = True, hidden: bool = False, kv: KVCache | None = None,
-                out_logits: torch.Tensor | None = None):
+                out_logits: torch.Tensor | None = None, padded_logits: bool = False):
         """ids: int32 [B, T] on the device.
-        Returns (logits [B,T,V] of logits_dtype | None, hidden [B,T,D] fp32 | None)."""
+        Returns (logits [B,T,V] of logits_dtype | None, hidden [B,T,D] fp32 | None).
+
+        padded_logits: the logits live in rows of logits_padded_ld elements
+        (gpt2_forward_strided, the faster layout); the result is the [B,T,V]
+        view of that buffer, and out_logits, when given, is the [B,T,ld] buffer."""
         assert ids.dtype == torch.int32 and ids.is_contiguous() and ids.device == self.device
         Bsz, T = ids.shape
-        lg = None
+        V = self.cfg.vocab_size
+        ld = self.logits_padded_ld if padded_logits else V
+        buf = None
         if logits:
-            lg = self._logits_out((Bsz, T, self.cfg.vocab_size), out_logits)
+            buf = self._logits_out((Bsz, T, ld), out_logits)
         hd = torch.empty((Bsz, T, self.cfg.d_model), dtype=torch.float32, device=self.device) if hidden else None
-        B.gpt2_forward(self.handle, ids.data_ptr(), Bsz, T, lg.data_ptr() if lg is not None else None,
-                       hd.data_ptr() if hd is not None else None, kv.view if kv is not None else None,
-                       self.stream)
+        B.gpt2_forward_strided(self.handle, ids.data_ptr(), Bsz, T, buf.data_ptr() if buf is not None else None, ld,
+                               hd.data_ptr() if hd is not None else None, kv.view if kv is not None else None,
+                               self.stream)
+        lg = buf[..., :V] if buf is not None and ld != V else buf
         return lg, hd
 
     def loss(self, ids: torch.Tensor, labels: torch.Tensor | None = None, token_loss: bool = False,

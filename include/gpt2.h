@@ -146,6 +146,27 @@ gpt2_status gpt2_init_params(gpt2_model* model, const float* d_blob, size_t n_fl
 gpt2_status gpt2_forward(gpt2_model* model, const int32_t* d_tokens, int32_t B, int32_t T,
                          void* d_logits, float* d_hidden, gpt2_kv_view* kv, void* stream);
 
+/* Row stride (elements) of the padded logits layout: vocab_size rounded up to
+ * the device padding of the embedding matrix (a multiple of 256). */
+gpt2_status gpt2_logits_padded_ld(const gpt2_config* cfg, int64_t* ld);
+
+/* gpt2_forward with the logits rows logits_ld elements apart: row b*T + t
+ * starts at d_logits + (b*T + t) * logits_ld, and the caller's buffer holds
+ * (B*T - 1) * logits_ld + vocab_size elements (B*T * logits_ld when
+ * logits_ld >= the padded stride).  Same computation as gpt2_forward (the
+ * tied lm_head of pwwt.cn section GPT2LMHeadModel).
+ *   logits_ld >= gpt2_logits_padded_ld: every row is written in whole; the
+ *     columns [vocab_size, padded ld) receive 0 (the logits of the zero
+ *     padding rows of the embedding) and columns past that are not written.
+ *     This is the fast layout: no per-column test at the vocabulary edge, and
+ *     rows aligned to the buffer's alignment.
+ *   vocab_size <= logits_ld < padded ld: only columns [0, vocab_size) are written.
+ * Errors: GPT2_ERR_SHAPE when d_logits is given and logits_ld < vocab_size or
+ * logits_ld > INT32_MAX; the other checks are those of gpt2_forward. */
+gpt2_status gpt2_forward_strided(gpt2_model* model, const int32_t* d_tokens, int32_t B, int32_t T,
+                                 void* d_logits, int64_t logits_ld, float* d_hidden, gpt2_kv_view* kv,
+                                 void* stream);
+
 /* Next-token cross-entropy of B sequences of T tokens (2 <= T <= n_positions),
  * pwwt.cn section GPT2LMHeadModel (its second design): the logits of position
  * t are scored against the label of position t + 1 -- the shift happens here,

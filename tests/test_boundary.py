@@ -166,6 +166,20 @@ def test_forward_host_checks(B, handle):
     assert fwd(FAKE, 2, 8, kv=kv) == B.GPT2_ERR_INVALID_ARG
 
 
+def test_forward_strided_host_checks(B, handle):
+    h, cfg = handle
+    lib = B.load()
+    assert B.gpt2_logits_padded_ld(cfg) == 1024                    # vocab 1000 -> multiple of 256
+    assert B.gpt2_logits_padded_ld(B.make_config(50257, 1024, 768, 12, 12, 3072, 1e-5, "bf16")) == 50432
+    fwd = lambda ld, lg=FAKE, Bz=1, T=8: lib.gpt2_forward_strided(h, FAKE, Bz, T, lg, ld, None, None, None)
+    assert fwd(999) == B.GPT2_ERR_SHAPE                          # row stride below the vocabulary
+    assert fwd(1 << 31) == B.GPT2_ERR_SHAPE                      # beyond int32
+    assert fwd(999, lg=None, Bz=4, T=64) == B.GPT2_ERR_WORKSPACE  # no logits: the stride is not checked
+    assert fwd(1024, lg=FAKE + 1) == B.GPT2_ERR_INVALID_ARG       # bf16 logits need 2-byte alignment
+    assert fwd(1024, Bz=4, T=64) == B.GPT2_ERR_WORKSPACE
+    assert lib.gpt2_forward_strided(h, None, 1, 8, FAKE, 1024, None, None, None) == B.GPT2_ERR_INVALID_ARG
+
+
 def test_forward_loss_host_checks(B, handle):
     h, cfg = handle
     lib = B.load()

@@ -173,6 +173,49 @@ def test_sharp_attention_scores():
     assert_logits(lg, np.einsum("btd,vd->btv", ref_h, P["wte"]), "f32", "sharp attention")
 
 
+@pytest.mark.parametrize("dtype,logits_dtype", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_padded_logits_layout(dtype, logits_dtype):
+    """gpt2_forward_strided with the padded row stride: the [B,T,V] view holds
+    the same values as the contiguous layout (same kernels and accumulators),
+    the padding columns hold 0, and nothing past the padded stride is written."""
+    from gpt_pre_ln_amd.model import GPT2
+    s = W.ModelShape(vocab=777, n_positions=160, d_model=128, n_head=2, n_layer=2, d_ff=512)
+    Bsz, T = 3, 150
+    _announce(f"padded logits {dtype}/{logits_dtype} V={s.vocab} B={Bsz} T={T}")
+    blob = W.make_params(s, _init_small(), 11)
+    ids = np.random.default_rng(12).integers(0, s.vocab, size=(Bsz, T)).astype(np.int32)
+    m = GPT2.from_shape(s, dtype, max_batch=Bsz, max_seq=T, logits_dtype=logits_dtype)
+    m.load_blob(blob)
+    ld = m.logits_padded_ld
+    assert ld == 1024
+    ref = m.forward(_ids_dev(ids))[0]
+    buf = torch.full((Bsz, T, ld + 64), 7.0, dtype=ref.dtype, device=DEV)
+    view = buf[..., :ld]   # rows ld + 64 apart: columns [ld, ld + 64) must stay untouched
+    from gpt_pre_ln_amd import binding as Bn
+    Bn.gpt2_forward_strided(m.handle, _ids_dev(ids).data_ptr(), Bsz, T, buf.data_ptr(), ld + 64, None, None, m.stream)
+    torch.cuda.synchronize()
+    assert torch.equal(view[..., :s.vocab], ref)
+    assert (view[..., s.vocab:] == 0).all()
+    assert (buf[..., ld:] == 7.0).all()
+    lg, _ = m.forward(_ids_dev(ids), padded_logits=True)
+    assert lg.shape == (Bsz, T, s.vocab) and torch.equal(lg, ref)
+
+
+def test_padded_logits_gpt2_small_full_size():
+    """The padded layout on the GPT-2 small B=8 T=1024 lm_head (256x256 tiles,
+    whole rows): bitwise the contiguous logits, zero padding columns."""
+    w = W.WORKLOADS["gpt2-small-b8t1024"]
+    _announce(f"{w.name} padded logits")
+    m = _model(w.shape, w.dtype, w.batch, w.seq_len, W.make_params(w))
+    ids = _ids_dev(W.make_ids(w))
+    ref = m.forward(ids)[0]
+    lg, _ = m.forward(ids, padded_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, ref)
+    base = lg.as_strided((w.batch, w.seq_len, m.logits_padded_ld), lg.stride())
+    assert (base[..., w.shape.vocab:] == 0).all()
+
+
 def test_fp32_logits_from_bf16_model():
     """logits_dtype f32 on a bf16 model: the same lm_head products, stored unrounded."""
     _announce("bf16 model, fp32 logits")
@@ -259,6 +302,24 @@ def test_gpt2_small_b8t1024():
     for b in (0, 7):
         ref = oracle.forward(P, ids[b:b + 1])[0]
         assert_logits(lg[b].float().cpu().numpy(), ref, w.dtype, f"{w.name} seq {b}")
+
+
+def test_gpt2_small_b8t1020_ragged_tiles():
+    """B*T = 8160 is not a multiple of the 128-row tiles, and T = 1020 puts
+    sequence boundaries inside tiles: the 128x96 projections (qkv, both
+    c_proj) and the 256x256 lm_head with its ragged last tile-row."""
+    w = W.WORKLOADS["gpt2-small-b8t1024"]
+    T = 1020
+    _announce(f"{w.name} shape B={w.batch} T={T}")
+    blob = W.make_params(w)
+    ids = np.ascontiguousarray(W.make_ids(w)[:, :T])
+    m = _model(w.shape, w.dtype, w.batch, T, blob)
+    lg = m.forward(_ids_dev(ids))[0]
+    torch.cuda.synchronize()
+    P = oracle.prepare_params(blob, w.shape, w.dtype)
+    for b in (3, 7):
+        ref = oracle.forward(P, ids[b:b + 1])[0]
+        assert_logits(lg[b].float().cpu().numpy(), ref, w.dtype, f"{w.name} T={T} seq {b}")
 
 
 def test_gpt2_small_decode_b32p1023():
