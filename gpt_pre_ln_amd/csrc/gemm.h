@@ -151,6 +151,7 @@ struct EpiGelu {
 // unaligned 16- or 8-byte store, masked per element at the vocabulary edge.
 typedef float f32x4_u4_t __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_u2_t __attribute__((ext_vector_type(2), aligned(2)));
+typedef uint32_t u32x4_u2_t __attribute__((ext_vector_type(4), aligned(2)));
 template <typename O>
 struct EpiLogits {
   static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false, kRowArgmax = false;
@@ -175,6 +176,20 @@ struct EpiLogits {
     }
   }
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+  // bf16 logits only: a = C[m][n .. n+3], b = C[m][n+4 .. n+7], one 16-byte store
+  template <typename Q = O>
+    requires(sizeof(Q) == 2)
+  __device__ __forceinline__ void apply8(int m, int n, const f32x4_t& a, const f32x4_t& b) const {
+    O* p = out + (size_t)m * ldo + n;
+    if (n + 7 < n_valid) {
+      *reinterpret_cast<u32x4_u2_t*>(p) =
+          u32x4_u2_t{pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]), pack2_bf16(b[0], b[1]), pack2_bf16(b[2], b[3])};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < n_valid) p[e] = Elem<O>::from_f32(e < 4 ? a[e] : b[e - 4]);
+    }
+  }
 };
 
 // Backward-pass epilogues (block backward).

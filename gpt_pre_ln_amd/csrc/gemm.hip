@@ -312,6 +312,24 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
           const int r = i * 16 + lr, c = j * 4 + lg;
           *reinterpret_cast<f32x4_t*>(stg + r * RS + (slot(r, c) << 2)) = acc[rd * (R / 16) + i][j];
         }
+      if constexpr (kPow2Row && requires { epi.apply8(0, 0, f32x4_t{}, f32x4_t{}); }) {
+        // 8 columns per lane (two adjacent staged chunks): one 16-byte store
+        // per lane, 8 lanes per 64-column row segment (bf16 logits; 736 ->
+        // 725 us for the GPT-2 small lm_head standalone)
+        constexpr int LPR = CPR / 2, RPW = 64 / LPR;
+        static_assert(R % RPW == 0, "whole rows per store instruction");
+        const int c2 = (lane % LPR) * 2;
+        const int n = nw + c2 * 4;
+#pragma unroll
+        for (int q = 0; q < R / RPW; ++q) {
+          const int r = q * RPW + lane / LPR;
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c2) << 2));
+          const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c2 + 1) << 2));
+          const int m = mr + r;
+          if (m < M && n < N) epi.apply8(m, n, v0, v1);
+        }
+        continue;
+      }
       constexpr int RPI = 64 / CPR;            // rows per read instruction
       constexpr int NQ = (R + RPI - 1) / RPI;  // read instructions per round
       const int c = lane % CPR;
