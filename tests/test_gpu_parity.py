@@ -304,6 +304,23 @@ def test_gpt2_small_b8t1024():
         assert_logits(lg[b].float().cpu().numpy(), ref, w.dtype, f"{w.name} seq {b}")
 
 
+def test_gpt2_small_shape_fp32():
+    """The GPT-2 small shape in fp32 (fp32 MFMA operands, fp32 logits) at
+    B=8 T=1024: the 128x96 projection tiles and the 256x256 lm_head on the
+    fp32 path, checked to the fp32 tolerance and exact argmax on one sequence."""
+    w = W.WORKLOADS["gpt2-small-b8t1024"]
+    _announce(f"{w.name} shape in f32 B={w.batch} T={w.seq_len}")
+    blob = W.make_params(w)
+    ids = W.make_ids(w)
+    m = _model(w.shape, "f32", w.batch, w.seq_len, blob)
+    lg = m.forward(_ids_dev(ids))[0]
+    torch.cuda.synchronize()
+    got = lg[5].cpu().numpy().astype(np.float64)
+    del lg, m
+    ref = oracle.forward(oracle.prepare_params(blob, w.shape, "f32"), ids[5:6])[0]
+    assert_logits(got, ref, "f32", f"{w.name} f32 seq 5")
+
+
 def test_gpt2_small_b8t1020_ragged_tiles():
     """B*T = 8160 is not a multiple of the 128-row tiles, and T = 1020 puts
     sequence boundaries inside tiles: the 128x96 projections (qkv, both
