@@ -1,6 +1,8 @@
 // Block backward kernels (see backward.h).
 #include "backward.h"
 
+#include <type_traits>
+
 namespace gpt2 {
 
 namespace {
@@ -23,6 +25,42 @@ __global__ __launch_bounds__(256) void transpose_kernel(const Tin* __restrict__ 
   for (int i = ty; i < 32; i += 8) {
     const int c = c0 + i, r = r0 + tx;
     if (c < C && r < ld_dst) dst[(size_t)c * ld_dst + r] = Elem<Tout>::from_f32(tile[tx][i]);
+  }
+}
+
+// bf16 -> bf16 transpose on 64x64 tiles with 16-byte global accesses:
+// thread t reads 8 consecutive elements (16 bytes) of source row t/8 (+32),
+// and writes 8 consecutive destination elements, i.e. one source column over
+// 8 consecutive source rows, gathered from the LDS tile.  Needs C and ld_dst
+// multiples of 8 and 16-byte aligned pointers; rows r >= R read as 0, so the
+// destination columns R .. ld_dst-1 receive zeros.  A tile row is 64 + 2
+// elements (132 bytes) so the column gathers of one read instruction fall in
+// different banks.
+__global__ __launch_bounds__(256) void transpose64_bf16_kernel(const bf16_t* __restrict__ src, int R, int C,
+                                                                bf16_t* __restrict__ dst, int ld_dst) {
+  __shared__ uint16_t tile[64][66];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, cc = (tid & 7) * 8;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = (tid >> 3) + 32 * p, r = r0 + row, c = c0 + cc;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * C + c);
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[row][cc]);
+    t[0] = v[0];
+    t[1] = v[1];
+    t[2] = v[2];
+    t[3] = v[3];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int col = (tid >> 3) + 32 * p, c = c0 + col, r = r0 + cc;  // 8 source rows r .. r+7 of column c
+    if (c >= C || r >= ld_dst) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[cc + 2 * e][col] | ((uint32_t)tile[cc + 2 * e + 1][col] << 16);
+    *reinterpret_cast<u32x4_t*>(dst + (size_t)c * ld_dst + r) = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -50,6 +88,61 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restri
   red[ry][cx] = s;
   __syncthreads();
   if (ry == 0 && n < N) part[(size_t)rc * N + n] = ((red[0][cx] + red[1][cx]) + red[2][cx]) + red[3][cx];
+}
+
+// As colsum_partial_kernel with VEC consecutive columns per thread read as
+// one 16-byte load (8 bf16 or 4 fp32): the block covers 64*VEC columns, and
+// every column is summed in the same order as there (rows ry, ry+4, ... of
+// the chunk, then the four lane sums in order), so the result is the same.
+// Needs N % VEC == 0 and 16-byte aligned rows.
+template <typename Tin, bool kXhat>
+__global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __restrict__ src, int M, int N,
+                                                                  float* __restrict__ part, const float* __restrict__ x,
+                                                                  const float* __restrict__ mu,
+                                                                  const float* __restrict__ rstd) {
+  constexpr int VEC = 16 / (int)sizeof(Tin);
+  __shared__ float red[4][64 * VEC];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int n = (blockIdx.x * 64 + cx) * VEC, rc = blockIdx.y;
+  const int rows = (M + kColChunks - 1) / kColChunks;
+  const int m0 = rc * rows, m1 = min(M, m0 + rows);
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+  if (n < N) {
+    for (int m = m0 + ry; m < m1; m += 4) {
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + (size_t)m * N + n);
+      float v[VEC];
+      if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf16_to_f32(raw[e] & 0xFFFF);
+          v[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+        }
+      } else {
+        const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = f[e];
+      }
+      if constexpr (kXhat) {
+        const float mm = mu[m], rs = rstd[m];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] *= (x[(size_t)m * N + n + e] - mm) * rs;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s[e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) red[ry][cx * VEC + e] = s[e];
+  __syncthreads();
+  if (ry == 0 && n < N) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int j = cx * VEC + e;
+      part[(size_t)rc * N + n + e] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int N,
@@ -599,6 +692,15 @@ hipError_t launch_sum_splits(const float* part, int splits, size_t n, float* out
 template <typename Tin, typename Tout>
 hipError_t launch_transpose(const Tin* src, int R, int C, Tout* dst, int ld_dst, hipStream_t stream) {
   if (ld_dst < R) return hipErrorInvalidValue;
+  if constexpr (std::is_same_v<Tin, bf16_t> && std::is_same_v<Tout, bf16_t>) {
+    if (C % 8 == 0 && ld_dst % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      const dim3 grid((ld_dst + 63) / 64, (C + 63) / 64);
+      if (grid.x == 0 || grid.y == 0) return hipSuccess;
+      hipLaunchKernelGGL(transpose64_bf16_kernel, grid, dim3(256), 0, stream, src, R, C, dst, ld_dst);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid((ld_dst + 31) / 32, (C + 31) / 32);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   hipLaunchKernelGGL((transpose_kernel<Tin, Tout>), grid, dim3(256), 0, stream, src, R, C, dst, ld_dst);
@@ -611,6 +713,18 @@ template <typename Tin>
 hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, hipStream_t stream, const float* x,
                          const float* mu, const float* rstd) {
   if (N <= 0) return hipSuccess;
+  constexpr int VEC = 16 / (int)sizeof(Tin);
+  if (N % VEC == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    const dim3 gridv((N / VEC + 63) / 64, kColChunks);
+    if (x)
+      hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, true>), gridv, dim3(256), 0, stream, src, M, N, part, x, mu,
+                         rstd);
+    else
+      hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, false>), gridv, dim3(256), 0, stream, src, M, N, part, x,
+                         mu, rstd);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
+    return hipGetLastError();
+  }
   const dim3 grid1((N + 63) / 64, kColChunks);
   if (x)
     hipLaunchKernelGGL((colsum_partial_kernel<Tin, true>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu, rstd);

@@ -198,14 +198,19 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 // The erf GELU, 0.5 x (1 + erf(x / sqrt(2))), with the device library's erff.
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-// Derivatives for the backward pass (device library tanhf / erff / expf):
+// Derivatives for the backward pass:
 // gelu_new'(x) = 0.5 (1 + t) + 0.5 x (1 - t^2) k (1 + 3 c x^2),
-//   t = tanh(k (x + c x^3)), k = sqrt(2/pi), c = 0.044715;
-// gelu'(x) = Phi(x) + x phi(x) for the erf form.
+//   t = tanh(y), y = k (x + c x^3), k = sqrt(2/pi), c = 0.044715.
+// With s = (1 + t) / 2 = 1 / (1 + exp(-2y)) (the sigmoid the forward uses)
+// and 1 - t^2 = 4 s (1 - s) this is s + 2 x s (1 - s) k (1 + 3 c x^2): one
+// exp2 and one reciprocal, as in gelu_tanh; s saturates to 0 or 1 without NaN.
+// gelu'(x) = Phi(x) + x phi(x) for the erf form (device library erff / expf).
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
   const float k = 0.7978845608028654f, c = 0.044715f;
-  const float t = tanhf(k * (x + c * x * x * x));
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * c * x * x);
+  const float c1 = -2.3022081981f, c3 = -0.1029432396f;  // -2 k log2(e), times c
+  const float x2 = x * x;
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * (c1 + c3 * x2)));
+  return s + 2.0f * x * s * (1.0f - s) * k * (1.0f + 3.0f * c * x2);
 }
 __device__ __forceinline__ float gelu_erf_grad(float x) {
   return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * expf(-0.5f * x * x) * 0.3989422804014327f;
