@@ -23,6 +23,23 @@ template <typename Tin>
 hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, hipStream_t stream,
                          const float* x = nullptr, const float* mu = nullptr, const float* rstd = nullptr);
 
+// The first pass of launch_colsum alone, into part (colsum_partial_floats(N)
+// floats); with x / mu / rstd and part_plain given, the same read of src also
+// fills part_plain with the plain-sum partials.  launch_colsum_final then
+// finishes up to kMaxColsumJobs sums in one launch, each as launch_colsum
+// would (same order, same result).
+template <typename Tin>
+hipError_t launch_colsum_partial(const Tin* src, int M, int N, float* part, hipStream_t stream,
+                                 const float* x = nullptr, const float* mu = nullptr, const float* rstd = nullptr,
+                                 float* part_plain = nullptr);
+constexpr int kMaxColsumJobs = 8;
+struct ColsumJob {
+  const float* part;  // colsum_partial_floats(N) floats from launch_colsum_partial
+  float* out;         // [N]
+  int N;
+};
+hipError_t launch_colsum_final(const ColsumJob* jobs, int n_jobs, hipStream_t stream);
+
 // out[i] = sum_{s < splits} part[s * n + i] in increasing s (the split-K
 // partial products of the weight gradients).
 hipError_t launch_sum_splits(const float* part, int splits, size_t n, float* out, hipStream_t stream);

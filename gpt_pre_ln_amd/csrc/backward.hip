@@ -1,6 +1,7 @@
 // Block backward kernels (see backward.h).
 #include "backward.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace gpt2 {
@@ -94,14 +95,21 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const Tin* __restri
 // one 16-byte load (8 bf16 or 4 fp32): the block covers 64*VEC columns, and
 // every column is summed in the same order as there (rows ry, ry+4, ... of
 // the chunk, then the four lane sums in order), so the result is the same.
-// Needs N % VEC == 0 and 16-byte aligned rows.
+// Needs N % VEC == 0 and 16-byte aligned rows.  With part2 given (x-hat
+// form only) the same pass also writes the plain sums of src to part2 (the
+// LayerNorm gamma and beta gradients from one read of the row gradient).
 template <typename Tin, bool kXhat>
 __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __restrict__ src, int M, int N,
                                                                   float* __restrict__ part, const float* __restrict__ x,
                                                                   const float* __restrict__ mu,
-                                                                  const float* __restrict__ rstd) {
+                                                                  const float* __restrict__ rstd,
+                                                                  float* __restrict__ part2) {
   constexpr int VEC = 16 / (int)sizeof(Tin);
   __shared__ float red[4][64 * VEC];
+  __shared__ float red2[kXhat ? 4 : 1][kXhat ? 64 * VEC : 1];
+  float s2[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s2[e] = 0.f;
   const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
   const int n = (blockIdx.x * 64 + cx) * VEC, rc = blockIdx.y;
   const int rows = (M + kColChunks - 1) / kColChunks;
@@ -127,7 +135,10 @@ __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __re
       if constexpr (kXhat) {
         const float mm = mu[m], rs = rstd[m];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] *= (x[(size_t)m * N + n + e] - mm) * rs;
+        for (int e = 0; e < VEC; ++e) {
+          s2[e] += v[e];
+          v[e] *= (x[(size_t)m * N + n + e] - mm) * rs;
+        }
       }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) s[e] += v[e];
@@ -135,14 +146,35 @@ __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __re
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) red[ry][cx * VEC + e] = s[e];
+  if constexpr (kXhat) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red2[ry][cx * VEC + e] = s2[e];
+  }
   __syncthreads();
   if (ry == 0 && n < N) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const int j = cx * VEC + e;
       part[(size_t)rc * N + n + e] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+      if constexpr (kXhat) {
+        if (part2) part2[(size_t)rc * N + n + e] = ((red2[0][j] + red2[1][j]) + red2[2][j]) + red2[3][j];
+      }
     }
   }
+}
+
+// Second pass for several column sums in one launch (blockIdx.y = job):
+// out[n] = sum over row chunks rc of part[rc][n], in increasing rc.
+struct ColsumFinalArgs {
+  ColsumJob job[kMaxColsumJobs];
+};
+__global__ __launch_bounds__(256) void colsum_final_group_kernel(ColsumFinalArgs a) {
+  const ColsumJob j = a.job[blockIdx.y];
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= j.N) return;
+  float s = 0.f;
+  for (int rc = 0; rc < kColChunks; ++rc) s += j.part[(size_t)rc * j.N + n];
+  j.out[n] = s;
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int N,
@@ -718,10 +750,10 @@ hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, 
     const dim3 gridv((N / VEC + 63) / 64, kColChunks);
     if (x)
       hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, true>), gridv, dim3(256), 0, stream, src, M, N, part, x, mu,
-                         rstd);
+                         rstd, nullptr);
     else
       hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, false>), gridv, dim3(256), 0, stream, src, M, N, part, x,
-                         mu, rstd);
+                         mu, rstd, nullptr);
     hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
     return hipGetLastError();
   }
@@ -732,6 +764,48 @@ hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, 
     hipLaunchKernelGGL((colsum_partial_kernel<Tin, false>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu,
                        rstd);
   hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
+  return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_colsum_partial(const Tin* src, int M, int N, float* part, hipStream_t stream, const float* x,
+                                 const float* mu, const float* rstd, float* part_plain) {
+  if (N <= 0) return hipSuccess;
+  if (part_plain && !x) return hipErrorInvalidValue;
+  constexpr int VEC = 16 / (int)sizeof(Tin);
+  if (N % VEC == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    const dim3 gridv((N / VEC + 63) / 64, kColChunks);
+    if (x)
+      hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, true>), gridv, dim3(256), 0, stream, src, M, N, part, x, mu,
+                         rstd, part_plain);
+    else
+      hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, false>), gridv, dim3(256), 0, stream, src, M, N, part, x,
+                         mu, rstd, nullptr);
+    return hipGetLastError();
+  }
+  const dim3 grid1((N + 63) / 64, kColChunks);
+  if (x) {
+    hipLaunchKernelGGL((colsum_partial_kernel<Tin, true>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu, rstd);
+    if (part_plain)
+      hipLaunchKernelGGL((colsum_partial_kernel<Tin, false>), grid1, dim3(256), 0, stream, src, M, N, part_plain, x,
+                         mu, rstd);
+  } else {
+    hipLaunchKernelGGL((colsum_partial_kernel<Tin, false>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu,
+                       rstd);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_final(const ColsumJob* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 1 || n_jobs > kMaxColsumJobs) return hipErrorInvalidValue;
+  ColsumFinalArgs a{};
+  int n_max = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    a.job[i] = jobs[i];
+    n_max = std::max(n_max, jobs[i].N);
+  }
+  if (n_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_final_group_kernel, dim3((n_max + 255) / 256, n_jobs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -805,6 +879,10 @@ template hipError_t launch_colsum<float>(const float*, int, int, float*, float*,
                                          const float*, const float*);
 template hipError_t launch_colsum<bf16_t>(const bf16_t*, int, int, float*, float*, hipStream_t, const float*,
                                           const float*, const float*);
+template hipError_t launch_colsum_partial<float>(const float*, int, int, float*, hipStream_t, const float*,
+                                                 const float*, const float*, float*);
+template hipError_t launch_colsum_partial<bf16_t>(const bf16_t*, int, int, float*, hipStream_t, const float*,
+                                                  const float*, const float*, float*);
 template hipError_t launch_layernorm_backward<float>(const float*, const float*, const float*, const float*, float*,
                                                      float*, float*, float*, int, int, float, hipStream_t);
 template hipError_t launch_layernorm_backward<bf16_t>(const float*, const float*, const float*, const float*, float*,

@@ -598,7 +598,9 @@ BwdLayout bwd_layout(const gpt2_config& c, int B, int T) {
   L.tb = take(wide * Mp * es);
   L.mu = take(M * 4);
   L.rstd = take(M * 4);
-  L.part = take(colsum_partial_floats((int)wide) * 4);
+  // first-pass partials of the eight column sums (biases, gamma, beta), kept
+  // until one grouped second pass at the end: D + F + 2D + D + 3D + 2D columns
+  L.part = take(colsum_partial_floats((int)(9 * D + F)) * 4);
   size_t wp = 0;
   const int Di = (int)D, Fi = (int)F, Mpi = (int)Mp;
   for (const auto& mn : {std::pair<int, int>{Fi, Di}, {Di, Fi}, {Di, Di}, {Di, 3 * Di}}) {
@@ -691,29 +693,43 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
     EpiGeluBwd<T> e{gpre, dg, F, c.activation};
     GPT2_HIP(launch_gemm<T>(pick_tile(M, F, D), dyt, wt_pr, M, F, D, D, D, e, st), "bwd du");
   }
-  GPT2_HIP(launch_colsum<float>(dy, M, D, grads + G_prb, part, st), "bwd db_pr");
+  // column sums: first passes into their own partial slots now (their sources
+  // are overwritten later), one grouped second pass at the end
+  ColsumJob cjobs[kMaxColsumJobs];
+  int n_cjobs = 0;
+  float* pslot = part;
+  auto colsum_slot = [&](int N, float* out) {
+    float* p = pslot;
+    pslot += colsum_partial_floats(N);
+    cjobs[n_cjobs++] = ColsumJob{p, out, N};
+    return p;
+  };
+  GPT2_HIP(launch_colsum_partial<float>(dy, M, D, colsum_slot(D, grads + G_prb), st), "bwd db_pr");
   GPT2_HIP((launch_transpose<T, T>(u, M, F, ta, Mp, st)), "bwd u^T");
   GPT2_HIP((launch_transpose<T, T>(dyt, M, D, tb, Mp, st)), "bwd dy^T");
   GPT2_HIP(wgrad(ta, tb, F, D, grads + G_prw), "bwd dW_pr");
-  GPT2_HIP(launch_colsum<T>(dg, M, F, grads + G_fcb, part, st), "bwd db_fc");
+  GPT2_HIP(launch_colsum_partial<T>(dg, M, F, colsum_slot(F, grads + G_fcb), st), "bwd db_fc");
   GPT2_HIP((launch_transpose<T, T>(h2, M, D, ta, Mp, st)), "bwd h2^T");
   GPT2_HIP((launch_transpose<T, T>(dg, M, F, tb, Mp, st)), "bwd dg^T");
   GPT2_HIP(wgrad(ta, tb, D, F, grads + G_fcw), "bwd dW_fc");
   GPT2_HIP(gemm_f32(dg, wt_fc, M, D, F, dh, D), "bwd dh2");
   GPT2_HIP(launch_layernorm_backward<T>(xh, dh, pf(m, o.ln2_g), dy, dxh, dxht, mu, rstd, M, D, c.ln_eps, st),
            "bwd ln_2 backward");
-  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln2w, part, st, xh, mu, rstd), "bwd dgamma_2");
-  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln2b, part, st), "bwd dbeta_2");
+  {
+    float* pw = colsum_slot(D, grads + G_ln2w);
+    float* pb = colsum_slot(D, grads + G_ln2b);
+    GPT2_HIP(launch_colsum_partial<float>(dh, M, D, pw, st, xh, mu, rstd, pb), "bwd dgamma_2, dbeta_2");
+  }
 
   // attention
-  GPT2_HIP(launch_colsum<float>(dxh, M, D, grads + G_ob, part, st), "bwd db_o");
+  GPT2_HIP(launch_colsum_partial<float>(dxh, M, D, colsum_slot(D, grads + G_ob), st), "bwd db_o");
   GPT2_HIP((launch_transpose<T, T>(a, M, D, ta, Mp, st)), "bwd a^T");
   GPT2_HIP((launch_transpose<T, T>(dxht, M, D, tb, Mp, st)), "bwd dx_h^T");
   GPT2_HIP(wgrad(ta, tb, D, D, grads + G_ow), "bwd dW_o");
   GPT2_HIP(launch_gemm<T>(pick_tile(M, D, D), dxht, wt_o, M, D, D, D, D, EpiStore<T>{da, D}, st), "bwd da");
   GPT2_HIP(launch_attention_backward<T>(q, kk, vt, a, da, lse, dvec, dqkv, B, H, T_seq, Tp, hs, q_scale, st),
            "bwd attention backward");
-  GPT2_HIP(launch_colsum<float>(dqkv, M, 3 * D, grads + G_qkvb, part, st), "bwd db_qkv");
+  GPT2_HIP(launch_colsum_partial<float>(dqkv, M, 3 * D, colsum_slot(3 * D, grads + G_qkvb), st), "bwd db_qkv");
   GPT2_HIP(launch_convert<T>(dqkv, dqkvt, (size_t)M * 3 * D, (size_t)M * 3 * D, st), "bwd dqkv");
   GPT2_HIP((launch_transpose<T, T>(h1, M, D, ta, Mp, st)), "bwd h1^T");
   GPT2_HIP((launch_transpose<T, T>(dqkvt, M, 3 * D, tb, Mp, st)), "bwd dqkv^T");
@@ -722,8 +738,12 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   GPT2_HIP(launch_layernorm_backward<T>(x, dh, pf(m, o.ln1_g), dxh, dx, static_cast<T*>(nullptr), mu, rstd, M, D,
                                         c.ln_eps, st),
            "bwd ln_1 backward");
-  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln1w, part, st, x, mu, rstd), "bwd dgamma_1");
-  GPT2_HIP(launch_colsum<float>(dh, M, D, grads + G_ln1b, part, st), "bwd dbeta_1");
+  {
+    float* pw = colsum_slot(D, grads + G_ln1w);
+    float* pb = colsum_slot(D, grads + G_ln1b);
+    GPT2_HIP(launch_colsum_partial<float>(dh, M, D, pw, st, x, mu, rstd, pb), "bwd dgamma_1, dbeta_1");
+  }
+  GPT2_HIP(launch_colsum_final(cjobs, n_cjobs, st), "bwd column sums");
   return GPT2_OK;
 }
 
