@@ -170,15 +170,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    if w.decode:
-        return bench_decode(args, w)
-
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if w.decode:
+        return bench_decode(args, w)
 
     B, T = w.batch, w.seq_len
     logits_dtype = args.logits_dtype or w.dtype
@@ -356,6 +356,8 @@ def bench_decode(args, w):
     prefix, new = W.make_decode_ids(w)
     kv = model.new_kv_cache(B, P + 1)
     model.forward(torch.from_numpy(prefix).to(dev), logits=False, kv=kv)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill of {P} tokens done", file=sys.stderr, flush=True)
     new_d = torch.from_numpy(new).to(dev)
     logits = torch.empty((B, w.shape.vocab), dtype=model.logits_torch_dtype, device=dev)
 
@@ -371,6 +373,7 @@ def bench_decode(args, w):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    print(f"[bench] {args.steps} decode steps done", file=sys.stderr, flush=True)
     # greedy generation (gpt2_generate): the first 960 tokens as the prompt,
     # 64 steps chained on the device (positions 959 .. 1022), no logits stored
     gen_prompt, gen_steps = min(960, P), min(64, P + 1 - min(960, P))
@@ -380,6 +383,8 @@ def bench_decode(args, w):
     def gen():
         kv.view.past_len = gen_prompt - 1
         model.generate(kv, gen_first, gen_steps, out=gen_out)
+        torch.cuda.synchronize()
+        print(f"[bench] generation of {gen_steps} steps done", file=sys.stderr, flush=True)
 
     gen()
     torch.cuda.synchronize()
