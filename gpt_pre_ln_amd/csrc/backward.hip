@@ -476,11 +476,30 @@ __device__ __forceinline__ u32x4_t frag(const MmaTile& t, int row, int k8) {
 // Row-major copy ([row][d], 16-byte chunks) and, optionally, the transposed
 // copy ([d][row]) of 64 rows of 64 bf16 from global rows src + r * ld, rows
 // past `valid` zero.
-__device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf16_t* src, size_t ld, int valid) {
-  for (int c = threadIdx.x; c < kBT * 8; c += 256) {
-    const int r = c >> 3, d8 = (c & 7) * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (r < valid) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * ld + d8);
+// A 64 x 64 bf16 tile held in registers between its global read and its LDS
+// write: 256 threads, two 16-byte chunks each (chunk c = threadIdx.x + 256 j:
+// row c / 8, elements 8 (c % 8) .. +7), so the next tile's reads can be in
+// flight while the current tile is computed.
+struct TileRegs {
+  u32x4_t v[2];
+};
+static_assert(kBT * 8 == 2 * 256, "two 16-byte chunks per thread");
+
+__device__ __forceinline__ void fetch_rows_bf16(TileRegs& g, const bf16_t* src, size_t ld, int valid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + j * 256, r = c >> 3, d8 = (c & 7) * 8;
+    g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (r < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * ld + d8);
+  }
+}
+
+// Rows as [row][d] into t and, when tt is given, transposed as [d][row].
+__device__ __forceinline__ void put_rows_bf16(MmaTile& t, MmaTile* tt, const TileRegs& g) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + j * 256, r = c >> 3, d8 = (c & 7) * 8;
+    const u32x4_t v = g.v[j];
     *reinterpret_cast<u32x4_t*>(&t.a[r][d8]) = v;
     if (tt) {
 #pragma unroll
@@ -492,12 +511,30 @@ __device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf
   }
 }
 
-// V^T rows (global [d][kvT], keys contiguous) into V as [key][d].
-__device__ __forceinline__ void load_vt_bf16(MmaTile& t, const bf16_t* vt, int kvT, int j0, int valid) {
-  for (int c = threadIdx.x; c < kBT * 8; c += 256) {
-    const int d = c >> 3, k8 = (c & 7) * 8;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (k8 < valid) v = *reinterpret_cast<const u32x4_t*>(vt + (size_t)d * kvT + j0 + k8);
+// Rows r < valid of a [rows][ld] bf16 matrix into t (and transposed into tt),
+// rows past `valid` zero.
+__device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf16_t* src, size_t ld, int valid) {
+  TileRegs g;
+  fetch_rows_bf16(g, src, ld, valid);
+  put_rows_bf16(t, tt, g);
+}
+
+// V^T rows (global [d][kvT], keys contiguous) into V as [key][d]; keys past
+// `valid` zero.
+__device__ __forceinline__ void fetch_vt_bf16(TileRegs& g, const bf16_t* vt, int kvT, int j0, int valid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + j * 256, d = c >> 3, k8 = (c & 7) * 8;
+    g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (k8 < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(vt + (size_t)d * kvT + j0 + k8);
+  }
+}
+
+__device__ __forceinline__ void put_vt_bf16(MmaTile& t, const TileRegs& g, int valid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = threadIdx.x + j * 256, d = c >> 3, k8 = (c & 7) * 8;
+    const u32x4_t v = g.v[j];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool lo = k8 + 2 * e < valid, hi = k8 + 2 * e + 1 < valid;
@@ -505,6 +542,12 @@ __device__ __forceinline__ void load_vt_bf16(MmaTile& t, const bf16_t* vt, int k
       t.a[k8 + 2 * e + 1][d].bits = hi ? (uint16_t)(v[e] >> 16) : (uint16_t)0;
     }
   }
+}
+
+__device__ __forceinline__ void load_vt_bf16(MmaTile& t, const bf16_t* vt, int kvT, int j0, int valid) {
+  TileRegs g;
+  fetch_vt_bf16(g, vt, kvT, j0, valid);
+  put_vt_bf16(t, g, valid);
 }
 
 // S and dP of one 16-row block (rows `r16` of X-side tiles Qs / dOs) against
@@ -561,16 +604,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mma_kernel(const bf16_t* __
   f32x4_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // The next query tile's Q, dO, lse and dvec are read into registers while
+  // the current one is computed.
+  TileRegs gq, gdo;
+  float glse = 0.f, gdv = 0.f;
+  auto fetch_qtile = [&](int qt) {
+    const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
+    fetch_rows_bf16(gq, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
+    fetch_rows_bf16(gdo, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
+    if (threadIdx.x < kBT) {
+      const int i = threadIdx.x;
+      glse = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
+      gdv = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+    }
+  };
+  fetch_qtile(kt);
   for (int qt = kt; qt < n_tiles; ++qt) {
     const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
     __syncthreads();
-    load_rows_bf16(sm.Q, &sm.Qt, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
-    load_rows_bf16(sm.dO, &sm.dOt, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
+    put_rows_bf16(sm.Q, &sm.Qt, gq);
+    put_rows_bf16(sm.dO, &sm.dOt, gdo);
     if (threadIdx.x < kBT) {
-      const int i = threadIdx.x;
-      sm.lse[i] = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
-      sm.dv[i] = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+      sm.lse[threadIdx.x] = glse;
+      sm.dv[threadIdx.x] = gdv;
     }
+    if (qt + 1 < n_tiles) fetch_qtile(qt + 1);
     __syncthreads();
     // R[q][key] for the 4 query blocks (x varies) against this wave's keys
     f32x4_t s[4], dp[4];
@@ -660,11 +718,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mma_kernel(const bf16_t* __re
   f32x4_t dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // The next key tile's K and V^T are read into registers while the current
+  // one is computed.
+  TileRegs gk, gv;
+  auto fetch_ktile = [&](int kt) {
+    const int j0 = kt * kBT, nk = min(kBT, T_seq - j0);
+    fetch_rows_bf16(gk, k + ((size_t)bh * kvT + j0) * 64, 64, nk);
+    fetch_vt_bf16(gv, vt + (size_t)bh * 64 * kvT, kvT, j0, nk);
+  };
+  fetch_ktile(0);
   for (int kt = 0; kt <= qt; ++kt) {
     const int j0 = kt * kBT, nk = min(kBT, T_seq - j0);
     __syncthreads();
-    load_rows_bf16(sm.K, &sm.Kt, k + ((size_t)bh * kvT + j0) * 64, 64, nk);
-    load_vt_bf16(sm.V, vt + (size_t)bh * 64 * kvT, kvT, j0, nk);
+    put_rows_bf16(sm.K, &sm.Kt, gk);
+    put_vt_bf16(sm.V, gv, nk);
+    if (kt + 1 <= qt) fetch_ktile(kt + 1);
     __syncthreads();
     // R[q][key] for this wave's queries (y varies over the 4 key blocks)
     f32x4_t s[4], dp[4];
