@@ -477,36 +477,35 @@ __device__ __forceinline__ u32x4_t frag(const MmaTile& t, int row, int k8) {
 // copy ([d][row]) of 64 rows of 64 bf16 from global rows src + r * ld, rows
 // past `valid` zero.
 // A 64 x 64 bf16 tile held in registers between its global read and its LDS
-// write: 256 threads, two 16-byte chunks each (chunk c = threadIdx.x + 256 j:
-// row c / 8, elements 8 (c % 8) .. +7), so the next tile's reads can be in
-// flight while the current tile is computed.
+// write, so the next tile's reads can be in flight while the current tile is
+// computed.  256 threads, two 16-byte chunks each: thread t holds elements
+// 8 (t % 8) .. +7 of rows 2 (t / 8) and 2 (t / 8) + 1, so that the transposed
+// copy takes one 4-byte LDS write per element pair of the two rows.
 struct TileRegs {
   u32x4_t v[2];
 };
 static_assert(kBT * 8 == 2 * 256, "two 16-byte chunks per thread");
 
 __device__ __forceinline__ void fetch_rows_bf16(TileRegs& g, const bf16_t* src, size_t ld, int valid) {
+  const int r0 = 2 * (threadIdx.x >> 3), d8 = (threadIdx.x & 7) * 8;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + j * 256, r = c >> 3, d8 = (c & 7) * 8;
     g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (r < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * ld + d8);
+    if (r0 + j < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(r0 + j) * ld + d8);
   }
 }
 
 // Rows as [row][d] into t and, when tt is given, transposed as [d][row].
 __device__ __forceinline__ void put_rows_bf16(MmaTile& t, MmaTile* tt, const TileRegs& g) {
+  const int r0 = 2 * (threadIdx.x >> 3), d8 = (threadIdx.x & 7) * 8;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + j * 256, r = c >> 3, d8 = (c & 7) * 8;
-    const u32x4_t v = g.v[j];
-    *reinterpret_cast<u32x4_t*>(&t.a[r][d8]) = v;
-    if (tt) {
+  for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&t.a[r0 + j][d8]) = g.v[j];
+  if (tt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tt->a[d8 + 2 * e][r].bits = (uint16_t)(v[e] & 0xFFFF);
-        tt->a[d8 + 2 * e + 1][r].bits = (uint16_t)(v[e] >> 16);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t a = g.v[0][e], b = g.v[1][e];  // rows r0, r0 + 1; elements d8 + 2e, d8 + 2e + 1
+      *reinterpret_cast<uint32_t*>(&tt->a[d8 + 2 * e][r0]) = (a & 0xFFFFu) | (b << 16);
+      *reinterpret_cast<uint32_t*>(&tt->a[d8 + 2 * e + 1][r0]) = (a >> 16) | (b & 0xFFFF0000u);
     }
   }
 }
@@ -520,27 +519,25 @@ __device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf
 }
 
 // V^T rows (global [d][kvT], keys contiguous) into V as [key][d]; keys past
-// `valid` zero.
+// `valid` zero.  Thread t holds keys k8 .. k8+7 (k8 = 8 (t % 8)) of rows
+// d = 2 (t / 8) and d + 1, so each key's two values leave as one 4-byte write.
 __device__ __forceinline__ void fetch_vt_bf16(TileRegs& g, const bf16_t* vt, int kvT, int j0, int valid) {
+  const int d0 = 2 * (threadIdx.x >> 3), k8 = (threadIdx.x & 7) * 8;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + j * 256, d = c >> 3, k8 = (c & 7) * 8;
     g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (k8 < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(vt + (size_t)d * kvT + j0 + k8);
+    if (k8 < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(vt + (size_t)(d0 + j) * kvT + j0 + k8);
   }
 }
 
 __device__ __forceinline__ void put_vt_bf16(MmaTile& t, const TileRegs& g, int valid) {
+  const int d0 = 2 * (threadIdx.x >> 3), k8 = (threadIdx.x & 7) * 8;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = threadIdx.x + j * 256, d = c >> 3, k8 = (c & 7) * 8;
-    const u32x4_t v = g.v[j];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool lo = k8 + 2 * e < valid, hi = k8 + 2 * e + 1 < valid;
-      t.a[k8 + 2 * e][d].bits = lo ? (uint16_t)(v[e] & 0xFFFF) : (uint16_t)0;
-      t.a[k8 + 2 * e + 1][d].bits = hi ? (uint16_t)(v[e] >> 16) : (uint16_t)0;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t a = g.v[0][e], b = g.v[1][e];  // rows d0, d0 + 1; keys k8 + 2e, k8 + 2e + 1
+    const bool lo = k8 + 2 * e < valid, hi = k8 + 2 * e + 1 < valid;
+    *reinterpret_cast<uint32_t*>(&t.a[k8 + 2 * e][d0]) = lo ? (a & 0xFFFFu) | (b << 16) : 0u;
+    *reinterpret_cast<uint32_t*>(&t.a[k8 + 2 * e + 1][d0]) = hi ? (a >> 16) | (b & 0xFFFF0000u) : 0u;
   }
 }
 
