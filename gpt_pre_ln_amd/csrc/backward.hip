@@ -262,6 +262,32 @@ __global__ __launch_bounds__(256) void attn_bwd_dvec_kernel(const T* __restrict_
   if (lane == 0) dvec[r] = s;
 }
 
+// bf16 rows of 64: eight lanes per row, 16 bytes each (eight products added
+// in order, then the eight lane sums by xor shuffles), 32 rows per block.
+__global__ __launch_bounds__(256) void attn_bwd_dvec_bf16_kernel(const bf16_t* __restrict__ o,
+                                                                 const bf16_t* __restrict__ dout,
+                                                                 float* __restrict__ dvec, int B, int H, int T_seq) {
+  const int r = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  const bool on = r < B * H * T_seq;
+  const int rr = on ? r : 0;
+  const int bh = rr / T_seq, i = rr - bh * T_seq;
+  const int b = bh / H, h = bh - b * H;
+  const size_t off = ((size_t)b * T_seq + i) * (H * 64) + h * 64 + sub * 8;
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(dout + off);
+  const u32x4_t c = *reinterpret_cast<const u32x4_t*>(o + off);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s += __uint_as_float(a[e] << 16) * __uint_as_float(c[e] << 16);
+    s += __uint_as_float(a[e] & 0xFFFF0000u) * __uint_as_float(c[e] & 0xFFFF0000u);
+  }
+  s += __shfl_xor(s, 1, 8);
+  s += __shfl_xor(s, 2, 8);
+  s += __shfl_xor(s, 4, 8);
+  if (on && sub == 0) dvec[r] = s;
+}
+
 constexpr int kBT = 64;  // keys per key tile, queries per query tile
 
 // Shared pieces of the two attention-backward kernels: 256 threads,
@@ -908,7 +934,7 @@ hipError_t launch_attention_backward(const T* q, const T* k, const T* vt, const 
   const dim3 grid(B * H * n_tiles), block(256);
   if constexpr (sizeof(T) == 2) {
     if (hs == 64) {
-      hipLaunchKernelGGL((attn_bwd_dvec_kernel<T, 64>), dim3((rows + 3) / 4), block, 0, stream, o, dout, dvec, B, H,
+      hipLaunchKernelGGL(attn_bwd_dvec_bf16_kernel, dim3((rows + 31) / 32), block, 0, stream, o, dout, dvec, B, H,
                          T_seq);
       hipLaunchKernelGGL(attn_bwd_dkdv_mma_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
                          T_seq, kvT, n_tiles);
