@@ -113,9 +113,33 @@ def measured_traffic(workload, cls):
     return round(entry["read_bytes"] + entry["write_bytes"])
 
 
-def cpu_baseline(w, budget_s=12.0):
+def host_cpu():
+    """(logical CPUs this process may run on, CPU model name) of the host."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(w, budget_s=12.0, gpu_argmax=None):
     """The fp64 oracle, as it stands, on the first sequences of the same batch
-    until about `budget_s` seconds of host work have been spent."""
+    until about `budget_s` seconds of host work have been spent.
+
+    gpu_argmax: {label: int array [B, T]} of the GPU's arg-max token per
+    position; for the sequences the oracle computed, the exact agreement with
+    the oracle's arg-max (first index on ties, both sides) and the admissible
+    agreement (the GPU's token has an oracle logit within 2e-2 * max|logit| of
+    the oracle's best) are returned beside the timing."""
     import numpy as np
     import oracle
     import workloads as W
@@ -124,21 +148,75 @@ def cpu_baseline(w, budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    nproc, model = host_cpu()
     blob = W.make_params(w)
     ids = W.make_ids(w)
     P = oracle.prepare_params(blob, w.shape, w.dtype)
     del blob
-    t0 = time.perf_counter()
+    agree = {k: [0, 0, 0] for k in (gpu_argmax or {})}   # exact, admissible, rows
+    elapsed = 0.0
     n = 0
     while n < w.batch:
-        oracle.forward(P, ids[n:n + 1])
+        t0 = time.perf_counter()
+        ref = oracle.forward(P, ids[n:n + 1])[0]
+        elapsed += time.perf_counter() - t0
+        if gpu_argmax:
+            best = ref.argmax(-1)
+            tol = 2e-2 * np.abs(ref).max()
+            top = ref[np.arange(ref.shape[0]), best]
+            for k, g in gpu_argmax.items():
+                gi = np.asarray(g[n], dtype=np.int64)
+                agree[k][0] += int((gi == best).sum())
+                agree[k][1] += int((top - ref[np.arange(ref.shape[0]), gi] <= tol).sum())
+                agree[k][2] += ref.shape[0]
+        del ref
         n += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if elapsed >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": n * w.seq_len / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {w.batch} sequences x {w.seq_len} tokens, full logits, fp64 numpy "
-                      f"oracle ({dt:.1f} s)"}
+    out = {"value": n * w.seq_len / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {n} of {w.batch} sequences x {w.seq_len} tokens, full logits, fp64 numpy "
+                     f"oracle ({elapsed:.1f} s)",
+           "threads_note": "cores = BLAS threads the oracle's matrix products used",
+           "nproc": nproc, "cpu_model": model}
+    argmax = {k: {"exact": round(a[0] / a[2], 5), "admissible": round(a[1] / a[2], 5), "rows": a[2],
+                  "sequences": n} for k, a in agree.items() if a[2]}
+    return out, argmax
+
+
+def time_steps(fn, steps, warmup):
+    """Seconds per call of fn over `steps` calls after `warmup` untimed ones,
+    bracketed by device synchronisations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def forward_leg(W, w, steps, warmup, logits_dtype="bf16"):
+    """One more forward workload (the GPT-2 medium and XL shapes): ms per
+    forward with logits in the padded layout, and the fraction of peak."""
+    import torch
+    from gpt_pre_ln_amd.model import GPT2
+    dev = torch.device("cuda:0")
+    B, T = w.batch, w.seq_len
+    model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
+    model.load_blob(W.make_params(w))
+    ids = torch.from_numpy(W.make_ids(w)).to(dev)
+    logits = torch.empty((B, T, model.logits_padded_ld), dtype=model.logits_torch_dtype, device=dev)
+    el = time_steps(lambda: model.forward(ids, out_logits=logits, padded_logits=True), steps, warmup)
+    flops = forward_flops(w.shape, B, T)
+    del model, logits
+    torch.cuda.empty_cache()
+    print(f"[bench] {w.name} forward done", file=sys.stderr, flush=True)
+    return {"workload": w.name, "batch": B, "seq_len": T, "logits_dtype": logits_dtype,
+            "ms_per_step": round(el * 1e3, 4), "tokens_per_s": round(B * T / el, 1),
+            "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+            "frac_of_peak": round(flops / el / (PEAK_BF16_TFLOPS * 1e12), 4)}
 
 
 def main():
@@ -148,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-small-b8t1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline only: skip the loss, variant, backward, fp32-logits, decode, medium and XL legs")
     ap.add_argument("--logits-dtype", choices=["f32", "bf16"], default=None,
                     help="element type of the logits (default: the workload's arithmetic dtype)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -178,7 +258,8 @@ def main():
         del src, dst
 
     if w.decode:
-        return bench_decode(args, w)
+        print(json.dumps(bench_decode(args, w)), flush=True)
+        return
 
     B, T = w.batch, w.seq_len
     logits_dtype = args.logits_dtype or w.dtype
@@ -186,6 +267,7 @@ def main():
     model = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
     model.load_blob(blob)
     ids = torch.from_numpy(W.make_ids(w)).to(dev)
+    V = w.shape.vocab
     # logits in the padded layout (rows of logits_padded_ld elements; the
     # caller sees the [B, T, vocab] view): the fast layout of gpt2_forward_strided
     ld = model.logits_padded_ld
@@ -198,7 +280,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # which kernel class dominates: one timed step per class (outside the timed region)
+    # which kernel class dominates: one step per class with HIP events around
+    # each launch of that class (outside the timed region)
     per_class = {}
     for cls in CLASSES:
         binding.gpt2_timing_enable(model.handle, cls, True)
@@ -238,79 +321,9 @@ def main():
     roof["avg_launch_ms"] = round(dom_ms / max(dom_n, 1), 5)
     roof["launches_timed"] = dom_n
 
-    # forward + shifted next-token cross-entropy, logits never stored
-    # (gpt2_forward_loss; reported beside the headline value)
-    loss_mean = torch.empty(1, dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        model.loss(ids, out_mean=loss_mean)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        model.loss(ids, out_mean=loss_mean)
-    torch.cuda.synchronize()
-    el_loss = (time.perf_counter() - t2) / args.steps
-    loss_step = {"value": round(B * T / el_loss, 1), "unit": "tokens/s", "ms_per_step": round(el_loss * 1e3, 4),
-                 "mean_loss": round(float(loss_mean.item()), 5)}
-
-    # the same workload with every variant switch on (Post-LN wiring, per-layer
-    # score scaling, erf GELU, separate head): its own weights, same ids
-    import dataclasses
-    vshape = dataclasses.replace(w.shape, post_ln=True, scale_attn_by_inverse_layer_idx=True, activation="gelu",
-                                 tie_word_embeddings=False)
-    vmodel = GPT2.from_shape(vshape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
-    vmodel.load_blob(W.make_params(vshape, w.init, w.param_seed))
-    for _ in range(args.warmup):
-        vmodel.forward(ids, out_logits=logits, padded_logits=True)
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    for _ in range(args.steps):
-        vmodel.forward(ids, out_logits=logits, padded_logits=True)
-    torch.cuda.synchronize()
-    el_v = (time.perf_counter() - t3) / args.steps
-    variant_step = {"switches": ["post_ln", "scale_attn_by_inverse_layer_idx", "gelu_erf", "separate_head"],
-                    "value": round(B * T / el_v, 1), "unit": "tokens/s", "ms_per_step": round(el_v * 1e3, 4)}
-    del vmodel
-
-    # backward of one block (gpt2_block_backward, layer 0) on the same batch:
-    # seeded fp32 block input and output gradient
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(7)
-    xb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
-    dyb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
-    dxb, gb = model.block_backward(0, xb, dyb)
-    for _ in range(max(1, args.warmup // 2)):
-        model.block_backward(0, xb, dyb, out_dx=dxb, out_grads=gb)
-    torch.cuda.synchronize()
-    nb = max(2, args.steps // 4)
-    t4 = time.perf_counter()
-    for _ in range(nb):
-        model.block_backward(0, xb, dyb, out_dx=dxb, out_grads=gb)
-    torch.cuda.synchronize()
-    el_b = (time.perf_counter() - t4) / nb
-    bflop = backward_block_flops(w.shape, B, T)
-    block_backward = {"layer": 0, "ms_per_call": round(el_b * 1e3, 4), "algorithmic_tflop": round(bflop / 1e12, 4),
-                      "achieved_tflops": round(bflop / el_b / 1e12, 2),
-                      "note": "includes the recomputed forward of the block"}
-    del xb, dyb, dxb, gb
-    model._bwd_ws = None
-
-    # the same forward storing fp32 logits (reported beside the headline value)
-    alt = None
-    if logits_dtype != "f32":
-        del logits
-        model32 = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype="f32")
-        model32.load_blob(blob)
-        logits32 = torch.empty((B, T, ld), dtype=torch.float32, device=dev)
-        for _ in range(args.warmup):
-            model32.forward(ids, out_logits=logits32, padded_logits=True)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            model32.forward(ids, out_logits=logits32, padded_logits=True)
-        torch.cuda.synchronize()
-        el32 = (time.perf_counter() - t1) / args.steps
-        alt = {"value": round(B * T / el32, 1), "ms_per_step": round(el32 * 1e3, 4)}
-        del model32, logits32
+    # the GPU's arg-max token per position (outside the timed region), for the
+    # agreement with the oracle computed in the CPU-baseline leg
+    gpu_argmax = {logits_dtype: logits[..., :V].argmax(-1).cpu().numpy()}
 
     out = {
         "metric": "forward tokens/s and % bf16 MFMA peak, GPT-2 small B=8 T=1024, 1 GPU",
@@ -326,24 +339,94 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": T, "d_model": w.shape.d_model,
-                   "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": w.shape.vocab,
+                   "n_layer": w.shape.n_layer, "n_head": w.shape.n_head, "vocab": V,
                    "logits_dtype": logits_dtype, "logits_row_stride": ld},
         "frac_of_peak": round(flops / (elapsed / args.steps) / (peak * 1e12), 4),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
         "roofline": roof,
         "per_class_ms": {c: round(v["ms_per_step"], 4) for c, v in per_class.items()},
+        "per_class_note": (f"each class timed in a step of its own, with HIP events around each of its launches: "
+                           f"the events keep the launches apart, so the classes sum to "
+                           f"{sum(v['ms_per_step'] for v in per_class.values()):.3f} ms against "
+                           f"{ms_per_step:.3f} ms per step (not additive)"),
     }
-    out["loss_step"] = loss_step
-    out["variant_step"] = variant_step
-    out["block_backward"] = block_backward
-    if alt is not None:
-        out["fp32_logits"] = alt
+
+    if not args.no_extra:
+        # forward + shifted next-token cross-entropy, logits never stored (gpt2_forward_loss)
+        loss_mean = torch.empty(1, dtype=torch.float32, device=dev)
+        el_loss = time_steps(lambda: model.loss(ids, out_mean=loss_mean), args.steps, args.warmup)
+        out["loss_step"] = {"value": round(B * T / el_loss, 1), "unit": "tokens/s",
+                            "ms_per_step": round(el_loss * 1e3, 4), "mean_loss": round(float(loss_mean.item()), 5)}
+
+        # the same workload with every variant switch on (Post-LN wiring, per-layer
+        # score scaling, erf GELU, separate head): its own weights, same ids
+        import dataclasses
+        vshape = dataclasses.replace(w.shape, post_ln=True, scale_attn_by_inverse_layer_idx=True, activation="gelu",
+                                     tie_word_embeddings=False)
+        vmodel = GPT2.from_shape(vshape, w.dtype, max_batch=B, max_seq=T, logits_dtype=logits_dtype)
+        vmodel.load_blob(W.make_params(vshape, w.init, w.param_seed))
+        el_v = time_steps(lambda: vmodel.forward(ids, out_logits=logits, padded_logits=True), args.steps,
+                          args.warmup)
+        out["variant_step"] = {"switches": ["post_ln", "scale_attn_by_inverse_layer_idx", "gelu_erf",
+                                            "separate_head"],
+                               "value": round(B * T / el_v, 1), "unit": "tokens/s", "ms_per_step": round(el_v * 1e3, 4)}
+        del vmodel
+
+        # backward of one block (gpt2_block_backward, layer 0) on the same batch:
+        # seeded fp32 block input and output gradient
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        xb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
+        dyb = torch.randn((B, T, w.shape.d_model), generator=gen, device=dev, dtype=torch.float32)
+        dxb, gb = model.block_backward(0, xb, dyb)
+        el_b = time_steps(lambda: model.block_backward(0, xb, dyb, out_dx=dxb, out_grads=gb),
+                          max(2, args.steps // 4), max(1, args.warmup // 2))
+        bflop = backward_block_flops(w.shape, B, T)
+        out["block_backward"] = {"layer": 0, "ms_per_call": round(el_b * 1e3, 4),
+                                 "algorithmic_tflop": round(bflop / 1e12, 4),
+                                 "achieved_tflops": round(bflop / el_b / 1e12, 2),
+                                 "note": "includes the recomputed forward of the block"}
+        del xb, dyb, dxb, gb
+        model._bwd_ws = None
+
+        # the same forward storing fp32 logits: t_fwd of the measurement
+        # definition (device ids -> device fp32 logits), beside the headline value
+        if logits_dtype != "f32":
+            del logits
+            model32 = GPT2.from_shape(w.shape, w.dtype, max_batch=B, max_seq=T, logits_dtype="f32")
+            model32.load_blob(blob)
+            logits32 = torch.empty((B, T, ld), dtype=torch.float32, device=dev)
+            el32 = time_steps(lambda: model32.forward(ids, out_logits=logits32, padded_logits=True), args.steps,
+                              args.warmup)
+            gpu_argmax["f32"] = logits32[..., :V].argmax(-1).cpu().numpy()
+            out["fp32_logits"] = {"value": round(B * T / el32, 1), "unit": "tokens/s",
+                                  "ms_per_step": round(el32 * 1e3, 4),
+                                  "frac_of_peak": round(flops / el32 / (peak * 1e12), 4),
+                                  "note": "t_fwd from device token ids to device fp32 logits"}
+            del model32, logits32
+        del model
+        torch.cuda.empty_cache()
+        print("[bench] GPT-2 small legs done", file=sys.stderr, flush=True)
+
+        # the other workloads: the decode step, GPT-2 medium and XL forwards
+        dw = W.WORKLOADS["gpt2-small-decode-b32p1023"]
+        d = bench_decode(args, dw, generation=False)
+        out["decode_step"] = {"workload": dw.name, "batch": d["config"]["batch"], "prefix": d["config"]["prefix"],
+                              "ms_per_step": d["ms_per_step"], "tokens_per_s": d["value"],
+                              "achieved_gbs": d["roofline"]["achieved"], "frac_of_hbm": d["roofline"]["frac"],
+                              "algorithmic_bytes": d["roofline"]["algorithmic_bytes"]}
+        fsteps, fwarm = max(3, args.steps // 2), max(1, args.warmup // 2)
+        out["medium"] = forward_leg(W, W.WORKLOADS["gpt2-medium-b8t1024"], fsteps, fwarm)
+        out["xl"] = forward_leg(W, W.WORKLOADS["gpt2-xl-b4t1024"], fsteps, fwarm)
+
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        cb, agree = cpu_baseline(w, gpu_argmax=gpu_argmax)
+        out["cpu_baseline"] = cb
+        out["argmax_agreement"] = agree
     print(json.dumps(out), flush=True)
 
 
-def bench_decode(args, w):
+def bench_decode(args, w, generation=True):
     import torch
     import workloads as W
     from gpt_pre_ln_amd.model import GPT2
@@ -374,8 +457,37 @@ def bench_decode(args, w):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     print(f"[bench] {args.steps} decode steps done", file=sys.stderr, flush=True)
-    # greedy generation (gpt2_generate): the first 960 tokens as the prompt,
-    # 64 steps chained on the device (positions 959 .. 1022), no logits stored
+    generate = None
+    if generation:
+        generate = bench_generation(args, model, kv, prefix, B, P)
+
+    s = w.shape
+    D, F, L, V = s.d_model, s.d_ff, s.n_layer, s.vocab
+    weights = 2 * (L * (3 * D * D + D * D + 2 * D * F) + V * D)
+    kv_bytes = 2 * L * 2 * B * (P + 1) * D
+    logit_bytes = (2 if logits_dtype == "bf16" else 4) * B * V
+    total = weights + kv_bytes + logit_bytes
+    gbs = total / dt / 1e9
+    out = {"metric": "decode tokens/s (GPT-2 small, B=32, cached prefix 1023)", "value": round(B / dt, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "batch": B, "prefix": P, "logits_dtype": logits_dtype},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "kernel": "whole decode step", "algorithmic_bytes": total}}
+    if generate is not None:
+        out["generate"] = generate
+    del model, kv, logits
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_generation(args, model, kv, prefix, B, P):
+    """Greedy generation (gpt2_generate): the first 960 tokens as the prompt,
+    64 steps chained on the device (positions 959 .. 1022), no logits stored."""
+    import torch
+    dev = torch.device("cuda:0")
     gen_prompt, gen_steps = min(960, P), min(64, P + 1 - min(960, P))
     gen_first = torch.from_numpy(np.ascontiguousarray(prefix[:, gen_prompt - 1])).to(dev)
     gen_out = torch.empty((B, gen_steps), dtype=torch.int32, device=dev)
@@ -394,25 +506,8 @@ def bench_decode(args, w):
         gen()
     torch.cuda.synchronize()
     gdt = (time.perf_counter() - t1) / reps
-    generate = {"value": round(B * gen_steps / gdt, 1), "unit": "tokens/s", "batch": B, "prompt": gen_prompt,
-                "steps": gen_steps, "ms_per_step": round(gdt * 1e3 / gen_steps, 4)}
-
-    s = w.shape
-    D, F, L, V = s.d_model, s.d_ff, s.n_layer, s.vocab
-    weights = 2 * (L * (3 * D * D + D * D + 2 * D * F) + V * D)
-    kv_bytes = 2 * L * 2 * B * (P + 1) * D
-    logit_bytes = (2 if logits_dtype == "bf16" else 4) * B * V
-    total = weights + kv_bytes + logit_bytes
-    gbs = total / dt / 1e9
-    out = {"metric": "decode tokens/s (GPT-2 small, B=32, cached prefix 1023)", "value": round(B / dt, 1),
-           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name, "batch": B, "prefix": P, "logits_dtype": logits_dtype},
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                        "kernel": "whole decode step", "algorithmic_bytes": total},
-           "generate": generate}
-    print(json.dumps(out), flush=True)
+    return {"value": round(B * gen_steps / gdt, 1), "unit": "tokens/s", "batch": B, "prompt": gen_prompt,
+            "steps": gen_steps, "ms_per_step": round(gdt * 1e3 / gen_steps, 4)}
 
 
 if __name__ == "__main__":

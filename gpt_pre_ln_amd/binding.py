@@ -45,6 +45,12 @@ class gpt2_kv_view(ctypes.Structure):
                 ("past_len", ctypes.c_int32)]
 
 
+class gpt2_param_info(ctypes.Structure):
+    _fields_ = [("blob_offset", ctypes.c_int64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("dev_dtype", ctypes.c_int32), ("transposed", ctypes.c_int32), ("dev_offset", ctypes.c_int64),
+                ("dev_ld", ctypes.c_int64), ("dev_rows", ctypes.c_int64)]
+
+
 class GPT2Error(RuntimeError):
     def __init__(self, status: int, where: str):
         lib = load()
@@ -60,6 +66,12 @@ _P = ctypes.c_void_p
 _SIG = {
     "gpt2_param_blob_floats": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.POINTER(ctypes.c_size_t)]),
     "gpt2_param_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt2_param_tensor_count": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.POINTER(ctypes.c_int32)]),
+    "gpt2_param_tensor": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32,
+                                         ctypes.POINTER(gpt2_param_info)]),
+    "gpt2_kv_stride": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    "gpt2_set_id_check": (ctypes.c_int, [_P, _P]),
+    "gpt2_source_hash": (ctypes.c_char_p, []),
     "gpt2_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_size_t)]),
     "gpt2_kv_cache_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32, ctypes.c_int32,
@@ -89,13 +101,25 @@ _SIG = {
 
 
 def load(path: str = LIB_PATH):
-    """Load libgpt2.so (raises if it is missing: build it with gpt_pre_ln_amd/build.py)."""
+    """Load libgpt2.so (raises if it is missing: build it with gpt_pre_ln_amd/build.py).
+
+    The library carries the digest of the sources it was built from; loading
+    refuses a binary whose digest differs from that of the sources beside it
+    (a stale build), unless GPT2_ALLOW_STALE_LIB=1."""
     global _lib
     if _lib is None:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: the HIP library must be built "
                                "(python gpt_pre_ln_amd/build.py); there is no fallback")
         lib = ctypes.CDLL(path)
+        lib.gpt2_source_hash.restype = ctypes.c_char_p
+        lib.gpt2_source_hash.argtypes = []
+        built = lib.gpt2_source_hash().decode()
+        from gpt_pre_ln_amd.build import source_hash
+        want = source_hash()
+        if built != want and os.environ.get("GPT2_ALLOW_STALE_LIB") != "1":
+            raise RuntimeError(f"{path} was built from sources {built}, but the sources here hash to {want}: "
+                               "rebuild it (python gpt_pre_ln_amd/build.py)")
         for name, (res, args) in _SIG.items():
             fn = getattr(lib, name)
             fn.restype = res
@@ -227,3 +251,30 @@ def gpt2_timing_read(handle):
     n = ctypes.c_int32()
     _check(load().gpt2_timing_read(handle, ctypes.byref(ms), ctypes.byref(n)), "gpt2_timing_read")
     return ms.value, n.value
+
+
+def gpt2_param_tensor_count(cfg) -> int:
+    n = ctypes.c_int32()
+    _check(load().gpt2_param_tensor_count(ctypes.byref(cfg), ctypes.byref(n)), "gpt2_param_tensor_count")
+    return n.value
+
+
+def gpt2_param_tensor(cfg, index: int) -> gpt2_param_info:
+    info = gpt2_param_info()
+    _check(load().gpt2_param_tensor(ctypes.byref(cfg), index, ctypes.byref(info)), "gpt2_param_tensor")
+    return info
+
+
+def gpt2_kv_stride(cfg, max_T: int) -> int:
+    n = ctypes.c_int32()
+    _check(load().gpt2_kv_stride(ctypes.byref(cfg), max_T, ctypes.byref(n)), "gpt2_kv_stride")
+    return n.value
+
+
+def gpt2_set_id_check(handle, d_flag):
+    _check(load().gpt2_set_id_check(handle, d_flag), "gpt2_set_id_check")
+
+
+def gpt2_source_hash() -> str:
+    return load().gpt2_source_hash().decode()
+

@@ -34,9 +34,31 @@ HIP_FLAGS = [
 SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
+def source_files() -> list[str]:
+    """Every file the library is built from (kernel sources, their headers, the
+    public header and this script), in a fixed order."""
+    names = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    return [os.path.join(CSRC, f) for f in names] + [os.path.join(HERE, "..", "include", "gpt2.h"),
+                                                      os.path.abspath(__file__)]
+
+
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the sources (each file's name and
+    bytes).  Compiled into the library (gpt2_source_hash) so that a loader can
+    tell whether a built libgpt2.so matches the sources beside it."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in source_files():
+        h.update(os.path.basename(p).encode() + b"\0")
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), f'-DGPT2_SOURCE_HASH="{digest}"', "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -45,8 +67,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
+    digest = source_hash()
     with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda f: _compile(f, digest), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,7 +77,7 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} (sources {digest})")
     return OUT
 
 

@@ -114,6 +114,48 @@ size_t blob_floats(const gpt2_config& c) {
   return V * D + P * D + per_layer * c.n_layer + 2 * D + (c.separate_head ? V * D : 0);
 }
 
+// Every tensor of the blob, in blob order, with the place and form of its
+// converted copy in the device region (the layout run_init writes).
+std::vector<gpt2_param_info> param_table(const gpt2_config& c) {
+  const ParamLayout L = param_layout(c);
+  const int32_t dt = c.dtype;
+  const int64_t V = c.vocab_size, P = c.n_positions, D = c.d_model, F = c.d_ff, Vp = vocab_pad(c);
+  std::vector<gpt2_param_info> t;
+  int64_t src = 0;
+  auto emb = [&](size_t off, int64_t rows, int64_t rows_pad) {  // [rows][D] kept as is, zero rows appended
+    t.push_back(gpt2_param_info{src, (int32_t)rows, (int32_t)D, dt, 0, (int64_t)off, D, rows_pad});
+    src += rows * D;
+  };
+  auto mat = [&](size_t off, int64_t K, int64_t N) {  // blob [K][N] -> device [N][K]
+    t.push_back(gpt2_param_info{src, (int32_t)K, (int32_t)N, dt, 1, (int64_t)off, K, N});
+    src += K * N;
+  };
+  auto vec = [&](size_t off, int64_t n) {
+    t.push_back(gpt2_param_info{src, 1, (int32_t)n, GPT2_F32, 0, (int64_t)off, n, 1});
+    src += n;
+  };
+  emb(L.wte, V, Vp);
+  emb(L.wpe, P, P);
+  for (const LayerOff& o : L.layers) {
+    vec(o.ln1_g, D);
+    vec(o.ln1_b, D);
+    mat(o.w_qkv, D, 3 * D);
+    vec(o.b_qkv, 3 * D);
+    mat(o.w_o, D, D);
+    vec(o.b_o, D);
+    vec(o.ln2_g, D);
+    vec(o.ln2_b, D);
+    mat(o.w_fc, D, F);
+    vec(o.b_fc, F);
+    mat(o.w_pr, F, D);
+    vec(o.b_pr, D);
+  }
+  vec(L.lnf_g, D);
+  vec(L.lnf_b, D);
+  if (c.separate_head) emb(L.head, V, Vp);
+  return t;
+}
+
 // Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
 // 256 CUs many times over (the lm_head); 128x128 (2 blocks per CU) or 64x128
 // (3 blocks per CU) otherwise.
@@ -214,6 +256,7 @@ struct gpt2_model {
   ParamLayout lay;
   float* trace = nullptr;
   size_t trace_floats = 0;
+  int32_t* id_flag = nullptr;  // set to 1 by the embedding when an id was outside [0, V)
   bool timing_on = false;
   int timing_class = -1;
   std::vector<hipEvent_t> ev;  // 2 per launch
@@ -331,7 +374,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
 
   {
     TimedScope ts(m, kEmbed, st);
-    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, st), "embed");
+    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, V, m->id_flag, st), "embed");
   }
   // Post-LN: the first block's attention reads the embeddings themselves (an
   // operand copy of x); later blocks read the output of the previous ln_2.
@@ -445,24 +488,25 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
   const int B = kv->B, M = B, pos = kv->past_len;
   const WsLayout W = ws_layout(c, B, 1);
-  float* x = reinterpret_cast<float*>(m->ws + W.x);
-  T* h = reinterpret_cast<T*>(m->ws + W.h);
-  T* q = reinterpret_cast<T*>(m->ws + W.q);
-  T* a = reinterpret_cast<T*>(m->ws + W.a);
-  T* u = reinterpret_cast<T*>(m->ws + W.u);
-  float* part = reinterpret_cast<float*>(m->ws + W.part);
+  char* const wsb = m->ws;
+  float* x = reinterpret_cast<float*>(wsb + W.x);
+  T* h = reinterpret_cast<T*>(wsb + W.h);
+  T* q = reinterpret_cast<T*>(wsb + W.q);
+  T* a = reinterpret_cast<T*>(wsb + W.a);
+  T* u = reinterpret_cast<T*>(wsb + W.u);
+  float* part = reinterpret_cast<float*>(wsb + W.part);
   // Up to 32 rows the residual projections (attn.c_proj, mlp.c_proj) write
   // split-K partial products and the LayerNorm that follows each adds them,
   // the bias and the residual stream, writes x back and normalises: no reduce
   // launch.  More rows take the tiled GEMM with the residual epilogue.
   const bool split = M <= 32;
-  float* rpart = reinterpret_cast<float*>(m->ws + W.rpart);
+  float* rpart = reinterpret_cast<float*>(wsb + W.rpart);
   const int ks_o = skinny_splits(D, sizeof(T)), ks_p = skinny_splits(F, sizeof(T));
   const float* pending_bias = nullptr;  // mlp.c_proj bias of the previous layer, when partials are pending
   const int kvT = kv_stride(kv->max_T);
   const float q_scale = 1.0f / std::sqrt((float)hs);
 
-  GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, st), "embed");
+  GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, V, m->id_flag, st), "embed");
   // Post-LN: each LayerNorm follows a residual add (ln_1 after attn.c_proj,
   // ln_2 after mlp.c_proj) and also writes the normalised row back to x; the
   // first block's attention reads an operand copy of the embeddings.
@@ -518,7 +562,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
            "ln_f");
   if (gen) {
     // lm_head with the arg-max epilogue (no logits stored), then one wave per row
-    int2* apart = reinterpret_cast<int2*>(m->ws + W.ce_part);
+    int2* apart = reinterpret_cast<int2*>(wsb + W.ce_part);
     EpiArgmax e{apart, W.ce_nseg, V};
     GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c), D), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st),
              "lm_head argmax");
@@ -810,6 +854,11 @@ const char* gpt2_status_string(gpt2_status s) {
 
 const char* gpt2_last_error(void) { return g_last_error.c_str(); }
 
+#ifndef GPT2_SOURCE_HASH
+#define GPT2_SOURCE_HASH "unknown"
+#endif
+const char* gpt2_source_hash(void) { return GPT2_SOURCE_HASH; }
+
 gpt2_status gpt2_param_blob_floats(const gpt2_config* cfg, size_t* n) {
   gpt2_status s = check_config(cfg);
   if (s) return s;
@@ -823,6 +872,33 @@ gpt2_status gpt2_param_bytes(const gpt2_config* cfg, size_t* bytes) {
   if (s) return s;
   if (!bytes) return GPT2_ERR_INVALID_ARG;
   *bytes = param_layout(*cfg).total;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_param_tensor_count(const gpt2_config* cfg, int32_t* n) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!n) return GPT2_ERR_INVALID_ARG;
+  *n = (int32_t)param_table(*cfg).size();
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_param_tensor(const gpt2_config* cfg, int32_t index, gpt2_param_info* info) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!info) return GPT2_ERR_INVALID_ARG;
+  const std::vector<gpt2_param_info> t = param_table(*cfg);
+  if (index < 0 || (size_t)index >= t.size()) return GPT2_ERR_SHAPE;
+  *info = t[index];
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_kv_stride(const gpt2_config* cfg, int32_t max_T, int32_t* stride) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!stride) return GPT2_ERR_INVALID_ARG;
+  if (max_T < 1 || max_T > cfg->n_positions) return GPT2_ERR_SHAPE;
+  *stride = kv_stride(max_T);
   return GPT2_OK;
 }
 
@@ -982,6 +1058,13 @@ gpt2_status gpt2_block_backward(gpt2_model* m, int32_t layer, int32_t B, int32_t
   char* w = static_cast<char*>(ws);
   return m->cfg.dtype == GPT2_BF16 ? run_block_backward<bf16_t>(m, layer, B, T, x, dy, dx, grads, w, st)
                                    : run_block_backward<float>(m, layer, B, T, x, dy, dx, grads, w, st);
+}
+
+gpt2_status gpt2_set_id_check(gpt2_model* m, int32_t* d_flag) {
+  if (!m) return GPT2_ERR_INVALID_ARG;
+  if (d_flag && !aligned(d_flag, 4)) return GPT2_ERR_INVALID_ARG;
+  m->id_flag = d_flag;
+  return GPT2_OK;
 }
 
 gpt2_status gpt2_set_trace(gpt2_model* m, float* d_trace, size_t n) {

@@ -6,11 +6,18 @@
 
 namespace gpt2 {
 
+// Token id used for the gather: ids outside [0, V) (V = vocab_size, the rows
+// of wte holding the vocabulary, pwwt.cn GPT2Config vocab_size) are clamped
+// to the nearest valid row, so a bad id can never address memory outside wte.
+__host__ __device__ inline int clamp_token_id(int id, int V) { return id < 0 ? 0 : (id >= V ? V - 1 : id); }
+
 // x[m, :] = wte[ids[m], :] + wpe[pos0 + m % T, :] (fp32 out).
 // pwwt.cn "逐行拆GPT-2源码", GPT2Model (wte + wpe, positions from past_length).
+// ids are clamped by clamp_token_id; when bad is non-null and some id was
+// outside [0, V), *bad receives 1 (it is never cleared here).
 template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq,
-                        int pos0, int D, hipStream_t stream);
+                        int pos0, int D, int V, int32_t* bad, hipStream_t stream);
 
 // y[m, :] = gamma * (x - mean) / sqrt(var + eps) + beta over D (biased
 // variance, two passes over the row held in registers); optional fp32 copy

@@ -11,14 +11,18 @@ namespace {
 
 constexpr int kMaxV4 = 8;  // float4 per lane -> D <= 2048
 
+// Ids outside [0, V) are clamped to the nearest row of wte, so the gather
+// never leaves the matrix; `bad` (optional) then receives 1.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ wte,
                                                      const T* __restrict__ wpe, float* __restrict__ x, int M,
-                                                     int T_seq, int pos0, int D) {
+                                                     int T_seq, int pos0, int D, int V, int32_t* __restrict__ bad) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
-  const int id = ids[row];
+  const int raw = ids[row];
+  const int id = clamp_token_id(raw, V);
+  if (bad && id != raw && lane == 0) *bad = 1;
   const int pos = pos0 + row % T_seq;
   const T* we = wte + (size_t)id * D;
   const T* pe = wpe + (size_t)pos * D;
@@ -328,8 +332,10 @@ hipError_t launch_ce_mean(const float* loss, const int32_t* labels, int B, int T
 
 template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq, int pos0, int D,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(embed_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D);
+                        int V, int32_t* bad, hipStream_t stream) {
+  if (V < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V,
+                     bad);
   return hipGetLastError();
 }
 
@@ -393,7 +399,8 @@ hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipS
 }
 
 #define GPT2_ROWOPS(T)                                                                                          \
-  template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, hipStream_t); \
+  template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, int, int32_t*,  \
+                                      hipStream_t);                                                                 \
   template hipError_t launch_layernorm<T>(float*, const float*, const float*, T*, float*, int, int, float,          \
                                           hipStream_t, const void*, size_t, const float*, int, const float*);       \
   template hipError_t launch_transpose_convert<T>(const float*, T*, int, int, int, hipStream_t);                   \

@@ -24,8 +24,11 @@
  *     any error nothing is launched and nothing is written.
  *   - One handle must not be used concurrently from two streams: the forward
  *     and decode calls share its workspace.
- *   - Token ids must lie in [0, vocab_size); this precondition is not checked
- *     on the device.
+ *   - Token ids must lie in [0, vocab_size).  The embedding clamps an id
+ *     outside that range to the nearest valid one (0 or vocab_size - 1), so a
+ *     bad id never makes the gather read outside wte, but the outputs of that
+ *     position are then those of the clamped id; gpt2_set_id_check gives a
+ *     device flag that reports it.
  */
 #ifndef GPT2_H
 #define GPT2_H
@@ -91,10 +94,13 @@ typedef struct {
 typedef struct gpt2_model gpt2_model;
 
 /* A key/value cache in caller-owned device memory (gpt2_kv_cache_bytes bytes).
- * Layout per layer l: K as [B][n_head][max_T][head_dim] and V transposed as
- * [B][n_head][head_dim][max_T], element type as the model dtype.  past_len
- * counts the cached positions; gpt2_forward with a view sets it to T and
- * gpt2_decode_step increments it. */
+ * With S = gpt2_kv_stride(cfg, max_T) = max_T rounded up to a multiple of 64,
+ * layer l occupies 2*B*S*d_model elements starting at element
+ * l*2*B*S*d_model: K as [B][n_head][S][head_dim], then V transposed as
+ * [B][n_head][head_dim][S]; position t of a sequence is slot t of its S, and
+ * slots >= max_T are never read or written.  Element type as the model dtype.
+ * past_len counts the cached positions; gpt2_forward with a view sets it to T
+ * and gpt2_decode_step increments it. */
 typedef struct {
   void* d_kv;
   int32_t B;
@@ -112,6 +118,42 @@ gpt2_status gpt2_param_blob_floats(const gpt2_config* cfg, size_t* n_floats);
 
 /* Bytes of the device parameter region (converted layout, see gpt2_init_params). */
 gpt2_status gpt2_param_bytes(const gpt2_config* cfg, size_t* bytes);
+
+/* One tensor of the parameter blob (the safetensors key list of pwwt.cn,
+ * section on weights and architecture, in that order) and where
+ * gpt2_init_params puts its converted copy.  Host-only queries, no HIP call.
+ *   blob_offset:  first float of the tensor in the blob.
+ *   rows, cols:   its blob shape [rows, cols]; vectors (biases, LayerNorm
+ *                 gamma/beta) have rows = 1.
+ *   dev_dtype:    element type in the device region: GPT2_BF16 for matrices,
+ *                 wte, wpe (and lm_head.w) of a bf16 model, rounded to nearest
+ *                 even; GPT2_F32 otherwise (all vectors, every fp32 model tensor).
+ *   transposed:   1 when stored as [cols][rows] (element (r, c) of the blob
+ *                 tensor at element c * dev_ld + r), 0 when stored as [rows][cols].
+ *   dev_offset:   byte offset of the copy in the device region.
+ *   dev_ld:       elements between consecutive stored rows.
+ *   dev_rows:     stored rows, at least the blob's; the extra rows (wte and
+ *                 lm_head.w, padded to a multiple of 256) hold zeros.
+ * gpt2_param_tensor_count gives the number of tensors (4 + 12 * n_layer
+ * with the tied head, one more with separate_head); gpt2_param_tensor returns
+ * GPT2_ERR_SHAPE for an index outside [0, count). */
+typedef struct {
+  int64_t blob_offset;
+  int32_t rows;
+  int32_t cols;
+  int32_t dev_dtype;
+  int32_t transposed;
+  int64_t dev_offset;
+  int64_t dev_ld;
+  int64_t dev_rows;
+} gpt2_param_info;
+gpt2_status gpt2_param_tensor_count(const gpt2_config* cfg, int32_t* n);
+gpt2_status gpt2_param_tensor(const gpt2_config* cfg, int32_t index, gpt2_param_info* info);
+
+/* Slot stride S of a KV cache for max_T positions (see gpt2_kv_view):
+ * max_T rounded up to a multiple of 64.  GPT2_ERR_SHAPE unless
+ * 1 <= max_T <= n_positions. */
+gpt2_status gpt2_kv_stride(const gpt2_config* cfg, int32_t max_T, int32_t* stride);
 
 /* Bytes of device workspace needed for gpt2_forward at batch B, length T, and
  * for gpt2_decode_step at batch B (T = 1). */
@@ -235,6 +277,16 @@ gpt2_status gpt2_block_backward(gpt2_model* model, int32_t layer, int32_t B, int
                                 const float* d_dy, float* d_dx, float* d_grads, void* d_ws, size_t ws_bytes,
                                 void* stream);
 
+/* Token-id check (pwwt.cn GPT2Config: ids index the vocab_size rows of wte):
+ * when d_flag (DEVICE int32, caller-owned) is non-NULL, every later forward,
+ * loss, decode or generation call of this handle stores 1 into *d_flag when
+ * one of its input token ids lies outside [0, vocab_size) (that id was
+ * clamped, see the conventions above).  The library never clears the flag:
+ * the caller zeroes it and reads it after synchronising.  NULL turns the
+ * check off (the clamp stays).  Labels of gpt2_forward_loss are not covered
+ * (a label >= vocab_size gives a NaN loss). */
+gpt2_status gpt2_set_id_check(gpt2_model* model, int32_t* d_flag);
+
 /* Optional per-layer trace for debugging: when d_trace is non-NULL, the next
  * gpt2_forward calls copy the residual stream after every block (X_{l+1},
  * fp32 [n_layer][B*T][d_model]) into d_trace, which must hold that many floats.
@@ -254,6 +306,12 @@ const char* gpt2_status_string(gpt2_status s);
 
 /* Text of the last HIP error seen by this thread inside the library ("" if none). */
 const char* gpt2_last_error(void);
+
+/* Digest of the sources this library was built from (16 hex digits of a
+ * SHA-256 over the kernel sources, their headers, this header and the build
+ * script; "unknown" when built without it), so that a loader can refuse a
+ * binary that does not match the sources it ships with. */
+const char* gpt2_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -264,3 +264,96 @@ def test_status_strings(B):
     for s in range(7):
         assert lib.gpt2_status_string(s)
     assert lib.gpt2_last_error() is not None
+
+
+def test_source_hash_matches_the_sources(B):
+    """The loaded library was built from the sources beside it (load() refuses
+    a stale build; the digest is compiled in)."""
+    from gpt_pre_ln_amd.build import source_hash
+    assert B.gpt2_source_hash() == source_hash()
+    assert re.fullmatch(r"[0-9a-f]{16}", B.gpt2_source_hash())
+
+
+@pytest.mark.parametrize("dtype,tied", [("bf16", True), ("bf16", False), ("f32", True)])
+def test_param_tensor_table(B, dtype, tied):
+    """gpt2_param_tensor lists the blob's tensors in the safetensors key order
+    (offsets and shapes as the blob layout of workloads.py), each with a
+    device copy that is aligned, inside the region and disjoint from the
+    others; matrices and embeddings are bf16 in a bf16 model, everything
+    else fp32; Conv1D matrices [in, out] are stored transposed."""
+    import dataclasses
+    s = dataclasses.replace(W.ModelShape(vocab=1000, n_positions=128, d_model=128, n_head=2, n_layer=3, d_ff=512),
+                            tie_word_embeddings=tied)
+    cfg = _cfg(B, s, dtype)
+    offs = W.param_offsets(s)
+    n = B.gpt2_param_tensor_count(cfg)
+    assert n == len(offs) == 4 + 12 * s.n_layer + (0 if tied else 1)
+    region = B.gpt2_param_bytes(cfg)
+    spans = []
+    for i, (key, (off, shp)) in enumerate(offs.items()):
+        t = B.gpt2_param_tensor(cfg, i)
+        rows, cols = (shp[0], shp[1]) if len(shp) == 2 else (1, shp[0])
+        assert (t.blob_offset, t.rows, t.cols) == (off, rows, cols), key
+        matrix = len(shp) == 2
+        assert t.dev_dtype == (B.GPT2_BF16 if (dtype == "bf16" and matrix) else B.GPT2_F32), key
+        assert t.transposed == int(matrix and key not in ("wte", "wpe", "lm_head.w")), key
+        stored_rows, row_len = (cols, rows) if t.transposed else (rows, cols)
+        assert t.dev_ld == row_len and t.dev_rows >= stored_rows, key
+        if key in ("wte", "lm_head.w"):
+            assert t.dev_rows % 256 == 0 and t.dev_rows - stored_rows < 256
+        es = 2 if t.dev_dtype == B.GPT2_BF16 else 4
+        assert t.dev_offset % 256 == 0
+        end = t.dev_offset + t.dev_rows * t.dev_ld * es
+        assert end <= region
+        spans.append((t.dev_offset, end, key))
+    spans.sort()
+    for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
+        assert a1 <= b0, (ka, kb)
+    for bad in (-1, n):
+        with pytest.raises(B.GPT2Error) as e:
+            B.gpt2_param_tensor(cfg, bad)
+        assert e.value.status == B.GPT2_ERR_SHAPE
+
+
+def test_kv_stride(B):
+    s = W.ModelShape(vocab=1000, n_positions=300, d_model=128, n_head=2, n_layer=2, d_ff=512)
+    cfg = _cfg(B, s, "bf16")
+    for max_T, want in ((1, 64), (40, 64), (64, 64), (65, 128), (70, 128), (300, 320)):
+        assert B.gpt2_kv_stride(cfg, max_T) == want
+        # the cache size is n_layer * 2 (K and V^T) * B * S * d_model elements
+        assert B.gpt2_kv_cache_bytes(cfg, 3, max_T) == s.n_layer * 2 * 3 * want * s.d_model * 2
+    for bad in (0, 301):
+        with pytest.raises(B.GPT2Error) as e:
+            B.gpt2_kv_stride(cfg, bad)
+        assert e.value.status == B.GPT2_ERR_SHAPE
+
+
+def test_set_id_check_host_checks(B, handle):
+    h, _ = handle
+    assert B.load().gpt2_set_id_check(None, None) == B.GPT2_ERR_INVALID_ARG
+    assert B.load().gpt2_set_id_check(h, 0x1002) == B.GPT2_ERR_INVALID_ARG  # not 4-byte aligned
+    assert B.load().gpt2_set_id_check(h, 0x1000) == B.GPT2_OK
+    assert B.load().gpt2_set_id_check(h, None) == B.GPT2_OK
+
+
+def test_token_id_clamp_host_build(tmp_path):
+    """The clamp the embedding applies to every id (rowops.h, clamp_token_id),
+    compiled for the host with the same header: ids outside [0, V) go to the
+    nearest row, ids inside are kept."""
+    src = tmp_path / "clamp.hip"
+    src.write_text('#include "rowops.h"\n#include <cstdio>\n#include <climits>\n'
+                   'int main() { const int V = 50257;\n'
+                   '  const int ids[] = {INT_MIN, -50257, -1, 0, 1, 777, V - 2, V - 1, V, V + 1, INT_MAX};\n'
+                   '  for (int id : ids) std::printf("%d %d\\n", id, gpt2::clamp_token_id(id, V));\n'
+                   '  std::printf("%d %d\\n", 5, gpt2::clamp_token_id(5, 1));\n  return 0; }\n')
+    exe = tmp_path / "clamp"
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-std=c++20", "-w", "--offload-arch=gfx950",
+                        "-I", os.path.join(ROOT, "gpt_pre_ln_amd", "csrc"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = [tuple(map(int, l.split())) for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                               check=True).stdout.split("\n") if l]
+    V = 50257
+    want = [(i, min(max(i, 0), V - 1)) for i in (-2**31, -V, -1, 0, 1, 777, V - 2, V - 1, V, V + 1, 2**31 - 1)]
+    assert got == want + [(5, 0)]
+

@@ -173,6 +173,33 @@ def test_bf16_round_hand_values_and_torch():
     np.testing.assert_array_equal(oracle.bf16_round(x), ref)
 
 
+@pytest.mark.parametrize("tied", [True, False])
+def test_bf16_rounding_set_is_the_stored_matrices(tied):
+    """Reading R10 ("bf16 weights"): in a bf16 model exactly the two-dimensional
+    tensors of the safetensors key list (pwwt.cn, section on weights and
+    architecture: wte [V, D], wpe [P, D], c_attn.w, c_proj.w, c_fc.w, the
+    separate head lm_head.w) are rounded to bf16 once, and every one-dimensional
+    tensor (biases, LayerNorm gamma and beta) keeps its fp32 value exactly.  The
+    set is read off the blob shapes, not off the oracle's key names; every
+    tensor holds values that bf16 cannot represent, so a wrongly rounded or a
+    wrongly kept tensor shows."""
+    import dataclasses
+    s = dataclasses.replace(_tiny_shape(n_head=2, d=32, L=2, vocab=64, npos=16), tie_word_embeddings=tied)
+    blob = W.make_params(s, W.Init(w_std=0.3, proj_std=0.3, bias_std=0.3, gamma=(1.0, 0.3), beta=(0.0, 0.3)), 11)
+    raw = W.unpack(blob, s)
+    P16 = oracle.prepare_params(blob, s, "bf16")
+    P32 = oracle.prepare_params(blob, s, "f32")
+    matrices = {k for k, a in raw.items() if a.ndim == 2}
+    assert {"wte", "wpe"} <= matrices and ("lm_head.w" in matrices) == (not tied)
+    assert len(matrices) == 2 + 4 * s.n_layer + (0 if tied else 1)
+    for k, a in raw.items():
+        a32 = a.astype(np.float32)
+        assert not np.array_equal(oracle.bf16_round(a32), a32), k   # rounding changes this tensor
+        want16 = oracle.bf16_round(a32) if k in matrices else a32
+        np.testing.assert_array_equal(P16[k], want16.astype(np.float64), err_msg=k)
+        np.testing.assert_array_equal(P32[k], a32.astype(np.float64), err_msg=k)
+
+
 # ---------------------------------------------------------------- parameter layout
 
 
