@@ -71,6 +71,9 @@ _SIG = {
                                          ctypes.POINTER(gpt2_param_info)]),
     "gpt2_kv_stride": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "gpt2_set_id_check": (ctypes.c_int, [_P, _P]),
+    "gpt2_decode_step_noalloc": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
+    "gpt2_decode_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "gpt2_source_hash": (ctypes.c_char_p, []),
     "gpt2_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_size_t)]),
@@ -278,3 +281,15 @@ def gpt2_set_id_check(handle, d_flag):
 def gpt2_source_hash() -> str:
     return load().gpt2_source_hash().decode()
 
+
+def gpt2_decode_step_noalloc(handle, kv, d_new_tokens: int, d_logits: int, stream: int):
+    _check(load().gpt2_decode_step_noalloc(handle, ctypes.byref(kv), d_new_tokens, d_logits, stream),
+           "gpt2_decode_step_noalloc")
+
+
+def gpt2_decode_scratch_bytes(cfg, B: int):
+    """(bytes the allocation-free decode step needs at batch B, the library's per-device limit)."""
+    n, lim = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().gpt2_decode_scratch_bytes(ctypes.byref(cfg), B, ctypes.byref(n), ctypes.byref(lim)),
+           "gpt2_decode_scratch_bytes")
+    return n.value, lim.value

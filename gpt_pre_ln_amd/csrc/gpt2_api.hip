@@ -8,6 +8,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -203,7 +204,9 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout ws_layout(const gpt2_config& c, int B, int T) {
+// decode_only: the layout of a decode step alone, without the prefill key and
+// value buffers (a decode step reads and appends to the caller's cache).
+WsLayout ws_layout(const gpt2_config& c, int B, int T, bool decode_only = false) {
   WsLayout W;
   const size_t es = esize(c), D = c.d_model, F = c.d_ff, M = (size_t)B * T;
   const size_t Tp = kv_stride(T);
@@ -217,8 +220,8 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
   W.x = take(M * D * 4);
   W.h = take(M * D * es);
   W.q = take(M * D * es);
-  W.k = take((size_t)B * Tp * D * es);
-  W.vt = take((size_t)B * Tp * D * es);
+  W.k = take(decode_only ? 0 : (size_t)B * Tp * D * es);
+  W.vt = take(decode_only ? 0 : (size_t)B * Tp * D * es);
   W.a = take(M * D * es);
   W.u = take(M * F * es);
   W.part = take(decode_partials_floats(B, c.n_head, hs) * 4);
@@ -238,6 +241,37 @@ WsLayout ws_layout(const gpt2_config& c, int B, int T) {
 
 size_t kv_layer_bytes(const gpt2_config& c, int B, int max_T) {
   return 2 * (size_t)B * kv_stride(max_T) * c.d_model * esize(c);
+}
+
+// ------------------------------------------------------------------ allocation-free decode
+
+// Scratch of gpt2_decode_step_noalloc: the decode step's activations and
+// partial results, in a device array that exists for the life of the process
+// (one per GPU), for callers that cannot allocate.  Host code never passes the
+// array's name to a kernel or a copy: that name is a host-side stand-in, and
+// the device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (set up on first use).
+gpt2_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  GPT2_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return GPT2_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    GPT2_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return GPT2_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return GPT2_OK;
 }
 
 // ------------------------------------------------------------------ timing
@@ -481,14 +515,16 @@ struct GenOut {
   int32_t* next;
 };
 
+// ws (optional): run on this scratch region, laid out by
+// ws_layout(.., decode_only = true), instead of the handle's workspace.
 template <typename T>
 gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits, const GenOut* gen,
-                       hipStream_t st) {
+                       hipStream_t st, char* ws = nullptr) {
   const gpt2_config& c = m->cfg;
   const int D = c.d_model, H = c.n_head, hs = D / H, F = c.d_ff, V = c.vocab_size;
   const int B = kv->B, M = B, pos = kv->past_len;
-  const WsLayout W = ws_layout(c, B, 1);
-  char* const wsb = m->ws;
+  const WsLayout W = ws_layout(c, B, 1, ws != nullptr);
+  char* const wsb = ws ? ws : m->ws;
   float* x = reinterpret_cast<float*>(wsb + W.x);
   T* h = reinterpret_cast<T*>(wsb + W.h);
   T* q = reinterpret_cast<T*>(wsb + W.q);
@@ -1011,6 +1047,38 @@ gpt2_status gpt2_decode_step(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tok
   hipStream_t st = static_cast<hipStream_t>(stream);
   return m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, tokens, logits, nullptr, st)
                                    : run_decode<float>(m, kv, tokens, logits, nullptr, st);
+}
+
+gpt2_status gpt2_decode_step_noalloc(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, void* logits,
+                                     void* stream) {
+  if (!m || !kv || !tokens || !logits || !kv->d_kv) return GPT2_ERR_INVALID_ARG;
+  const size_t lsz = m->cfg.logits_dtype == GPT2_BF16 ? 2 : 4;
+  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(logits, lsz)) return GPT2_ERR_INVALID_ARG;
+  if (kv->B < 1 || kv->max_T < 1 || kv->max_T > m->cfg.n_positions) return GPT2_ERR_SHAPE;
+  if (kv->past_len < 0) return GPT2_ERR_SHAPE;
+  if (kv->past_len >= kv->max_T) return GPT2_ERR_CAPACITY;
+  if (ws_layout(m->cfg, kv->B, 1, true).total > kNoAllocScratchBytes) {
+    g_last_error = "gpt2_decode_step_noalloc: the step needs " +
+                   std::to_string(ws_layout(m->cfg, kv->B, 1, true).total) + " bytes of scratch, more than the " +
+                   std::to_string(kNoAllocScratchBytes) + " the library holds per device";
+    return GPT2_ERR_WORKSPACE;
+  }
+  char* ws = nullptr;
+  gpt2_status s = scratch_of_current_device(&ws);
+  if (s != GPT2_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, tokens, logits, nullptr, st, ws)
+                                   : run_decode<float>(m, kv, tokens, logits, nullptr, st, ws);
+}
+
+gpt2_status gpt2_decode_scratch_bytes(const gpt2_config* cfg, int32_t B, size_t* bytes, size_t* limit) {
+  gpt2_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes && !limit) return GPT2_ERR_INVALID_ARG;
+  if (B < 1 || B > (1 << 24)) return GPT2_ERR_SHAPE;
+  if (bytes) *bytes = ws_layout(*cfg, B, 1, true).total;
+  if (limit) *limit = kNoAllocScratchBytes;
+  return GPT2_OK;
 }
 
 gpt2_status gpt2_generate(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, int32_t n_steps, int32_t* out,

@@ -233,6 +233,27 @@ gpt2_status gpt2_forward_loss(gpt2_model* model, const int32_t* d_tokens, const 
 gpt2_status gpt2_decode_step(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_new_tokens,
                              void* d_logits, void* stream);
 
+/* gpt2_decode_step without the handle's workspace, for callers that cannot
+ * allocate device memory or must not touch the workspace (code under HIP
+ * graph capture, tight serving loops).  Same arguments, checks, kernels and
+ * results as gpt2_decode_step; the step's activations and partial results live
+ * in a scratch array of fixed size (gpt2_decode_scratch_bytes: `limit`, 16 MiB)
+ * that the library holds on each GPU it runs on until the process ends.  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array
+ * (nothing in it needs to start at zero: each step writes what it later
+ * reads), so calls that overlap on one GPU -- on two streams, or from two
+ * threads -- race and must be serialised by the caller; the handle's
+ * workspace is not touched.  The device is the current HIP device.
+ * Errors: those of gpt2_decode_step, and GPT2_ERR_WORKSPACE when the step
+ * needs more scratch than the limit (gpt2_decode_scratch_bytes: `bytes`;
+ * GPT-2 small needs about 3.2 MB at B = 32). */
+gpt2_status gpt2_decode_step_noalloc(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_new_tokens,
+                                     void* d_logits, void* stream);
+
+/* Scratch bytes gpt2_decode_step_noalloc needs at batch B (`bytes`, optional)
+ * and the size of the library's per-device array (`limit`, optional). */
+gpt2_status gpt2_decode_scratch_bytes(const gpt2_config* cfg, int32_t B, size_t* bytes, size_t* limit);
+
 /* Greedy generation: n_steps decode steps in one call, each feeding the token
  * it chose to the next, with no host round trip (pwwt.cn closing section:
  * generation one token at a time over a KV cache; bbs.huaweicloud.com blog

@@ -357,3 +357,25 @@ def test_token_id_clamp_host_build(tmp_path):
     want = [(i, min(max(i, 0), V - 1)) for i in (-2**31, -V, -1, 0, 1, 777, V - 2, V - 1, V, V + 1, 2**31 - 1)]
     assert got == want + [(5, 0)]
 
+
+def test_decode_noalloc_host_checks(B, handle):
+    """The allocation-free decode step rejects what gpt2_decode_step rejects,
+    and a batch whose scratch exceeds the per-device array, before any HIP call."""
+    h, cfg = handle
+    lib = B.load()
+    kv = B.gpt2_kv_view(FAKE + (1 << 30), 2, 64, 0)
+    assert lib.gpt2_decode_step_noalloc(None, ctypes.byref(kv), FAKE, FAKE, None) == B.GPT2_ERR_INVALID_ARG
+    assert lib.gpt2_decode_step_noalloc(h, ctypes.byref(kv), None, FAKE, None) == B.GPT2_ERR_INVALID_ARG
+    assert lib.gpt2_decode_step_noalloc(h, ctypes.byref(kv), FAKE, None, None) == B.GPT2_ERR_INVALID_ARG
+    full = B.gpt2_kv_view(FAKE + (1 << 30), 2, 64, 64)
+    assert lib.gpt2_decode_step_noalloc(h, ctypes.byref(full), FAKE, FAKE, None) == B.GPT2_ERR_CAPACITY
+    long = B.gpt2_kv_view(FAKE + (1 << 30), 2, 129, 0)   # n_positions is 128
+    assert lib.gpt2_decode_step_noalloc(h, ctypes.byref(long), FAKE, FAKE, None) == B.GPT2_ERR_SHAPE
+    need1, limit = B.gpt2_decode_scratch_bytes(cfg, 1)
+    assert 0 < need1 < limit == 16 << 20
+    big = 1
+    while B.gpt2_decode_scratch_bytes(cfg, big)[0] <= limit:
+        big *= 2
+    huge = B.gpt2_kv_view(FAKE + (1 << 30), big, 64, 0)
+    assert lib.gpt2_decode_step_noalloc(h, ctypes.byref(huge), FAKE, FAKE, None) == B.GPT2_ERR_WORKSPACE
+    assert "scratch" in lib.gpt2_last_error().decode()
