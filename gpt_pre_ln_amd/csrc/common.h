@@ -216,6 +216,19 @@ __device__ __forceinline__ float gelu_erf_grad(float x) {
   return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * expf(-0.5f * x * x) * 0.3989422804014327f;
 }
 
+// Workgroup i of a grid runs on XCD i % 8 (MI355X: 8 accelerator dies, each
+// with its own L2; the GEMM tile order relies on the same placement).
+// xcd_block renumbers a grid of n blocks so that each XCD takes a contiguous
+// eighth of the work: block i handles item (i % 8) * (n / 8) + i / 8 when
+// n % 8 == 0 (identity otherwise).  Row kernels use it so that the rows an
+// XCD reads are the rows the same XCD wrote in the GEMM before (and writes
+// the rows the same XCD reads in the GEMM after): those accesses then hit
+// its L2 instead of crossing to another die's data.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int i, int n) {
+  return (n % kXcds == 0) ? (i % kXcds) * (n / kXcds) + i / kXcds : i;
+}
+
 // Division by a runtime-invariant positive divisor through a precomputed
 // multiplier (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI 1994): for 0 <= n < 2^31 and 1 <= d < 2^31,

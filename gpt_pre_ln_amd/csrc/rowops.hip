@@ -17,7 +17,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ wte,
                                                      const T* __restrict__ wpe, float* __restrict__ x, int M,
                                                      int T_seq, int pos0, int D, int V, int32_t* __restrict__ bad) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = xcd_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const int raw = ids[row];
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* x, const fl
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < pf16; i += (size_t)gridDim.x * 256) acc ^= pf[i];
     asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
   }
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = xcd_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const float* xr = x + (size_t)row * D;
