@@ -91,6 +91,8 @@ _SIG = {
     "gpt2_forward_loss": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, _P, _P]),
     "gpt2_generate": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, ctypes.c_int32, _P, _P]),
+    "gpt2_generate_sample": (ctypes.c_int, [_P, ctypes.POINTER(gpt2_kv_view), _P, ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_uint64, _P, _P]),
     "gpt2_block_backward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(gpt2_config), ctypes.c_int32,
                                                            ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "gpt2_block_backward": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P,
@@ -225,6 +227,12 @@ def gpt2_decode_step(handle, kv, d_new_tokens: int, d_logits: int, stream: int):
 
 def gpt2_generate(handle, kv, d_tokens: int, n_steps: int, d_out_tokens: int, stream: int):
     _check(load().gpt2_generate(handle, ctypes.byref(kv), d_tokens, n_steps, d_out_tokens, stream), "gpt2_generate")
+
+
+def gpt2_generate_sample(handle, kv, d_tokens: int, n_steps: int, temperature: float, seed: int, d_out_tokens: int,
+                         stream: int):
+    _check(load().gpt2_generate_sample(handle, ctypes.byref(kv), d_tokens, n_steps, temperature, seed, d_out_tokens,
+                                       stream), "gpt2_generate_sample")
 
 
 def gpt2_block_backward_workspace_bytes(cfg, B: int, T: int) -> int:

@@ -312,6 +312,59 @@ struct EpiArgmax {
   __device__ __forceinline__ void partial(int m, int s, float v, int col) const {
     part[(size_t)m * nseg + s] = make_int2(__builtin_bit_cast(int, v), col);
   }
+  // the value compared for row m, column col: the logit itself
+  __device__ __forceinline__ uint64_t row_key(int) const { return 0; }
+  __device__ __forceinline__ float score(uint64_t, int, float v) const { return v; }
+};
+
+// SplitMix64 output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014): the state advanced by the
+// golden-ratio increment, then two xor-shift-multiply rounds.
+__host__ __device__ inline uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Sampling from softmax(logits / temperature) by the Gumbel-max identity:
+// argmax_v (logit_v / temperature + G_v) with G_v = -ln(-ln U_v) independent
+// standard Gumbel variables is distributed as that softmax (huaweicloud blog
+// 476445, architecture overview: softmax over the vocabulary, then a token is
+// picked).  U_v comes from a counter-based generator, so the draw depends only
+// on (seed, position, row, column):
+//   key_row = splitmix64(splitmix64(seed) ^ (position << 32) ^ row)
+//   U_v     = ((splitmix64(key_row ^ v) >> 40) + 1/2) / 2^24, in (0, 1).
+// Same slice partials as EpiArgmax, with the perturbed score in place of the
+// logit.
+struct EpiSample {
+  static constexpr bool kPreload = false, kBias = false, kTransposed = false, kRowReduce = false,
+                        kRowArgmax = true;
+  int2* part;       // [M][nseg]: (bits of the slice's largest score, its first column)
+  int nseg;
+  int n_valid;      // vocabulary size
+  uint64_t seed_mix;  // splitmix64(seed)
+  int pos;          // position of the step's input token
+  float inv_temp;   // 1 / temperature
+  __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
+  __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
+  __device__ __forceinline__ bool transposed(int) const { return false; }
+  __device__ __forceinline__ void apply(int, int, const f32x4_t&, const float4&) const {}
+  __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+  __device__ __forceinline__ void partial(int m, int s, float v, int col) const {
+    part[(size_t)m * nseg + s] = make_int2(__builtin_bit_cast(int, v), col);
+  }
+  __device__ __forceinline__ uint64_t row_key(int m) const {
+    return splitmix64(seed_mix ^ ((uint64_t)(uint32_t)pos << 32) ^ (uint64_t)(uint32_t)m);
+  }
+  __device__ __forceinline__ float score(uint64_t key, int col, float v) const {
+    const uint64_t z = splitmix64(key ^ (uint64_t)(uint32_t)col);
+    const float u = ((float)(uint32_t)(z >> 40) + 0.5f) * 5.9604644775390625e-8f;  // 2^-24
+    // -ln(-ln u) through the hardware base-2 logarithm: ln x = log2(x) ln 2
+    const float ln2 = 0.69314718055994531f;
+    const float e = -__builtin_amdgcn_logf(u) * ln2;  // -ln u > 0
+    return v * inv_temp - __builtin_amdgcn_logf(e) * ln2;
+  }
 };
 
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),

@@ -250,13 +250,15 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
       const int m = m0 + wm * WTM + i * 16 + lr;
       float best = -INFINITY;
       int bi = 0x7fffffff;
+      const uint64_t rk = epi.row_key(m);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = nw + j * 16 + lg * 4 + e;
-          if (col < epi.n_valid && acc[i][j][e] > best) {
-            best = acc[i][j][e];
+          const float v = epi.score(rk, col, acc[i][j][e]);
+          if (col < epi.n_valid && v > best) {
+            best = v;
             bi = col;
           }
         }
@@ -601,6 +603,10 @@ template hipError_t launch_gemm<float, EpiArgmax>(GemmTile, const float*, const 
                                                   const EpiArgmax&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiArgmax>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,
                                                    const EpiArgmax&, hipStream_t);
+template hipError_t launch_gemm<float, EpiSample>(GemmTile, const float*, const float*, int, int, int, int, int,
+                                                  const EpiSample&, hipStream_t);
+template hipError_t launch_gemm<bf16_t, EpiSample>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,
+                                                   const EpiSample&, hipStream_t);
 template hipError_t launch_gemm<float, EpiCE>(GemmTile, const float*, const float*, int, int, int, int, int,
                                               const EpiCE&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiCE>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,

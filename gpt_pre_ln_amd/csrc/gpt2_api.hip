@@ -513,6 +513,9 @@ struct GenOut {
   int32_t* out;
   int stride, col;
   int32_t* next;
+  bool sample = false;  // draw from softmax(logits / temperature) instead of the arg-max
+  uint64_t seed_mix = 0;  // splitmix64(seed)
+  float inv_temp = 1.f;
 };
 
 // ws (optional): run on this scratch region, laid out by
@@ -599,9 +602,17 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   if (gen) {
     // lm_head with the arg-max epilogue (no logits stored), then one wave per row
     int2* apart = reinterpret_cast<int2*>(wsb + W.ce_part);
-    EpiArgmax e{apart, W.ce_nseg, V};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c), D), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e, st),
-             "lm_head argmax");
+    if (gen->sample) {
+      EpiSample e{apart, W.ce_nseg, V, gen->seed_mix, pos, gen->inv_temp};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c), D), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e,
+                              st),
+               "lm_head sample");
+    } else {
+      EpiArgmax e{apart, W.ce_nseg, V};
+      GPT2_HIP(launch_gemm<T>(pick_tile(M, vocab_pad(c), D), h, pp<T>(m, m->lay.head), M, vocab_pad(c), D, D, D, e,
+                              st),
+               "lm_head argmax");
+    }
     GPT2_HIP(launch_argmax_rows(apart, W.ce_nseg, M, V, gen->out + gen->col, gen->stride, gen->next, st), "argmax");
   } else {
     GPT2_HIP(launch_lm_head<T>(m, h, logits, c.vocab_size, M, st), "lm_head");
@@ -1078,6 +1089,33 @@ gpt2_status gpt2_decode_scratch_bytes(const gpt2_config* cfg, int32_t B, size_t*
   if (B < 1 || B > (1 << 24)) return GPT2_ERR_SHAPE;
   if (bytes) *bytes = ws_layout(*cfg, B, 1, true).total;
   if (limit) *limit = kNoAllocScratchBytes;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_generate_sample(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, int32_t n_steps,
+                                 float temperature, uint64_t seed, int32_t* out, void* stream) {
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return GPT2_ERR_INVALID_ARG;
+  if (temperature == 0.f) return gpt2_generate(m, kv, tokens, n_steps, out, stream);
+  if (!m || !kv || !tokens || !out || !kv->d_kv) return GPT2_ERR_INVALID_ARG;
+  if (!aligned(kv->d_kv, kAlign) || !aligned(tokens, 4) || !aligned(out, 4)) return GPT2_ERR_INVALID_ARG;
+  if (n_steps < 1) return GPT2_ERR_SHAPE;
+  if (kv->B < 1 || kv->max_T < 1 || kv->max_T > m->cfg.n_positions) return GPT2_ERR_SHAPE;
+  if (kv->past_len < 0) return GPT2_ERR_SHAPE;
+  if ((int64_t)kv->past_len + n_steps > kv->max_T) return GPT2_ERR_CAPACITY;
+  const WsLayout W = ws_layout(m->cfg, kv->B, 1);
+  if (W.total > m->ws_bytes) return GPT2_ERR_WORKSPACE;
+  int32_t* next = reinterpret_cast<int32_t*>(m->ws + W.gen_tok);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int i = 0; i < n_steps; ++i) {
+    GenOut g{out, n_steps, i, next};
+    g.sample = true;
+    g.seed_mix = splitmix64(seed);
+    g.inv_temp = 1.0f / temperature;
+    const int32_t* in = i == 0 ? tokens : next;
+    const gpt2_status s = m->cfg.dtype == GPT2_BF16 ? run_decode<bf16_t>(m, kv, in, nullptr, &g, st)
+                                                    : run_decode<float>(m, kv, in, nullptr, &g, st);
+    if (s != GPT2_OK) return s;
+  }
   return GPT2_OK;
 }
 

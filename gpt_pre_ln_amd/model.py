@@ -153,6 +153,19 @@ class GPT2:
         B.gpt2_generate(self.handle, kv.view, first_ids.data_ptr(), n_steps, out.data_ptr(), self.stream)
         return out
 
+    def generate_sample(self, kv: KVCache, first_ids: torch.Tensor, n_steps: int, temperature: float = 1.0,
+                        seed: int = 0, out: torch.Tensor | None = None):
+        """Sampled generation (gpt2_generate_sample): each step draws from
+        softmax(logits / temperature); reproducible from (seed, position, row)."""
+        assert first_ids.dtype == torch.int32 and first_ids.is_contiguous() and first_ids.device == self.device
+        Bsz = kv.view.B
+        if out is None:
+            out = torch.empty((Bsz, n_steps), dtype=torch.int32, device=self.device)
+        assert out.dtype == torch.int32 and out.is_contiguous() and tuple(out.shape) == (Bsz, n_steps)
+        B.gpt2_generate_sample(self.handle, kv.view, first_ids.data_ptr(), n_steps, float(temperature),
+                               int(seed) & ((1 << 64) - 1), out.data_ptr(), self.stream)
+        return out
+
     def layer_param_count(self) -> int:
         D, F = self.cfg.d_model, self.cfg.d_ff
         return 2 * D + (3 * D * D + 3 * D) + (D * D + D) + 2 * D + (D * F + F) + (F * D + D)

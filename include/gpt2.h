@@ -272,6 +272,26 @@ gpt2_status gpt2_decode_scratch_bytes(const gpt2_config* cfg, int32_t B, size_t*
 gpt2_status gpt2_generate(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_tokens, int32_t n_steps,
                           int32_t* d_out_tokens, void* stream);
 
+/* Generation that samples: like gpt2_generate, but each step draws its token
+ * from softmax(logits / temperature) over the vocabulary -- the pages' last
+ * step, a softmax over the vocabulary and a token picked from it
+ * (bbs.huaweicloud.com blog 476445, architecture overview; nano-ai.tech
+ * Transformer Stack: with random weights the pick is essentially a random
+ * draw).  The draw uses the Gumbel-max form, argmax_v (logit_v / temperature
+ * + G_v) with G_v = -ln(-ln U_v), evaluated in fp32 from the lm_head's
+ * accumulators (no logits are written), and a counter-based generator, so
+ * the tokens depend only on (seed, position, row) and are reproducible:
+ *   s0  = splitmix64(seed)
+ *   key = splitmix64(s0 ^ (position << 32) ^ row)      position: of the step's
+ *                                                     input token (kv->past_len)
+ *   U_v = ((splitmix64(key ^ v) >> 40) + 0.5) * 2^-24
+ * with splitmix64(x) the SplitMix64 output function of x + 0x9E3779B97F4A7C15
+ * (Steele, Lea and Flood, OOPSLA 2014).  temperature == 0 is the greedy
+ * gpt2_generate; temperature < 0, NaN or infinite gives GPT2_ERR_INVALID_ARG.
+ * Other arguments, checks and results as gpt2_generate. */
+gpt2_status gpt2_generate_sample(gpt2_model* model, gpt2_kv_view* kv, const int32_t* d_tokens, int32_t n_steps,
+                                 float temperature, uint64_t seed, int32_t* d_out_tokens, void* stream);
+
 /* Bytes of the backward workspace for gpt2_block_backward at batch B, length T. */
 gpt2_status gpt2_block_backward_workspace_bytes(const gpt2_config* cfg, int32_t B, int32_t T, size_t* bytes);
 

@@ -9,6 +9,7 @@ See ``oracle.gpt2`` for the functions and the passages each one follows.
 from .gpt2 import (  # noqa: F401
     bf16_round, layer_norm, gelu_new, gelu_erf, causal_attention, block_forward,
     embed, forward_hidden, forward, decode_logits, shifted_cross_entropy, lm_loss, generate_greedy,
+    splitmix64, sample_uniforms, sample_token, generate_sample,
     gelu_new_grad, gelu_erf_grad, layer_norm_backward, block_backward, block_backward_batch, prepare_params,
     TRACE_POINTS,
 )

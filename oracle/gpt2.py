@@ -315,6 +315,65 @@ def generate_greedy(P: dict, prompt: np.ndarray, n_steps: int) -> np.ndarray:
     return out
 
 
+_U64 = np.uint64
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: np.ndarray) -> np.ndarray:
+    """SplitMix64 output function (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", OOPSLA 2014): state x advanced by the
+    golden-ratio increment 0x9E3779B97F4A7C15, then z ^= z >> 30, z *= 0xBF58476D1CE4E5B9,
+    z ^= z >> 27, z *= 0x94D049BB133111EB, z ^= z >> 31, all modulo 2^64."""
+    with np.errstate(over="ignore"):
+        z = np.asarray(x, dtype=_U64) + _U64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> _U64(30))) * _U64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> _U64(27))) * _U64(0x94D049BB133111EB)
+        return z ^ (z >> _U64(31))
+
+
+def sample_uniforms(seed: int, position: int, row: int, n: int) -> np.ndarray:
+    """U_v in (0, 1) for v = 0..n-1 of one row at one position: a counter-based
+    draw, U_v = ((splitmix64(key ^ v) >> 40) + 1/2) / 2^24 with
+    key = splitmix64(splitmix64(seed) ^ (position << 32) ^ row)."""
+    s0 = int(splitmix64(_U64(seed & _M64)))
+    key = int(splitmix64(_U64((s0 ^ ((position & 0xFFFFFFFF) << 32) ^ (row & 0xFFFFFFFF)) & _M64)))
+    z = splitmix64(_U64(key) ^ np.arange(n, dtype=_U64))
+    return ((z >> _U64(40)).astype(np.float64) + 0.5) / float(1 << 24)
+
+
+def sample_token(logits: np.ndarray, temperature: float, seed: int, position: int, row: int):
+    """One token drawn from softmax(logits / temperature): the Gumbel-max
+    identity, argmax_v (logit_v / temperature + G_v) with G_v = -ln(-ln U_v)
+    standard Gumbel variables, is distributed as that softmax (the pages' last
+    step: [Anatomy] architecture overview, softmax over the vocabulary and a
+    token picked from it; [Stack]: with random weights the pick is a random
+    draw).  Returns (token, the perturbed scores); ties to the lowest index."""
+    u = sample_uniforms(seed, position, row, logits.shape[-1])
+    scores = np.asarray(logits, np.float64) / temperature - np.log(-np.log(u))
+    return int(scores.argmax()), scores
+
+
+def generate_sample(P: dict, prompt: np.ndarray, n_steps: int, temperature: float, seed: int):
+    """Sampled continuation of prompt [B, P]: as generate_greedy, with each
+    token drawn by sample_token at the position of the step's input token
+    (the last token of the sequence so far) for row b.  Returns (tokens
+    [B, n_steps], the perturbed scores [B, n_steps, V])."""
+    seq = np.atleast_2d(np.asarray(prompt)).copy()
+    Bn = seq.shape[0]
+    out = np.empty((Bn, n_steps), dtype=np.int64)
+    all_scores = []
+    for i in range(n_steps):
+        pos = seq.shape[1] - 1
+        last = forward(P, seq, positions=[pos])[:, 0, :]
+        step_scores = []
+        for b in range(Bn):
+            out[b, i], sc = sample_token(last[b], temperature, seed, pos, b)
+            step_scores.append(sc)
+        all_scores.append(np.stack(step_scores))
+        seq = np.concatenate([seq, out[:, i:i + 1]], axis=1)
+    return out, np.stack(all_scores, axis=1)
+
+
 # --------------------------------------------------------------------------
 # Backward of one block
 # --------------------------------------------------------------------------

@@ -713,3 +713,70 @@ def test_gelu_grads_vs_torch_autograd():
     for approx, fn in (("tanh", oracle.gelu_new_grad), ("none", oracle.gelu_erf_grad)):
         g, = torch.autograd.grad(F.gelu(x, approximate=approx).sum(), x)
         np.testing.assert_allclose(fn(x.detach().numpy()), g.numpy(), rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- sampled generation
+
+
+def test_splitmix64_published_outputs():
+    """The generator: SplitMix64 seeded with 0 gives 0xE220A8397B1DCDAF,
+    0x6E789E6AA1B965F4, 0x06C45D188009454F as its first three outputs (the
+    state advancing by the golden-ratio increment between calls)."""
+    g = 0x9E3779B97F4A7C15
+    got = [int(oracle.splitmix64(np.uint64(k * g % (1 << 64)))) for k in range(3)]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_sample_uniforms_are_uniform_and_keyed():
+    """U in (0, 1), flat (Kolmogorov-Smirnov against U(0, 1)), different for a
+    different seed, position or row, the same for the same key."""
+    from scipy import stats
+    u = oracle.sample_uniforms(7, 100, 3, 200000)
+    assert u.min() > 0.0 and u.max() < 1.0
+    assert stats.kstest(u, "uniform").pvalue > 1e-4
+    np.testing.assert_array_equal(u, oracle.sample_uniforms(7, 100, 3, 200000))
+    for other in ((8, 100, 3), (7, 101, 3), (7, 100, 4)):
+        assert (oracle.sample_uniforms(*other, 1000) != u[:1000]).mean() > 0.99
+
+
+@pytest.mark.parametrize("temperature", [0.5, 1.0, 2.0])
+def test_sample_token_distribution_is_softmax(temperature):
+    """Gumbel-max: over independent rows, the drawn tokens follow
+    softmax(logits / temperature) (chi-square goodness of fit)."""
+    from scipy import stats
+    logits = np.array([2.0, 1.0, 0.5, 0.0, -1.0, 3.0, 1.5, -0.5])
+    n = 20000
+    toks = np.array([oracle.sample_token(logits, temperature, 11, 5, r)[0] for r in range(n)])
+    p = np.exp(logits / temperature - (logits / temperature).max())
+    p /= p.sum()
+    counts = np.bincount(toks, minlength=len(logits))
+    assert stats.chisquare(counts, p * n).pvalue > 1e-4
+
+
+def test_sample_small_temperature_is_greedy():
+    """As the temperature goes to 0 the draw is the arg-max (the noise spread,
+    at most about 20, is far below logit gaps / temperature), so sampled
+    generation at a tiny temperature equals greedy generation on the
+    closed-form model of test_generate_greedy_closed_form."""
+    V, D, NP = 48, 64, 32
+    s = _tiny_shape(n_head=1, d=D, L=2, vocab=V, npos=NP)
+    blob = W.make_params(s, W.Init(w_std=0.2, proj_std=0.2, bias_std=0.1, gamma=(1.0, 0.3), beta=(0.0, 0.3)), 39)
+    view = W.unpack(blob, s)
+    for l in range(s.n_layer):
+        for k in ("attn.c_proj.w", "attn.c_proj.b", "mlp.c_proj.w", "mlp.c_proj.b"):
+            view[f"h.{l}.{k}"][...] = 0.0
+    view["ln_f.w"][...] = 1.0
+    view["ln_f.b"][...] = 0.0
+    view["wte"][...] = 0.0
+    view["wte"][np.arange(V), np.arange(V)] = 1.0
+    view["wpe"][...] = 0.0
+    view["wpe"][np.arange(NP), [(5 * t + 3) % V for t in range(NP)]] = 3.0
+    P = oracle.prepare_params(blob, s, "f32")
+    prompt = np.random.default_rng(40).integers(0, V, size=(2, 7))
+    toks, _ = oracle.generate_sample(P, prompt, 6, 1e-3, 99)
+    np.testing.assert_array_equal(toks, oracle.generate_greedy(P, prompt, 6))
+    # at a high temperature (logit gap about 8 here, so temperature 4) the
+    # draws are mostly not the arg-max, and a new seed changes them
+    t1, _ = oracle.generate_sample(P, prompt, 6, 4.0, 99)
+    t2, _ = oracle.generate_sample(P, prompt, 6, 4.0, 100)
+    assert (t1 != oracle.generate_greedy(P, prompt, 6)).any() and (t1 != t2).any()
