@@ -312,37 +312,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
 // ---------------------------------------------------------------- decode
 
-constexpr int kDecKeys = 256;  // keys per split block
+constexpr int kDecKeys = 256;  // keys per slice (256 threads)
+constexpr int kDecMaxSlices = 4;  // slices one fused block merges (1024 threads)
+constexpr int kDecFusedMinBH = 96;  // (b, h) pairs from which one block per pair fills the chip
 
-// One block per (bh, split) of up to 256 keys.  All global reads are 16-byte
-// coalesced runs: K rows are read 8 lanes per row (each lane a 16-byte chunk
-// of head_dim), V^T rows 32 lanes per row (each lane 8 consecutive keys).
-// Writes the partial (max, sum, o[HS]) of its split.
 template <typename T, int HS>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q,
-                                                                 const T* __restrict__ k,
-                                                                 const T* __restrict__ vt,
-                                                                 float* __restrict__ part, int n_keys,
-                                                                 int kvT, int nsplit) {
-  constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-  constexpr int KCH = HS / EPC;                     // chunks per K row
-  constexpr int ROWS_K = 256 / KCH;                 // K rows per pass
-  constexpr int VCH = kDecKeys / EPC;               // chunks per V^T row (256 keys)
-  constexpr int ROWS_V = 256 / VCH;                 // V^T rows per pass
+struct DecSlice {
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int KCH = HS / EPC;             // chunks per K row
+  static constexpr int ROWS_K = 256 / KCH;         // K rows per pass
+  static constexpr int VCH = kDecKeys / EPC;       // chunks per V^T row (256 keys)
+  static constexpr int ROWS_V = 256 / VCH;         // V^T rows per pass
+  static constexpr int PK = kDecKeys / ROWS_K, PV = HS / ROWS_V;
   static_assert(KCH >= 1 && KCH <= 64 && (KCH & (KCH - 1)) == 0, "K chunking");
-  __shared__ float sp[kDecKeys];
-  __shared__ float sred[8];
-  __shared__ float so[HS][VCH + 1];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
-  const int j0 = split * kDecKeys;
-  const int nj = min(kDecKeys, n_keys - j0);
+  float sp[kDecKeys];
+  float sred[8];
+  float so[HS][VCH + 1];
+};
 
-  // q chunk owned by this lane (fixed over passes)
-  const int kc = tid % KCH;
+// One slice of up to 256 keys [j0, j0 + nj) of one (b, h), taken by 256
+// threads (t = 0..255).  Every global read is a 16-byte coalesced run: K rows
+// are read KCH lanes per row (each lane a 16-byte chunk of head_dim), V^T rows
+// VCH lanes per row (each lane EPC consecutive keys).  All K loads of the
+// slice are issued at once; the first VP of its V^T passes go out with them
+// (their stream then overlaps the scores and the softmax), the rest after the
+// softmax.  VP = PV where registers are plentiful (the split kernel), 0 where
+// every block must be resident at once (the fused kernel: issuing part of
+// V^T early measured slower there than the occupancy it costs).  Returns the
+// slice maximum mx and sum ls (all threads) and o[t] = sum_j e^{s_j - mx}
+// v_j[t] (t < HS).
+template <typename T, int HS, int VP>
+__device__ __forceinline__ void decode_slice(const T* __restrict__ qrow, const T* __restrict__ kb,
+                                             const T* __restrict__ vb, int nj, int kvT, int t,
+                                             DecSlice<T, HS>& sm, float& mx_out, float& ls_out, float& o_out) {
+  using S = DecSlice<T, HS>;
+  constexpr int EPC = S::EPC, KCH = S::KCH, ROWS_K = S::ROWS_K, VCH = S::VCH, ROWS_V = S::ROWS_V;
+  constexpr int PK = S::PK, PV = S::PV;
+  static_assert(VP >= 0 && VP <= PV, "prefetched V passes");
+  const int lane = t & 63;
+  const int kc = t % KCH;
+  const int vc = t % VCH;
+  const bool chunk_ok = vc * EPC < nj;  // keys past nj have p = 0; unwritten chunks are not read
+  auto kload = [&](int p) {
+    const int r = p * ROWS_K + t / KCH;
+    return r < nj ? *reinterpret_cast<const u32x4_t*>(kb + (size_t)r * HS + kc * EPC) : u32x4_t{0, 0, 0, 0};
+  };
+  auto vload = [&](int p) {
+    const int d = p * ROWS_V + t / VCH;
+    return chunk_ok ? *reinterpret_cast<const u32x4_t*>(vb + (size_t)d * kvT + vc * EPC) : u32x4_t{0, 0, 0, 0};
+  };
+  u32x4_t kraw[PK], vraw[PV];
+#pragma unroll
+  for (int p = 0; p < PK; ++p) kraw[p] = kload(p);
+#pragma unroll
+  for (int p = 0; p < VP; ++p) vraw[p] = vload(p);
+  // q chunk owned by this lane
   float qv[EPC];
   {
-    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)bh * HS + kc * EPC);
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qrow + kc * EPC);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -356,13 +383,11 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
     }
   }
   // scores: pass p covers rows p*ROWS_K .. +ROWS_K; KCH lanes per row
-  const T* kb = k + ((size_t)bh * kvT + j0) * HS;
-#pragma unroll 4
-  for (int p = 0; p < kDecKeys / ROWS_K; ++p) {
-    const int r = p * ROWS_K + tid / KCH;
+  auto score = [&](int p) {
+    const int r = p * ROWS_K + t / KCH;
     float acc = 0.f;
     if (r < nj) {
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kb + (size_t)r * HS + kc * EPC);
+      const u32x4_t raw = kraw[p];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -374,35 +399,37 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
     }
 #pragma unroll
     for (int o = KCH / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (tid % KCH == 0) sp[r] = r < nj ? acc : -INFINITY;
-  }
+    if (t % KCH == 0) sm.sp[r] = r < nj ? acc : -INFINITY;
+  };
+#pragma unroll
+  for (int p = 0; p < PK; ++p) score(p);
   __syncthreads();
-  // block softmax over the split
-  const float s = sp[tid];
+  // softmax over the slice
+  const float s = sm.sp[t];
   float mx = wave_max(s);
-  if (lane == 0) sred[tid >> 6] = mx;
+  if (lane == 0) sm.sred[t >> 6] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
-  const float pv = tid < nj ? __builtin_amdgcn_exp2f((s - mx) * kLog2e) : 0.f;
+  mx = fmaxf(fmaxf(sm.sred[0], sm.sred[1]), fmaxf(sm.sred[2], sm.sred[3]));
+  const float pv = t < nj ? __builtin_amdgcn_exp2f((s - mx) * kLog2e) : 0.f;
   float ls = wave_sum(pv);
   __syncthreads();
-  sp[tid] = pv;
-  if (lane == 0) sred[4 + (tid >> 6)] = ls;
+  sm.sp[t] = pv;
+  if (lane == 0) sm.sred[4 + (t >> 6)] = ls;
   __syncthreads();
-  ls = sred[4] + sred[5] + sred[6] + sred[7];
+  ls = sm.sred[4] + sm.sred[5] + sm.sred[6] + sm.sred[7];
 
   // o[d] = sum_j p_j V^T[d][j0 + j]: lane owns chunk vc (EPC keys) of rows d
-  const int vc = tid % VCH;
+#pragma unroll
+  for (int p = VP; p < PV; ++p) vraw[p] = vload(p);
   float pk[EPC];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) pk[e] = sp[vc * EPC + e];
-  const T* vb = vt + (size_t)bh * HS * kvT + j0 + vc * EPC;
-  const bool chunk_ok = vc * EPC < nj;  // keys past nj have p = 0; skip unwritten chunks
-  for (int p = 0; p < HS / ROWS_V; ++p) {
-    const int d = p * ROWS_V + tid / VCH;
+  for (int e = 0; e < EPC; ++e) pk[e] = sm.sp[vc * EPC + e];
+#pragma unroll
+  for (int p = 0; p < PV; ++p) {
+    const int d = p * ROWS_V + t / VCH;
     float acc = 0.f;
     if (chunk_ok) {
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(vb + (size_t)d * kvT);
+      const u32x4_t raw = vraw[p];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -418,19 +445,82 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
         }
       }
     }
-    so[d][vc] = acc;
+    sm.so[d][vc] = acc;
   }
   __syncthreads();
-  float* dst = part + ((size_t)bh * nsplit + split) * (HS + 2);
-  if (tid < HS) {
-    float o = 0.f;
+  float o = 0.f;
+  if (t < HS) {
 #pragma unroll 8
-    for (int c = 0; c < VCH; ++c) o += so[tid][c];
-    dst[tid] = o;
+    for (int c = 0; c < VCH; ++c) o += sm.so[t][c];
   }
+  mx_out = mx;
+  ls_out = ls;
+  o_out = o;
+}
+
+// One block per (bh, split) of up to 256 keys; writes the partial
+// (o[HS], max, sum) of its split for attn_decode_merge_kernel.
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q,
+                                                                 const T* __restrict__ k,
+                                                                 const T* __restrict__ vt,
+                                                                 float* __restrict__ part, int n_keys,
+                                                                 int kvT, int nsplit) {
+  __shared__ DecSlice<T, HS> sm;
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+  const int j0 = split * kDecKeys;
+  const int nj = min(kDecKeys, n_keys - j0);
+  float mx, ls, o;
+  constexpr int VP = sizeof(T) == 2 ? DecSlice<T, HS>::PV : 0;  // fp32 head_dim 64: too many registers
+  decode_slice<T, HS, VP>(q + (size_t)bh * HS, k + ((size_t)bh * kvT + j0) * HS,
+                          vt + (size_t)bh * HS * kvT + j0, nj, kvT, tid, sm, mx, ls, o);
+  float* dst = part + ((size_t)bh * nsplit + split) * (HS + 2);
+  if (tid < HS) dst[tid] = o;
   if (tid == 0) {
     dst[HS] = mx;
     dst[HS + 1] = ls;
+  }
+}
+
+// One block per (b, h) for up to kDecMaxSlices slices: 256 threads per slice,
+// the slices' (o, max, sum) merged in LDS by the same formula as
+// attn_decode_merge_kernel, so the result is the same bits as the split +
+// merge pair, in one launch and without the partials' round trip.
+template <typename T, int HS>
+__global__ __launch_bounds__(256 * kDecMaxSlices) __attribute__((amdgpu_waves_per_eu(8))) void attn_decode_fused_kernel(const T* __restrict__ q,
+                                                                                const T* __restrict__ k,
+                                                                                const T* __restrict__ vt,
+                                                                                T* __restrict__ out, int n_keys,
+                                                                                int kvT, int H) {
+  __shared__ DecSlice<T, HS> sm[kDecMaxSlices];
+  __shared__ float so[kDecMaxSlices][HS + 2];
+  const int nsl = (int)blockDim.x / kDecKeys;
+  const int slice = threadIdx.x / kDecKeys, t = threadIdx.x % kDecKeys;
+  const int bh = blockIdx.x;
+  const int j0 = slice * kDecKeys;
+  const int nj = min(kDecKeys, n_keys - j0);
+  float mx, ls, o;
+  decode_slice<T, HS, 0>(q + (size_t)bh * HS, k + ((size_t)bh * kvT + j0) * HS,
+                             vt + (size_t)bh * HS * kvT + j0, nj, kvT, t, sm[slice], mx, ls, o);
+  if (t < HS) so[slice][t] = o;
+  if (t == 0) {
+    so[slice][HS] = mx;
+    so[slice][HS + 1] = ls;
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  if (d < HS) {
+    float M = -INFINITY;
+    for (int s = 0; s < nsl; ++s) M = fmaxf(M, so[s][HS]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsl; ++s) {
+      const float w = __builtin_amdgcn_exp2f((so[s][HS] - M) * kLog2e);
+      den += w * so[s][HS + 1];
+      num += w * so[s][d];
+    }
+    const int b = bh / H, h = bh - b * H;
+    out[(size_t)b * H * HS + h * HS + d] = Elem<T>::from_f32(num / den);
   }
 }
 
@@ -481,16 +571,34 @@ template <typename T>
 hipError_t launch_attention_decode(const T* q, const T* k, const T* vt, T* out, float* part, int B, int H,
                                    int n_keys, int kvT, int hs, hipStream_t stream) {
   const int nsplit = (n_keys + kDecKeys - 1) / kDecKeys;
+  if (n_keys < 1 || nsplit * kDecKeys > 4096 || (hs != 64 && hs != 16)) return hipErrorInvalidValue;
+  // Enough (b, h) pairs to fill the chip with one block each: the fused
+  // kernel (no partials, no merge launch).  Otherwise, or past
+  // kDecMaxSlices slices, one block per slice and a merge launch.
+  // (fp32 with head_dim 64 holds too many K chunks for two 1024-thread blocks per CU.)
+  const bool fused = nsplit <= kDecMaxSlices && B * H >= kDecFusedMinBH;
   if (hs == 64) {
-    hipLaunchKernelGGL((attn_decode_split_kernel<T, 64>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
-                       part, n_keys, kvT, nsplit);
-    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 64>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
-  } else if (hs == 16) {
-    hipLaunchKernelGGL((attn_decode_split_kernel<T, 16>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
-                       part, n_keys, kvT, nsplit);
-    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 16>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
+    if constexpr (sizeof(T) == 2) {
+      if (fused) {
+        hipLaunchKernelGGL((attn_decode_fused_kernel<T, 64>), dim3(B * H), dim3(kDecKeys * nsplit), 0, stream, q,
+                           k, vt, out, n_keys, kvT, H);
+        return hipGetLastError();
+      }
+    }
+    {
+      hipLaunchKernelGGL((attn_decode_split_kernel<T, 64>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
+                         part, n_keys, kvT, nsplit);
+      hipLaunchKernelGGL((attn_decode_merge_kernel<T, 64>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
+    }
   } else {
-    return hipErrorInvalidValue;
+    if (fused) {
+      hipLaunchKernelGGL((attn_decode_fused_kernel<T, 16>), dim3(B * H), dim3(kDecKeys * nsplit), 0, stream, q, k,
+                         vt, out, n_keys, kvT, H);
+    } else {
+      hipLaunchKernelGGL((attn_decode_split_kernel<T, 16>), dim3(B * H * nsplit), dim3(256), 0, stream, q, k, vt,
+                         part, n_keys, kvT, nsplit);
+      hipLaunchKernelGGL((attn_decode_merge_kernel<T, 16>), dim3(B * H), dim3(64), 0, stream, part, out, H, nsplit);
+    }
   }
   return hipGetLastError();
 }

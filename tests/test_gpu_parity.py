@@ -274,6 +274,29 @@ def test_decode_small_shapes(dtype, Bsz):
         assert_logits(lg, ref_all[:, Pn + i], dtype, f"decode step {i}")
 
 
+@pytest.mark.parametrize("dtype,d_model,n_head,Pn", [("bf16", 128, 2, 600), ("f32", 64, 4, 700)])
+def test_decode_many_heads_sliced_keys(dtype, d_model, n_head, Pn):
+    """At least 96 (sequence, head) pairs: decode attention takes one block per
+    pair and merges its 256-key slices in LDS.  Prefixes of 600 / 700 keys give
+    three slices with a ragged last one; the steps must match the oracle."""
+    Bsz = 48
+    _announce(f"decode sliced keys dtype={dtype} D={d_model} H={n_head} B={Bsz} prefix={Pn}")
+    s = W.ModelShape(vocab=600, n_positions=1024, d_model=d_model, n_head=n_head, n_layer=2, d_ff=4 * d_model)
+    blob = W.make_params(s, _init_small(0.08), 15)
+    steps, max_T = 2, Pn + 8
+    rng = np.random.default_rng(16)
+    ids = rng.integers(0, 600, size=(Bsz, Pn + steps)).astype(np.int32)
+    m = _model(s, dtype, Bsz, Pn, blob)
+    kv = m.new_kv_cache(Bsz, max_T)
+    m.forward(_ids_dev(ids[:, :Pn]), logits=False, kv=kv)
+    sel = [0, 17, 47]
+    P = oracle.prepare_params(blob, s, dtype)
+    ref_all = oracle.forward(P, ids[sel])
+    for i in range(steps):
+        lg = m.decode_step(kv, _ids_dev(ids[:, Pn + i])).float().cpu().numpy()
+        assert_logits(lg[sel], ref_all[:, Pn + i], dtype, f"sliced decode step {i}")
+
+
 def test_decode_capacity_error():
     from gpt_pre_ln_amd import binding
     s = W.ModelShape(vocab=100, n_positions=64, d_model=64, n_head=1, n_layer=1, d_ff=256)
