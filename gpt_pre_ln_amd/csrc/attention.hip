@@ -333,12 +333,13 @@ struct DecSlice {
 // One slice of up to 256 keys [j0, j0 + nj) of one (b, h), taken by 256
 // threads (t = 0..255).  Every global read is a 16-byte coalesced run: K rows
 // are read KCH lanes per row (each lane a 16-byte chunk of head_dim), V^T rows
-// VCH lanes per row (each lane EPC consecutive keys).  All K loads of the
-// slice are issued at once; the first VP of its V^T passes go out with them
-// (their stream then overlaps the scores and the softmax), the rest after the
-// softmax.  VP = PV where registers are plentiful (the split kernel), 0 where
-// every block must be resident at once (the fused kernel: issuing part of
-// V^T early measured slower there than the occupancy it costs).  Returns the
+// VCH lanes per row (each lane EPC consecutive keys).  q and all K loads of
+// the slice are issued at once, the first VP of its V^T passes with them
+// (their stream then overlaps the scores and the softmax), the rest after
+// the softmax.  VP = PV where registers are plentiful (the split kernel), 0
+// where every block must be resident at once (the fused kernel).  Measured
+// and not kept: half of V^T by LDS DMA in the fused kernel (the compiler
+// then waits for every load in flight at the first use of any).  Returns the
 // slice maximum mx and sum ls (all threads) and o[t] = sum_j e^{s_j - mx}
 // v_j[t] (t < HS).
 template <typename T, int HS, int VP>
@@ -348,54 +349,55 @@ __device__ __forceinline__ void decode_slice(const T* __restrict__ qrow, const T
   using S = DecSlice<T, HS>;
   constexpr int EPC = S::EPC, KCH = S::KCH, ROWS_K = S::ROWS_K, VCH = S::VCH, ROWS_V = S::ROWS_V;
   constexpr int PK = S::PK, PV = S::PV;
-  static_assert(VP >= 0 && VP <= PV, "prefetched V passes");
+  static_assert(VP >= 0 && VP <= PV, "V passes in flight early");
   const int lane = t & 63;
   const int kc = t % KCH;
   const int vc = t % VCH;
-  const bool chunk_ok = vc * EPC < nj;  // keys past nj have p = 0; unwritten chunks are not read
+  const bool chunk_ok = vc * EPC < nj;  // the chunk holds a key before nj
+  // Every load is unconditional (branch-free, so the compiler can count the
+  // loads in flight exactly): rows past the last key read the last key's row
+  // (its score is masked), chunks wholly past it the row's first chunk (its
+  // probabilities are zero and the values are not used).
   auto kload = [&](int p) {
-    const int r = p * ROWS_K + t / KCH;
-    return r < nj ? *reinterpret_cast<const u32x4_t*>(kb + (size_t)r * HS + kc * EPC) : u32x4_t{0, 0, 0, 0};
+    const int r = min(p * ROWS_K + t / KCH, nj - 1);
+    return *reinterpret_cast<const u32x4_t*>(kb + (size_t)r * HS + kc * EPC);
   };
+  const int vcol = chunk_ok ? vc * EPC : 0;
   auto vload = [&](int p) {
     const int d = p * ROWS_V + t / VCH;
-    return chunk_ok ? *reinterpret_cast<const u32x4_t*>(vb + (size_t)d * kvT + vc * EPC) : u32x4_t{0, 0, 0, 0};
+    return *reinterpret_cast<const u32x4_t*>(vb + (size_t)d * kvT + vcol);
   };
   u32x4_t kraw[PK], vraw[PV];
+  const u32x4_t qraw = *reinterpret_cast<const u32x4_t*>(qrow + kc * EPC);
 #pragma unroll
   for (int p = 0; p < PK; ++p) kraw[p] = kload(p);
 #pragma unroll
   for (int p = 0; p < VP; ++p) vraw[p] = vload(p);
-  // q chunk owned by this lane
   float qv[EPC];
-  {
-    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qrow + kc * EPC);
-    if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[2 * e] = bf16_to_f32(raw[e] & 0xFFFF);
-        qv[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
-      }
-    } else {
-      const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qv[e] = f[e];
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_to_f32(qraw[e] & 0xFFFF);
+      qv[2 * e + 1] = bf16_to_f32(qraw[e] >> 16);
     }
+  } else {
+    const f32x4_t f = __builtin_bit_cast(f32x4_t, qraw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[e] = f[e];
   }
   // scores: pass p covers rows p*ROWS_K .. +ROWS_K; KCH lanes per row
+  // (computed for every row, masked after: no branch around a use of a load)
   auto score = [&](int p) {
     const int r = p * ROWS_K + t / KCH;
     float acc = 0.f;
-    if (r < nj) {
-      const u32x4_t raw = kraw[p];
-      if constexpr (sizeof(T) == 2) {
+    const u32x4_t raw = kraw[p];
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc += qv[2 * e] * bf16_to_f32(raw[e] & 0xFFFF) + qv[2 * e + 1] * bf16_to_f32(raw[e] >> 16);
-      } else {
+      for (int e = 0; e < 4; ++e)
+        acc += qv[2 * e] * bf16_to_f32(raw[e] & 0xFFFF) + qv[2 * e + 1] * bf16_to_f32(raw[e] >> 16);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += qv[e] * __builtin_bit_cast(f32x4_t, raw)[e];
-      }
+      for (int e = 0; e < 4; ++e) acc += qv[e] * __builtin_bit_cast(f32x4_t, raw)[e];
     }
 #pragma unroll
     for (int o = KCH / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -424,29 +426,31 @@ __device__ __forceinline__ void decode_slice(const T* __restrict__ qrow, const T
   float pk[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) pk[e] = sm.sp[vc * EPC + e];
+  // (every element past the last key is selected to 0, its probability is 0:
+  // no branch around a use of a load)
+  float accv[PV];
 #pragma unroll
   for (int p = 0; p < PV; ++p) {
-    const int d = p * ROWS_V + t / VCH;
     float acc = 0.f;
-    if (chunk_ok) {
-      const u32x4_t raw = vraw[p];
-      if constexpr (sizeof(T) == 2) {
+    const u32x4_t raw = vraw[p];
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = vc * EPC + 2 * e < nj ? bf16_to_f32(raw[e] & 0xFFFF) : 0.f;
-          const float v1 = vc * EPC + 2 * e + 1 < nj ? bf16_to_f32(raw[e] >> 16) : 0.f;
-          acc += pk[2 * e] * v0 + pk[2 * e + 1] * v1;
-        }
-      } else {
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = vc * EPC + 2 * e < nj ? bf16_to_f32(raw[e] & 0xFFFF) : 0.f;
+        const float v1 = vc * EPC + 2 * e + 1 < nj ? bf16_to_f32(raw[e] >> 16) : 0.f;
+        acc += pk[2 * e] * v0 + pk[2 * e + 1] * v1;
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = vc * EPC + e < nj ? __builtin_bit_cast(f32x4_t, raw)[e] : 0.f;
-          acc += pk[e] * v0;
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = vc * EPC + e < nj ? __builtin_bit_cast(f32x4_t, raw)[e] : 0.f;
+        acc += pk[e] * v0;
       }
     }
-    sm.so[d][vc] = acc;
+    accv[p] = acc;
   }
+#pragma unroll
+  for (int p = 0; p < PV; ++p) sm.so[p * ROWS_V + t / VCH][vc] = accv[p];
   __syncthreads();
   float o = 0.f;
   if (t < HS) {
