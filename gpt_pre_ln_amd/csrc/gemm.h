@@ -386,6 +386,15 @@ template <typename T>
 hipError_t launch_gemm_splitk(GemmTile tile, const T* A, const T* B, int M, int N, int K_split, int lda, int ldb,
                               int splits, const EpiStore<float>& epi, hipStream_t stream);
 
+// Both operands K-major (bf16): C[m][n] = sum_k A[k][m] B[k][n] with A
+// [K][M] (row stride lda) and B [K][N] (row stride ldb), e.g. a weight
+// gradient X^T dY straight from the activations as the forward stored them,
+// no transposed copies.  128x128 tiles; split-K as launch_gemm_splitk (slice
+// y covers rows [y*K_split, (y+1)*K_split) of A and B).  M, N, lda, ldb
+// multiples of 8 (whole 16-byte chunks), K_split a multiple of 64.
+hipError_t launch_gemm_kmajor(const bf16_t* A, const bf16_t* B, int M, int N, int K_split, int lda, int ldb,
+                              int splits, const EpiStore<float>& epi, hipStream_t stream);
+
 // M <= 32 (decode): one kernel for the product and the fused epilogue `epi`;
 // K % 32 == 0 (bf16) or K % 16 == 0 (fp32), no workspace.
 template <typename T, class Epi>

@@ -110,6 +110,17 @@ def test_block_backward_matches_oracle(case):
     _compare(s, dtype, blob, x, dy, dx, g, layer, f"{case}")
 
 
+@pytest.mark.parametrize("D,H,B,T", [(128, 2, 2, 640), (192, 3, 1, 1088)])
+def test_block_backward_kmajor_weight_gradients(D, H, B, T):
+    """bf16 with B*T a multiple of 64 and k-loops over 1024 positions: the
+    weight gradients read the activations K-major (no transposed copies),
+    with split-K slices; d_model 192 leaves partial 128-wide tiles."""
+    _announce(f"block backward K-major bf16 D={D} H={H} B={B} T={T}")
+    s = W.ModelShape(vocab=300, n_positions=2048, d_model=D, n_head=H, n_layer=1, d_ff=4 * D)
+    blob, x, dy, dx, g = _run(s, "bf16", B, T, 0, 850 + D + T)
+    _compare(s, "bf16", blob, x, dy, dx, g, 0, f"K-major D={D} B={B} T={T}")
+
+
 def test_block_backward_gpt2_small():
     """GPT-2 small shapes: B=8 T=1024 (the benchmark batch; the weight
     gradients take the split-K products, 4 to 16 slices), dx and every
