@@ -95,21 +95,22 @@ TRAFFIC_KERNELS = {"lm_head_gemm": r"void gemm_kernel<bf16_t, 256, 256, 2, 4, 2,
 def measured_traffic(workload, cls):
     """HBM bytes per dispatch of the kernel (read + write) from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is none for
-    this workload or the kernel sources changed since the counters were taken."""
+    this workload or the sources that kernel is built from changed since the
+    counters were taken (each entry carries the hash of its own sources)."""
     import hashlib
+    import re
     path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('gpt2-', 'gpt2_').replace('-', '_')}.json")
     if not os.path.exists(path) or cls not in TRAFFIC_KERNELS:
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])).hexdigest()[:16]
-    if h != rec["source_hash"]:
-        return None
-    import re
     hits = [v for k, v in rec["per_dispatch"].items() if re.fullmatch(TRAFFIC_KERNELS[cls], k)]
-    if len(hits) != 1:
+    if len(hits) != 1 or "sources" not in hits[0]:
         return None
     entry = hits[0]
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read() for p in entry["sources"])).hexdigest()[:16]
+    if h != entry["source_hash"]:
+        return None
     return round(entry["read_bytes"] + entry["write_bytes"])
 
 
