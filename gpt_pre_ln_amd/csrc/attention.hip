@@ -1,7 +1,9 @@
 // Causal attention on gfx950 (see attention.h for what is computed).
 //
 // Prefill kernel (flash-style):
-//   * one block = 4 waves = 128 queries of one (b, h); blocks of the longest
+//   * one block = 4 waves of QW queries (kPrefillQW = 16: 64 queries, 92
+//     registers, 5 waves per SIMD; 32 queries per wave took 156 registers and
+//     3 waves per SIMD, 1.5 % slower) of one (b, h); blocks of the longest
 //     query tiles are launched first (causal work grows with the tile index).
 //   * key tiles of 64 keys are staged in LDS (K as [key][d], V transposed as
 //     [d][key]) through a double-buffered ring; the next tile's global loads
@@ -45,11 +47,11 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int HS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_prefill_kernel(
+template <typename T, int HS, int QW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 5 : 3))) void attn_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, T* __restrict__ out, int BH, int H,
     int Tq, int kvT, int n_qtiles, float* __restrict__ lse) {
-  constexpr int QW = 32, NW = 4, BQ = QW * NW, BKEYS = 64;
+  constexpr int NW = 4, BQ = QW * NW, BKEYS = 64;
   constexpr int ESZ = (int)sizeof(T);
   constexpr int KROWB = HS * ESZ, KCH = KROWB / 16;     // K tile rows (keys)
   constexpr int VROWB = BKEYS * ESZ, VCH = VROWB / 16;  // V^T tile rows (d)
@@ -549,16 +551,19 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const float* __re
 
 }  // namespace
 
+constexpr int kPrefillQW = 16;  // queries per wave (see the kernel's notes)
+
 template <typename T>
 hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out, int B, int H, int Tq,
                                     int kvT, int hs, hipStream_t stream, float* lse) {
-  const int n_qtiles = (Tq + 127) / 128;
+  constexpr int QW = kPrefillQW;
+  const int n_qtiles = (Tq + 4 * QW - 1) / (4 * QW);
   dim3 grid(B * H * n_qtiles), block(256);
   if (hs == 64) {
-    hipLaunchKernelGGL((attn_prefill_kernel<T, 64>), grid, block, 0, stream, q, k, vt, out, B * H, H, Tq, kvT,
+    hipLaunchKernelGGL((attn_prefill_kernel<T, 64, QW>), grid, block, 0, stream, q, k, vt, out, B * H, H, Tq, kvT,
                        n_qtiles, lse);
   } else if (hs == 16 && sizeof(T) == 4) {
-    hipLaunchKernelGGL((attn_prefill_kernel<T, (sizeof(T) == 4 ? 16 : 64)>), grid, block, 0, stream, q, k,
+    hipLaunchKernelGGL((attn_prefill_kernel<T, (sizeof(T) == 4 ? 16 : 64), QW>), grid, block, 0, stream, q, k,
                        vt, out, B * H, H, Tq, kvT, n_qtiles, lse);
   } else {
     return hipErrorInvalidValue;
