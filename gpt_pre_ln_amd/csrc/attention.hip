@@ -201,16 +201,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 
     if (key0 <= q0w + QW - 1) {  // wave-uniform: otherwise the whole tile is masked for this wave
       // S^T = K Q^T: lane holds S^T[key = key0 + key_of_row(kf*16 + 4*lg + e)][query = q0w + qf*16 + lr]
       f32x4_t s[KF][QF];
+      u32x4_t kfr[NSLAB][KF];
+#pragma unroll
+      for (int sl = 0; sl < NSLAB; ++sl)
+#pragma unroll
+        for (int kf = 0; kf < KF; ++kf) {
+          const int row = kf * 16 + lr;
+          kfr[sl][kf] = sK[buf][row * KCH + swz_ch<KCH>(row, sl * 4 + lg)];
+        }
 #pragma unroll
       for (int sl = 0; sl < NSLAB; ++sl) {
 #pragma unroll
         for (int kf = 0; kf < KF; ++kf) {
-          const int row = kf * 16 + lr;
-          const u32x4_t kfr = sK[buf][row * KCH + swz_ch<KCH>(row, sl * 4 + lg)];
 #pragma unroll
           for (int qf = 0; qf < QF; ++qf) {
             if (sl == 0) s[kf][qf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            Mma<T>::run(s[kf][qf], kfr, qfrag[qf][sl]);
+            Mma<T>::run(s[kf][qf], kfr[sl][kf], qfrag[qf][sl]);
           }
         }
       }
@@ -224,6 +230,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 
             for (int e = 0; e < 4; ++e)
               if (key_of_row(kf * 16 + 4 * lg + e) > lim) s[kf][qf][e] = -INFINITY;
         }
+      }
+      // V^T fragments of the first matrix step, read now: their LDS latency
+      // then passes under the softmax arithmetic below
+      constexpr int NPRE = DF >= 2 ? DF / 2 : 1;
+      u32x4_t vpre[NPRE];
+#pragma unroll
+      for (int df = 0; df < NPRE; ++df) {
+        const int d = df * 16 + lr;
+        vpre[df] = sV[buf][d * VCH + swz_ch<VCH>(d, lg)];
       }
       // tile maximum per query: 16 values in the lane, then across the four
       // lanes (lr, lr+16, lr+32, lr+48) that hold the same query
@@ -275,14 +290,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 
           }
           Mma<T>::run(lsum[qf], ones, pf[qf]);
         }
+        u32x4_t vf[DF];
 #pragma unroll
         for (int df = 0; df < DF; ++df) {
           const int d = df * 16 + lr;
           // bf16: keys st*32 + 8*lg .. +7; fp32: keys st*16 + 4*lg .. +3 (16 bytes)
-          const u32x4_t vf = sV[buf][d * VCH + swz_ch<VCH>(d, st * 4 + lg)];
-#pragma unroll
-          for (int qf = 0; qf < QF; ++qf) Mma<T>::run(o[df][qf], vf, pf[qf]);
+          vf[df] = st == 0 && df < NPRE ? vpre[df < NPRE ? df : 0] : sV[buf][d * VCH + swz_ch<VCH>(d, st * 4 + lg)];
         }
+#pragma unroll
+        for (int df = 0; df < DF; ++df)
+#pragma unroll
+          for (int qf = 0; qf < QF; ++qf) Mma<T>::run(o[df][qf], vf[df], pf[qf]);
       }
     }
     if (kt + 1 < n_kt) {

@@ -60,6 +60,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Staged reads the row-mode epilogue keeps in flight at once.
+constexpr int kEpiBatch = 4;
+
 // Map the linear block id to a (tile_m, tile_n) pair: XCD-contiguous ranges,
 // then GROUP_M tile-rows per group with tile_m varying fastest.
 __device__ __forceinline__ void tile_of_block(int ntm, int ntn, int& tm, int& tn) {
@@ -396,6 +399,24 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
         static_assert(R % RPW == 0, "whole rows per store instruction");
         const int c2 = (lane % LPR) * 2;
         const int n = nw + c2 * 4;
+        if (mr + R <= M && nw + WTN <= N) {
+          // whole round inside C (uniform): staged reads in batches, as below
+          constexpr int NQ8 = R / RPW, G = NQ8 < kEpiBatch ? NQ8 : kEpiBatch;
+          static_assert(NQ8 % G == 0, "whole batches");
+#pragma unroll
+          for (int q0 = 0; q0 < NQ8; q0 += G) {
+            f32x4_t v0[G], v1[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const int r = (q0 + g) * RPW + lane / LPR;
+              v0[g] = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c2) << 2));
+              v1[g] = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c2 + 1) << 2));
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) epi.apply8(mr + (q0 + g) * RPW + lane / LPR, n, v0[g], v1[g]);
+          }
+          continue;
+        }
 #pragma unroll
         for (int q = 0; q < R / RPW; ++q) {
           const int r = q * RPW + lane / LPR;
@@ -416,14 +437,49 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
           pre[q] = epi.preload(min(mr + min(q * RPI + lane / CPR, R - 1), M - 1), min(n, N - 4));
+        asm volatile("" ::: "memory");  // every preload issued before the first store
       }
+      if constexpr (RPI * CPR == 64 && NQ * RPI == R) {
+        // the wave's rows and columns of this round all inside C (uniform):
+        // no per-lane conditions, so the staged reads go out in batches of
+        // kEpiBatch and their latency is paid once per batch
+        if (mr + R <= M && nw + WTN <= N) {
+          constexpr int G = NQ < kEpiBatch ? NQ : kEpiBatch;
+          static_assert(NQ % G == 0, "whole batches");
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int r = q * RPI + lane / CPR;
-        if (!lane_on || r >= R) continue;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c) << 2));
-        const int m = mr + r;
-        if (m < M && n < N) epi.apply(m, n, v, pre[q]);
+          for (int q0 = 0; q0 < NQ; q0 += G) {
+            f32x4_t v[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const int r = (q0 + g) * RPI + lane / CPR;
+              v[g] = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c) << 2));
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) epi.apply(mr + (q0 + g) * RPI + lane / CPR, n, v[g], pre[q0 + g]);
+          }
+          continue;
+        }
+      }
+      // Otherwise the same batches with the per-lane tests on the stores
+      // only (rows past the round clamped to its last row).
+      constexpr int G = NQ < kEpiBatch ? NQ : kEpiBatch;
+#pragma unroll
+      for (int q0 = 0; q0 < NQ; q0 += G) {
+        f32x4_t v[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (q0 + g >= NQ) break;
+          const int r = min((q0 + g) * RPI + lane / CPR, R - 1);
+          v[g] = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c) << 2));
+        }
+        asm volatile("" ::: "memory");  // keeps the batch's reads from sinking into the stores' branches
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (q0 + g >= NQ) break;
+          const int r = (q0 + g) * RPI + lane / CPR;
+          const int m = mr + r;
+          if (lane_on && r < R && m < M && n < N) epi.apply(m, n, v[g], pre[q0 + g]);
+        }
       }
     } else {
       // column-major [WTN][R] with chunk c of column n at slot c ^ (n % CPT)
@@ -437,13 +493,23 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
             stg[col * R + (((r >> 2) ^ (col & (CPT - 1))) << 2) + (r & 3)] = acc[rd * (R / 16) + i][j][e];
           }
       constexpr int CPI = 64 / CPT;  // columns per read instruction
+      constexpr int NQT = WTN / CPI, GT = NQT < kEpiBatch ? NQT : kEpiBatch;
+      static_assert(NQT % GT == 0, "whole batches");
       const int c = lane % CPT;
 #pragma unroll
-      for (int q = 0; q < WTN / CPI; ++q) {
-        const int col = q * CPI + lane / CPT;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + col * R + ((c ^ (col & (CPT - 1))) << 2));
-        const int m = mr + c * 4, n = nw + col;
-        if (m < M && n < N) epi.apply_t(m, n, v);
+      for (int q0 = 0; q0 < NQT; q0 += GT) {
+        f32x4_t v[GT];
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const int col = (q0 + g) * CPI + lane / CPT;
+          v[g] = *reinterpret_cast<const f32x4_t*>(stg + col * R + ((c ^ (col & (CPT - 1))) << 2));
+        }
+        asm volatile("" ::: "memory");  // as in row mode: the batch's reads stay together
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          const int m = mr + c * 4, n = nw + (q0 + g) * CPI + lane / CPT;
+          if (m < M && n < N) epi.apply_t(m, n, v[g]);
+        }
       }
     }
   }
