@@ -481,314 +481,281 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
 }
 
 // ----------------------------------------------------------- bf16, matrix cores
-// Head size 64, 64 x 64 tiles, 4 waves.  R = X Y^T on 16 x 16 blocks with
-// v_mfma_f32_16x16x32_bf16 (Mma<bf16_t>::run(acc, X, Y)): lane l supplies
-// X[l % 16][8 (l / 16) .. +7] and Y[l % 16][8 (l / 16) .. +7] (16 bytes of a
-// row whose contraction index is contiguous) and receives
-// R[4 (l / 16) + e][l % 16], e = 0..3.  Every operand therefore lives in LDS
-// with its contraction index contiguous: Q, dO, K, V as [row][d] and the
-// transposed copies Q^T, dO^T, K^T as [d][row]; P and dS are written by the
-// wave that computed them in the layout of the product that reads them.
-constexpr int kLdsRow = 64 + 8;  // bf16 per LDS row (16 bytes of padding)
+// Head size 64.  Each 64-row operand tile (Q, dO, K: rows of 64 d; V^T: rows
+// of 64 keys) sits in LDS as 64 rows of 128 bytes, 16-byte chunk c of row r
+// at slot c ^ (r & 7), filled by global_load_lds (one wave instruction = 8
+// rows).  Fragments whose contraction index runs along a tile row are plain
+// 16-byte reads; fragments whose contraction index runs down the rows are
+// read with ds_read_b64_tr_b16 (tr_frag).  The probabilities P and dS stay
+// in the registers of the MFMA that produced them: lane (lr, lg) of
+// R = X Y^T holds R[4 lg + e][lr], and two 16-row blocks b, b + 1 give it
+// rows 16 b + 4 lg + e and 16 (b + 1) + 4 lg + e -- the eight contraction
+// slots 8 lg .. 8 lg + 7 of the next product, in the order pslot() names;
+// the other operand of that product is read in the same order.
+constexpr int kTileBytes = kBT * 128;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-struct alignas(16) MmaTile {
-  bf16_t a[kBT][kLdsRow];
-};
-
-__device__ __forceinline__ u32x4_t frag(const MmaTile& t, int row, int k8) {
-  return *reinterpret_cast<const u32x4_t*>(&t.a[row][k8]);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_bwd() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Row-major copy ([row][d], 16-byte chunks) and, optionally, the transposed
-// copy ([d][row]) of 64 rows of 64 bf16 from global rows src + r * ld, rows
-// past `valid` zero.
-// A 64 x 64 bf16 tile held in registers between its global read and its LDS
-// write, so the next tile's reads can be in flight while the current tile is
-// computed.  256 threads, two 16-byte chunks each: thread t holds elements
-// 8 (t % 8) .. +7 of rows 2 (t / 8) and 2 (t / 8) + 1, so that the transposed
-// copy takes one 4-byte LDS write per element pair of the two rows.
-struct TileRegs {
-  u32x4_t v[2];
-};
-static_assert(kBT * 8 == 2 * 256, "two 16-byte chunks per thread");
+__device__ __forceinline__ int pslot_row(int s2, int lg, int h) { return 32 * s2 + 16 * h + 4 * lg; }
 
-__device__ __forceinline__ void fetch_rows_bf16(TileRegs& g, const bf16_t* src, size_t ld, int valid) {
-  const int r0 = 2 * (threadIdx.x >> 3), d8 = (threadIdx.x & 7) * 8;
+__device__ __forceinline__ u32x4_t plain_frag(const char* tile, int row, int chunk) {
+  return *reinterpret_cast<const u32x4_t*>(tile + row * 128 + ((chunk ^ (row & 7)) << 4));
+}
+
+// Four consecutive tile rows row0 .. row0 + 3 of column nb + lr (16-lane
+// group semantics of ds_read_b64_tr_b16: lane l names row row0 + l / 4,
+// columns nb + 4 (l % 4) .. +3; lane j receives X[row0 + t][nb + j]).
+__device__ __forceinline__ u32x2_t tr4(const char* tile, int row0, int nb, int lr) {
+  const int row = row0 + (lr >> 2), col = nb + 4 * (lr & 3);
+  const char* addr = tile + row * 128 + (((col >> 3) ^ (row & 7)) << 4) + ((col >> 2) & 1) * 8;
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(const_cast<char*>(addr)));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Fragment of column nb + lr over the rows r0 + t and r1 + t (t = 0..3).
+__device__ __forceinline__ u32x4_t tr_frag(const char* tile, int r0, int r1, int nb, int lr) {
+  const u32x2_t a = tr4(tile, r0, nb, lr), b = tr4(tile, r1, nb, lr);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// 64 rows of 128 bytes into a swizzled LDS tile: wave instruction j of 2
+// fills slots (2 w + j) * 64 + lane.  Source row r is src + min(r, last) * ld.
+__device__ __forceinline__ void dma_tile(char* tile, const bf16_t* src, size_t ld, int last) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (r0 + j < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(src + (size_t)(r0 + j) * ld + d8);
+    const int si = (2 * w + j) * 64 + lane, row = si >> 3, c = (si & 7) ^ (row & 7);
+    const bf16_t* g = src + (size_t)min(row, last) * ld + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (__attribute__((address_space(3))) void*)(tile + (2 * w + j) * 1024), 16, 0, 0);
   }
 }
 
-// Rows as [row][d] into t and, when tt is given, transposed as [d][row].
-__device__ __forceinline__ void put_rows_bf16(MmaTile& t, MmaTile* tt, const TileRegs& g) {
-  const int r0 = 2 * (threadIdx.x >> 3), d8 = (threadIdx.x & 7) * 8;
+// dK and dV of one key tile (64 keys): wave w owns keys 16 w .. 16 w + 15,
+// whose K and V rows it keeps as MFMA operands in registers.  Per query
+// tile at or after it (Q and dO tiles double-buffered in LDS): S and dP of
+// the 64 queries against the wave's keys, P = exp(S - lse) and
+// dS = P (dP - dvec) (selected to 0 where the key follows the query or the
+// query is past the end), then dV^T += dO^T P and dK^T += Q^T dS.
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_reg_kernel(const bf16_t* __restrict__ q,
+                                                                  const bf16_t* __restrict__ k,
+                                                                  const bf16_t* __restrict__ vt,
+                                                                  const bf16_t* __restrict__ dout,
+                                                                  const float* __restrict__ lse,
+                                                                  const float* __restrict__ dvec,
+                                                                  float* __restrict__ dqkv, int BH, int H,
+                                                                  int T_seq, int kvT, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) char sQ[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sO[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float sL[2][kBT];
+  __shared__ __attribute__((aligned(16))) float sD[2][kBT];
+  const int kt = blockIdx.x / BH, bh = blockIdx.x - kt * BH;  // key tile 0 (the longest) first
+  const int b = bh / H, h = bh - b * H;
+  const int j0 = kt * kBT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int Dm = H * 64;
+  const int key = j0 + 16 * w + lr;  // this lane's key (column of every S block)
+
+  // V^T tile of the key tile -> V rows of the wave's keys (through sQ[1],
+  // free until the second query tile); K rows straight from global.
+  dma_tile(sQ[1], vt + (size_t)bh * 64 * kvT + j0, kvT, 63);
+  u32x4_t kreg[2], vreg[2];
+  {
+    const bf16_t* kr = k + ((size_t)bh * kvT + min(key, T_seq - 1)) * 64;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&t.a[r0 + j][d8]) = g.v[j];
-  if (tt) {
+    for (int sl = 0; sl < 2; ++sl) kreg[sl] = *reinterpret_cast<const u32x4_t*>(kr + sl * 32 + lg * 8);
+  }
+  const float* lse_bh = lse + (size_t)bh * T_seq;
+  const float* dv_bh = dvec + (size_t)bh * T_seq;
+  auto issue = [&](int qt, int buf) {
+    const int i0 = qt * kBT;
+    dma_tile(sQ[buf], q + ((size_t)bh * T_seq + i0) * 64, 64, T_seq - 1 - i0);
+    dma_tile(sO[buf], dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, T_seq - 1 - i0);
+  };
+  float gl = 0.f, gd = 0.f;  // lse, dvec of query threadIdx.x of the next tile
+  auto fetch_ld = [&](int qt) {
+    if (threadIdx.x < kBT) {
+      const int i = min(qt * kBT + (int)threadIdx.x, T_seq - 1);
+      gl = lse_bh[i] * kLog2e;
+      gd = dv_bh[i];
+    }
+  };
+  wait_vmcnt_bwd<0>();
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t a = g.v[0][e], b = g.v[1][e];  // rows r0, r0 + 1; elements d8 + 2e, d8 + 2e + 1
-      *reinterpret_cast<uint32_t*>(&tt->a[d8 + 2 * e][r0]) = (a & 0xFFFFu) | (b << 16);
-      *reinterpret_cast<uint32_t*>(&tt->a[d8 + 2 * e + 1][r0]) = (a >> 16) | (b & 0xFFFF0000u);
+  for (int sl = 0; sl < 2; ++sl) vreg[sl] = tr_frag(sQ[1], 32 * sl + 8 * lg, 32 * sl + 8 * lg + 4, 16 * w, lr);
+  __syncthreads();  // sQ[1] free again
+  issue(kt, 0);
+  fetch_ld(kt);
+
+  f32x4_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qt = kt; qt < n_tiles; ++qt) {
+    const int buf = (qt - kt) & 1, i0 = qt * kBT;
+    if (threadIdx.x < kBT) {
+      sL[buf][threadIdx.x] = gl;
+      sD[buf][threadIdx.x] = gd;
+    }
+    wait_vmcnt_bwd<0>();
+    __syncthreads();  // tile qt landed everywhere; everyone is past tile qt - 1
+    if (qt + 1 < n_tiles) {
+      issue(qt + 1, buf ^ 1);
+      fetch_ld(qt + 1);
+    }
+    const char* tQ = sQ[buf];
+    const char* tO = sO[buf];
+    // S[q = 16 qb + 4 lg + e][key] and dP likewise
+    f32x4_t s[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) s[qb] = dp[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        Mma<bf16_t>::run(s[qb], plain_frag(tQ, 16 * qb + lr, sl * 4 + lg), kreg[sl]);
+        Mma<bf16_t>::run(dp[qb], plain_frag(tO, 16 * qb + lr, sl * 4 + lg), vreg[sl]);
+      }
+    const bool full = qt > kt && i0 + kBT <= T_seq;  // uniform: every entry of the tile kept
+    u32x4_t pf[2], sf[2];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][16 * qb + 4 * lg]);
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][16 * qb + 4 * lg]);
+      float pv[4], sv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qi = i0 + 16 * qb + 4 * lg + e;
+        const bool ok = full || (key <= qi && qi < T_seq);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], kLog2e, -l4[e]));
+        const float ds = p * (dp[qb][e] - d4[e]);
+        pv[e] = ok ? p : 0.f;
+        sv[e] = ok ? ds : 0.f;
+      }
+      pf[qb >> 1][(qb & 1) * 2] = pack2_bf16(pv[0], pv[1]);
+      pf[qb >> 1][(qb & 1) * 2 + 1] = pack2_bf16(pv[2], pv[3]);
+      sf[qb >> 1][(qb & 1) * 2] = pack2_bf16(sv[0], sv[1]);
+      sf[qb >> 1][(qb & 1) * 2 + 1] = pack2_bf16(sv[2], sv[3]);
+    }
+    // dV^T[d][key] += sum_q dO^T[d][q] P[q][key]; dK^T likewise with Q, dS
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int r0 = pslot_row(s2, lg, 0), r1 = pslot_row(s2, lg, 1);
+        Mma<bf16_t>::run(dv[db], tr_frag(tO, r0, r1, 16 * db, lr), pf[s2]);
+        Mma<bf16_t>::run(dk[db], tr_frag(tQ, r0, r1, 16 * db, lr), sf[s2]);
+      }
+  }
+  // lane holds dK^T, dV^T [d = 16 db + 4 lg + e][key]
+  if (key < T_seq) {
+    float* row = dqkv + ((size_t)b * T_seq + key) * (3 * Dm) + h * 64;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      *reinterpret_cast<f32x4_t*>(row + Dm + 16 * db + 4 * lg) = dk[db];
+      *reinterpret_cast<f32x4_t*>(row + 2 * Dm + 16 * db + 4 * lg) = dv[db];
     }
   }
 }
 
-// Rows r < valid of a [rows][ld] bf16 matrix into t (and transposed into tt),
-// rows past `valid` zero.
-__device__ __forceinline__ void load_rows_bf16(MmaTile& t, MmaTile* tt, const bf16_t* src, size_t ld, int valid) {
-  TileRegs g;
-  fetch_rows_bf16(g, src, ld, valid);
-  put_rows_bf16(t, tt, g);
-}
-
-// V^T rows (global [d][kvT], keys contiguous) into V as [key][d]; keys past
-// `valid` zero.  Thread t holds keys k8 .. k8+7 (k8 = 8 (t % 8)) of rows
-// d = 2 (t / 8) and d + 1, so each key's two values leave as one 4-byte write.
-__device__ __forceinline__ void fetch_vt_bf16(TileRegs& g, const bf16_t* vt, int kvT, int j0, int valid) {
-  const int d0 = 2 * (threadIdx.x >> 3), k8 = (threadIdx.x & 7) * 8;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    g.v[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (k8 < valid) g.v[j] = *reinterpret_cast<const u32x4_t*>(vt + (size_t)(d0 + j) * kvT + j0 + k8);
-  }
-}
-
-__device__ __forceinline__ void put_vt_bf16(MmaTile& t, const TileRegs& g, int valid) {
-  const int d0 = 2 * (threadIdx.x >> 3), k8 = (threadIdx.x & 7) * 8;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t a = g.v[0][e], b = g.v[1][e];  // rows d0, d0 + 1; keys k8 + 2e, k8 + 2e + 1
-    const bool lo = k8 + 2 * e < valid, hi = k8 + 2 * e + 1 < valid;
-    *reinterpret_cast<uint32_t*>(&t.a[k8 + 2 * e][d0]) = lo ? (a & 0xFFFFu) | (b << 16) : 0u;
-    *reinterpret_cast<uint32_t*>(&t.a[k8 + 2 * e + 1][d0]) = hi ? (a >> 16) | (b & 0xFFFF0000u) : 0u;
-  }
-}
-
-__device__ __forceinline__ void load_vt_bf16(MmaTile& t, const bf16_t* vt, int kvT, int j0, int valid) {
-  TileRegs g;
-  fetch_vt_bf16(g, vt, kvT, j0, valid);
-  put_vt_bf16(t, g, valid);
-}
-
-// S and dP of one 16-row block (rows `r16` of X-side tiles Qs / dOs) against
-// the 64 keys of Ks / Vs, or (keys_by_wave) of 64 query rows against one
-// 16-key block: acc[b] covers the b-th 16 x 16 block.
-__device__ __forceinline__ void mma_sp(f32x4_t (&s)[4], f32x4_t (&dp)[4], const MmaTile& X1, const MmaTile& Y1,
-                                       const MmaTile& X2, const MmaTile& Y2, int xrow0, int yrow0, bool x_varies) {
-  const int lr = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    s[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    dp[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int k8 = ks * 32 + lg * 8;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int xr = x_varies ? b * 16 + lr : xrow0 + lr;
-      const int yr = x_varies ? yrow0 + lr : b * 16 + lr;
-      Mma<bf16_t>::run(s[b], frag(X1, xr, k8), frag(Y1, yr, k8));
-      Mma<bf16_t>::run(dp[b], frag(X2, xr, k8), frag(Y2, yr, k8));
-    }
-  }
-}
-
-struct AttnBwdMmaKV {
-  MmaTile K, V, Q, Qt, dO, dOt, Pt, dSt;
-  float lse[kBT];
-  float dv[kBT];
-};
-
-// dK and dV of one key tile (64 keys): wave w owns keys 16w .. 16w+15.  Per
-// query tile at or after it: S and dP of all 64 queries against the wave's
-// keys; P = exp(S - lse), dS = P (dP - rowsum(dO o)) (exactly 0 where the key
-// follows the query or the query is past the end), written as P^T, dS^T
-// rows of the wave's keys; then dV += P^T dO and dK += dS^T Q.
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_mma_kernel(const bf16_t* __restrict__ q,
+// dQ of one query tile: wave w owns queries 16 w .. 16 w + 15, whose Q and
+// dO rows (and lse, dvec) it keeps in registers.  Per key tile at or before
+// it (K and V^T tiles double-buffered in LDS): S and dP of the 64 keys
+// against the wave's queries (lane (lr, lg): keys 16 kb + 4 lg + e, query lr),
+// dS = P (dP - dvec) selected to 0 where the key follows the query, then
+// dQ^T += K^T dS.
+__global__ __launch_bounds__(256) void attn_bwd_dq_reg_kernel(const bf16_t* __restrict__ q,
                                                                 const bf16_t* __restrict__ k,
                                                                 const bf16_t* __restrict__ vt,
                                                                 const bf16_t* __restrict__ dout,
                                                                 const float* __restrict__ lse,
                                                                 const float* __restrict__ dvec,
                                                                 float* __restrict__ dqkv, int BH, int H, int T_seq,
-                                                                int kvT, int n_tiles) {
-  __shared__ AttnBwdMmaKV sm;
-  const int kt = blockIdx.x / BH, bh = blockIdx.x - kt * BH;  // key tile 0 (the longest) first
-  const int b = bh / H, h = bh - b * H;
-  const int j0 = kt * kBT;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int Dm = H * 64;
-  load_rows_bf16(sm.K, nullptr, k + ((size_t)bh * kvT + j0) * 64, 64, min(kBT, T_seq - j0));
-  load_vt_bf16(sm.V, vt + (size_t)bh * 64 * kvT, kvT, j0, min(kBT, T_seq - j0));
-  f32x4_t dk[4], dv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // The next query tile's Q, dO, lse and dvec are read into registers while
-  // the current one is computed.
-  TileRegs gq, gdo;
-  float glse = 0.f, gdv = 0.f;
-  auto fetch_qtile = [&](int qt) {
-    const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
-    fetch_rows_bf16(gq, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
-    fetch_rows_bf16(gdo, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
-    if (threadIdx.x < kBT) {
-      const int i = threadIdx.x;
-      glse = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
-      gdv = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
-    }
-  };
-  fetch_qtile(kt);
-  for (int qt = kt; qt < n_tiles; ++qt) {
-    const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
-    __syncthreads();
-    put_rows_bf16(sm.Q, &sm.Qt, gq);
-    put_rows_bf16(sm.dO, &sm.dOt, gdo);
-    if (threadIdx.x < kBT) {
-      sm.lse[threadIdx.x] = glse;
-      sm.dv[threadIdx.x] = gdv;
-    }
-    if (qt + 1 < n_tiles) fetch_qtile(qt + 1);
-    __syncthreads();
-    // R[q][key] for the 4 query blocks (x varies) against this wave's keys
-    f32x4_t s[4], dp[4];
-    mma_sp(s, dp, sm.Q, sm.K, sm.dO, sm.V, 0, w * 16, true);
-    const int key = w * 16 + lr;  // local key of this lane's column
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      uint32_t pw[2], sw[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        float pv[2], sv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int e = e2 * 2 + u;
-          const int ql = qb * 16 + lg * 4 + e;
-          const bool ok = j0 + key <= i0 + ql && ql < nq;
-          const float p = ok ? __builtin_amdgcn_exp2f((s[qb][e] - sm.lse[ql]) * kLog2e) : 0.f;
-          pv[u] = p;
-          sv[u] = ok ? p * (dp[qb][e] - sm.dv[ql]) : 0.f;
-        }
-        pw[e2] = pack2_bf16(pv[0], pv[1]);
-        sw[e2] = pack2_bf16(sv[0], sv[1]);
-      }
-      // P^T[key][q .. q+3], dS^T likewise: one 8-byte store each
-      *reinterpret_cast<u32x2_t*>(&sm.Pt.a[key][qb * 16 + lg * 4]) = u32x2_t{pw[0], pw[1]};
-      *reinterpret_cast<u32x2_t*>(&sm.dSt.a[key][qb * 16 + lg * 4]) = u32x2_t{sw[0], sw[1]};
-    }
-    __syncthreads();
-    // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (contraction over the 64 queries)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k8 = ks * 32 + lg * 8;
-      const u32x4_t pf = frag(sm.Pt, w * 16 + lr, k8), sf = frag(sm.dSt, w * 16 + lr, k8);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        Mma<bf16_t>::run(dv[db], pf, frag(sm.dOt, db * 16 + lr, k8));
-        Mma<bf16_t>::run(dk[db], sf, frag(sm.Qt, db * 16 + lr, k8));
-      }
-    }
-  }
-  // lane holds R[key = 16w + 4 lg + e][d = 16 db + lr]
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int j = j0 + w * 16 + lg * 4 + e;
-    if (j < T_seq) {
-      float* row = dqkv + ((size_t)b * T_seq + j) * (3 * Dm) + h * 64 + lr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        row[Dm + db * 16] = dk[db][e];
-        row[2 * Dm + db * 16] = dv[db][e];
-      }
-    }
-  }
-}
-
-struct AttnBwdMmaQ {
-  MmaTile Q, dO, K, Kt, V, dS;
-  float lse[kBT];
-  float dv[kBT];
-};
-
-// dQ of one query tile: wave w owns queries 16w .. 16w+15.  Per key tile at
-// or before it: S, dP of the wave's queries against the 64 keys, dS written
-// as rows of the wave's queries, then dQ += dS K (against K^T).
-__global__ __launch_bounds__(256) void attn_bwd_dq_mma_kernel(const bf16_t* __restrict__ q,
-                                                              const bf16_t* __restrict__ k,
-                                                              const bf16_t* __restrict__ vt,
-                                                              const bf16_t* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ dvec,
-                                                              float* __restrict__ dqkv, int BH, int H, int T_seq,
-                                                              int kvT, int n_tiles, float scale) {
-  __shared__ AttnBwdMmaQ sm;
+                                                                int kvT, int n_tiles, float scale) {
+  __shared__ __attribute__((aligned(16))) char sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][kTileBytes];
   const int r = blockIdx.x / BH, bh = blockIdx.x - r * BH;
   const int qt = n_tiles - 1 - r;  // the last query tile (the longest) first
   const int b = bh / H, h = bh - b * H;
-  const int i0 = qt * kBT, nq = min(kBT, T_seq - i0);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int i0 = qt * kBT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int Dm = H * 64;
-  load_rows_bf16(sm.Q, nullptr, q + ((size_t)bh * T_seq + i0) * 64, 64, nq);
-  load_rows_bf16(sm.dO, nullptr, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, nq);
-  if (threadIdx.x < kBT) {
-    const int i = threadIdx.x;
-    sm.lse[i] = i < nq ? lse[(size_t)bh * T_seq + i0 + i] : 0.f;
-    sm.dv[i] = i < nq ? dvec[(size_t)bh * T_seq + i0 + i] : 0.f;
+  const int qi = i0 + 16 * w + lr;  // this lane's query
+  const int qc = min(qi, T_seq - 1);
+  auto issue = [&](int kt, int buf) {
+    const int j0 = kt * kBT;
+    dma_tile(sK[buf], k + ((size_t)bh * kvT + j0) * 64, 64, T_seq - 1 - j0);
+    dma_tile(sV[buf], vt + (size_t)bh * 64 * kvT + j0, kvT, 63);
+  };
+  issue(0, 0);
+  u32x4_t qreg[2], oreg[2];
+  {
+    const bf16_t* qr = q + ((size_t)bh * T_seq + qc) * 64;
+    const bf16_t* orow = dout + ((size_t)b * T_seq + qc) * Dm + h * 64;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      qreg[sl] = *reinterpret_cast<const u32x4_t*>(qr + sl * 32 + lg * 8);
+      oreg[sl] = *reinterpret_cast<const u32x4_t*>(orow + sl * 32 + lg * 8);
+    }
   }
+  const float l2 = lse[(size_t)bh * T_seq + qc] * kLog2e;
+  const float dvq = dvec[(size_t)bh * T_seq + qc];
   f32x4_t dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // The next key tile's K and V^T are read into registers while the current
-  // one is computed.
-  TileRegs gk, gv;
-  auto fetch_ktile = [&](int kt) {
-    const int j0 = kt * kBT, nk = min(kBT, T_seq - j0);
-    fetch_rows_bf16(gk, k + ((size_t)bh * kvT + j0) * 64, 64, nk);
-    fetch_vt_bf16(gv, vt + (size_t)bh * 64 * kvT, kvT, j0, nk);
-  };
-  fetch_ktile(0);
   for (int kt = 0; kt <= qt; ++kt) {
-    const int j0 = kt * kBT, nk = min(kBT, T_seq - j0);
-    __syncthreads();
-    put_rows_bf16(sm.K, &sm.Kt, gk);
-    put_vt_bf16(sm.V, gv, nk);
-    if (kt + 1 <= qt) fetch_ktile(kt + 1);
-    __syncthreads();
-    // R[q][key] for this wave's queries (y varies over the 4 key blocks)
+    const int buf = kt & 1, j0 = kt * kBT;
+    wait_vmcnt_bwd<0>();
+    __syncthreads();  // tile kt landed everywhere; everyone is past tile kt - 1
+    if (kt + 1 <= qt) issue(kt + 1, buf ^ 1);
+    const char* tK = sK[buf];
+    const char* tV = sV[buf];
+    // S[key = 16 kb + 4 lg + e][query lr] and dP likewise
     f32x4_t s[4], dp[4];
-    mma_sp(s, dp, sm.Q, sm.K, sm.dO, sm.V, w * 16, 0, false);
-    // lane holds R[q = 16w + 4 lg + e][key = 16 kb + lr]
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) s[kb] = dp[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        Mma<bf16_t>::run(s[kb], plain_frag(tK, 16 * kb + lr, sl * 4 + lg), qreg[sl]);
+        Mma<bf16_t>::run(dp[kb], tr_frag(tV, 32 * sl + 8 * lg, 32 * sl + 8 * lg + 4, 16 * kb, lr), oreg[sl]);
+      }
+    const bool full = kt < qt;  // uniform: every key before every query of the tile
+    u32x4_t sf[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float sv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int ql = w * 16 + lg * 4 + e, key = kb * 16 + lr;
-        const bool ok = j0 + key <= i0 + ql && ql < nq;
-        const float p = ok ? __builtin_amdgcn_exp2f((s[kb][e] - sm.lse[ql]) * kLog2e) : 0.f;
-        sm.dS.a[ql][key].bits = f32_to_bf16(ok ? p * (dp[kb][e] - sm.dv[ql]) : 0.f);
+        const int kj = j0 + 16 * kb + 4 * lg + e;
+        const bool ok = full || kj <= qi;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], kLog2e, -l2));
+        const float ds = p * (dp[kb][e] - dvq);
+        sv[e] = ok ? ds : 0.f;
       }
-    __syncthreads();
-    // dQ[q][d] += dS K  (contraction over the 64 keys; K^T rows are d)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k8 = ks * 32 + lg * 8;
-      const u32x4_t sf = frag(sm.dS, w * 16 + lr, k8);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) Mma<bf16_t>::run(dq[db], sf, frag(sm.Kt, db * 16 + lr, k8));
+      sf[kb >> 1][(kb & 1) * 2] = pack2_bf16(sv[0], sv[1]);
+      sf[kb >> 1][(kb & 1) * 2 + 1] = pack2_bf16(sv[2], sv[3]);
     }
+    // dQ^T[d][q] += sum_key K^T[d][key] dS[q][key]
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        Mma<bf16_t>::run(dq[db], tr_frag(tK, pslot_row(s2, lg, 0), pslot_row(s2, lg, 1), 16 * db, lr), sf[s2]);
   }
-  // lane holds R[q = 16w + 4 lg + e][d = 16 db + lr]
+  // lane holds dQ^T[d = 16 db + 4 lg + e][query]
+  if (qi < T_seq) {
+    float* row = dqkv + ((size_t)b * T_seq + qi) * (3 * Dm) + h * 64;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = i0 + w * 16 + lg * 4 + e;
-    if (i < T_seq) {
-      float* row = dqkv + ((size_t)b * T_seq + i) * (3 * Dm) + h * 64 + lr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) row[db * 16] = scale * dq[db][e];
-    }
+    for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4_t*>(row + 16 * db + 4 * lg) = dq[db] * scale;
   }
 }
 
@@ -936,9 +903,9 @@ hipError_t launch_attention_backward(const T* q, const T* k, const T* vt, const 
     if (hs == 64) {
       hipLaunchKernelGGL(attn_bwd_dvec_bf16_kernel, dim3((rows + 31) / 32), block, 0, stream, o, dout, dvec, B, H,
                          T_seq);
-      hipLaunchKernelGGL(attn_bwd_dkdv_mma_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
+      hipLaunchKernelGGL(attn_bwd_dkdv_reg_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
                          T_seq, kvT, n_tiles);
-      hipLaunchKernelGGL(attn_bwd_dq_mma_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
+      hipLaunchKernelGGL(attn_bwd_dq_reg_kernel, grid, block, 0, stream, q, k, vt, dout, lse, dvec, dqkv, B * H, H,
                          T_seq, kvT, n_tiles, scale);
       return hipGetLastError();
     }
