@@ -495,9 +495,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const T* __restrict__ 
 constexpr int kTileBytes = kBT * 128;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
+// s_waitcnt vmcnt(N) (N < 16) as the builtin, so the compiler's own wait
+// insertion knows which loads it has retired.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_bwd() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ int pslot_row(int s2, int lg, int h) { return 32 * s2 + 16 * h + 4 * lg; }
@@ -536,13 +539,36 @@ __device__ __forceinline__ void dma_tile(char* tile, const bf16_t* src, size_t l
   }
 }
 
+// A 64-row tile between its global read and its LDS write, so that the next
+// tile's reads are in flight while the current one is computed (the loop
+// issues no LDS DMA: with one in flight the compiler waits for it before
+// every transposing read).  Thread t holds chunks 2 (t % 4) and +1 of row
+// t / 4; source row r is src + min(r, last) * ld.
+struct TileRegs {
+  u32x4_t v[2];
+};
+
+__device__ __forceinline__ void fetch_tile(TileRegs& g, const bf16_t* src, size_t ld, int last) {
+  const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 2;
+  const bf16_t* p = src + (size_t)min(row, last) * ld + c0 * 8;
+  g.v[0] = *reinterpret_cast<const u32x4_t*>(p);
+  g.v[1] = *reinterpret_cast<const u32x4_t*>(p + 8);
+}
+
+__device__ __forceinline__ void put_tile(char* tile, const TileRegs& g) {
+  const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 2;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *reinterpret_cast<u32x4_t*>(tile + row * 128 + (((c0 + j) ^ (row & 7)) << 4)) = g.v[j];
+}
+
 // dK and dV of one key tile (64 keys): wave w owns keys 16 w .. 16 w + 15,
 // whose K and V rows it keeps as MFMA operands in registers.  Per query
 // tile at or after it (Q and dO tiles double-buffered in LDS): S and dP of
 // the 64 queries against the wave's keys, P = exp(S - lse) and
 // dS = P (dP - dvec) (selected to 0 where the key follows the query or the
 // query is past the end), then dV^T += dO^T P and dK^T += Q^T dS.
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_reg_kernel(const bf16_t* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_dkdv_reg_kernel(const bf16_t* __restrict__ q,
                                                                   const bf16_t* __restrict__ k,
                                                                   const bf16_t* __restrict__ vt,
                                                                   const bf16_t* __restrict__ dout,
@@ -573,42 +599,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_reg_kernel(const bf16_t* __
   }
   const float* lse_bh = lse + (size_t)bh * T_seq;
   const float* dv_bh = dvec + (size_t)bh * T_seq;
-  auto issue = [&](int qt, int buf) {
+  TileRegs gq, go;
+  float gl, gd;  // lse (unscaled while in flight), dvec of query threadIdx.x % 64
+  auto fetch = [&](int qt) {
     const int i0 = qt * kBT;
-    dma_tile(sQ[buf], q + ((size_t)bh * T_seq + i0) * 64, 64, T_seq - 1 - i0);
-    dma_tile(sO[buf], dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, T_seq - 1 - i0);
-  };
-  float gl = 0.f, gd = 0.f;  // lse, dvec of query threadIdx.x of the next tile
-  auto fetch_ld = [&](int qt) {
-    if (threadIdx.x < kBT) {
-      const int i = min(qt * kBT + (int)threadIdx.x, T_seq - 1);
-      gl = lse_bh[i] * kLog2e;
-      gd = dv_bh[i];
-    }
+    fetch_tile(gq, q + ((size_t)bh * T_seq + i0) * 64, 64, T_seq - 1 - i0);
+    fetch_tile(go, dout + ((size_t)b * T_seq + i0) * Dm + h * 64, Dm, T_seq - 1 - i0);
+    const int i = min(i0 + (int)(threadIdx.x & 63), T_seq - 1);  // every thread loads (no branch)
+    gl = lse_bh[i];
+    gd = dv_bh[i];
   };
   wait_vmcnt_bwd<0>();
   __syncthreads();
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) vreg[sl] = tr_frag(sQ[1], 32 * sl + 8 * lg, 32 * sl + 8 * lg + 4, 16 * w, lr);
-  __syncthreads();  // sQ[1] free again
-  issue(kt, 0);
-  fetch_ld(kt);
+  fetch(kt);
 
   f32x4_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dk[i] = dv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int qt = kt; qt < n_tiles; ++qt) {
     const int buf = (qt - kt) & 1, i0 = qt * kBT;
+    // tile qt into buffer buf (last read two tiles ago, before the previous barrier)
+    put_tile(sQ[buf], gq);
+    put_tile(sO[buf], go);
     if (threadIdx.x < kBT) {
-      sL[buf][threadIdx.x] = gl;
+      sL[buf][threadIdx.x] = gl * kLog2e;
       sD[buf][threadIdx.x] = gd;
     }
-    wait_vmcnt_bwd<0>();
-    __syncthreads();  // tile qt landed everywhere; everyone is past tile qt - 1
-    if (qt + 1 < n_tiles) {
-      issue(qt + 1, buf ^ 1);
-      fetch_ld(qt + 1);
-    }
+    __syncthreads();  // tile qt in LDS; everyone is past tile qt - 1
+    if (qt + 1 < n_tiles) fetch(qt + 1);
     const char* tQ = sQ[buf];
     const char* tO = sO[buf];
     // S[q = 16 qb + 4 lg + e][key] and dP likewise
@@ -689,12 +709,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reg_kernel(const bf16_t* __re
   const int Dm = H * 64;
   const int qi = i0 + 16 * w + lr;  // this lane's query
   const int qc = min(qi, T_seq - 1);
-  auto issue = [&](int kt, int buf) {
+  TileRegs gk, gv;
+  auto fetch = [&](int kt) {
     const int j0 = kt * kBT;
-    dma_tile(sK[buf], k + ((size_t)bh * kvT + j0) * 64, 64, T_seq - 1 - j0);
-    dma_tile(sV[buf], vt + (size_t)bh * 64 * kvT + j0, kvT, 63);
+    fetch_tile(gk, k + ((size_t)bh * kvT + j0) * 64, 64, T_seq - 1 - j0);
+    fetch_tile(gv, vt + (size_t)bh * 64 * kvT + j0, kvT, 63);
   };
-  issue(0, 0);
   u32x4_t qreg[2], oreg[2];
   {
     const bf16_t* qr = q + ((size_t)bh * T_seq + qc) * 64;
@@ -705,16 +725,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reg_kernel(const bf16_t* __re
       oreg[sl] = *reinterpret_cast<const u32x4_t*>(orow + sl * 32 + lg * 8);
     }
   }
-  const float l2 = lse[(size_t)bh * T_seq + qc] * kLog2e;
+  const float lq = lse[(size_t)bh * T_seq + qc];
   const float dvq = dvec[(size_t)bh * T_seq + qc];
+  fetch(0);
+  wait_vmcnt_bwd<4>();  // the wave's own rows are in; the first tile's four loads may not be
+  const float l2 = lq * kLog2e;
   f32x4_t dq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dq[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int kt = 0; kt <= qt; ++kt) {
     const int buf = kt & 1, j0 = kt * kBT;
-    wait_vmcnt_bwd<0>();
-    __syncthreads();  // tile kt landed everywhere; everyone is past tile kt - 1
-    if (kt + 1 <= qt) issue(kt + 1, buf ^ 1);
+    // tile kt into buffer buf (last read two tiles ago, before the previous barrier)
+    put_tile(sK[buf], gk);
+    put_tile(sV[buf], gv);
+    __syncthreads();  // tile kt in LDS; everyone is past tile kt - 1
+    if (kt + 1 <= qt) fetch(kt + 1);
     const char* tK = sK[buf];
     const char* tV = sV[buf];
     // S[key = 16 kb + 4 lg + e][query lr] and dP likewise

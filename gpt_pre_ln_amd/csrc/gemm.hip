@@ -190,7 +190,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const bool more = kt + S - 1 < KT;
-    if (!(KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW);
+    // K-major tiles: every fragment of the step is read before the next
+    // stage's loads go out.  The transposing LDS reads carry no alias
+    // information, so the compiler waits for all LDS DMA in flight before
+    // each of them; issued after them, the loads overlap this step's MFMAs.
+    constexpr bool kReadsFirst = AKM || BKM;
+    if (!(KNOB & kSplitIssue) && !kReadsFirst && more) issue(kt + S - 1, 0, RBW);
 
     const u32x4_t* s = smem + (kt % S) * STAGE;
     u32x4_t af[2][FM], bfr[2][FN];
@@ -224,6 +229,13 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
       if (KNOB & kPrio) __builtin_amdgcn_s_setprio(0);
     };
     read_frags(0);
+    if constexpr (kReadsFirst) {
+      read_frags(1);
+      if (more) issue(kt + S - 1, 0, RBW);
+      mfma_slab(0);
+      mfma_slab(1);
+      continue;
+    }
     if (KNOB & kInterleave) {
       if ((KNOB & kSplitIssue) && more) issue(kt + S - 1, 0, RBW / 2);
       if (KNOB & kPrio) __builtin_amdgcn_s_setprio(1);
