@@ -66,8 +66,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 
   static_assert(KI * 64 * NW == K_CHUNKS && VI * 64 * NW == V_CHUNKS && KI >= 1 && VI >= 1, "tile split");
   static_assert(KI + VI <= 63, "loads in flight must fit the vmcnt counter");
 
-  __shared__ u32x4_t sK[2][K_CHUNKS];
-  __shared__ u32x4_t sV[2][V_CHUNKS];
+  // Dynamic LDS: with the two buffers in one dynamic allocation the compiler
+  // does not wait for the next tile's DMA (in flight into the other buffer)
+  // before reading this one; as static arrays it did, every tile.
+  extern __shared__ u32x4_t attn_lds[];
+  u32x4_t(*sK)[K_CHUNKS] = reinterpret_cast<u32x4_t(*)[K_CHUNKS]>(attn_lds);
+  u32x4_t(*sV)[V_CHUNKS] = reinterpret_cast<u32x4_t(*)[V_CHUNKS]>(attn_lds + 2 * K_CHUNKS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -576,6 +580,13 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const float* __re
 
 constexpr int kPrefillQW = 16;  // queries per wave (see the kernel's notes)
 
+// Dynamic LDS of attn_prefill_kernel<T, HS, ...>: two K tiles (64 keys x HS)
+// and two V^T tiles (HS x 64 keys).
+template <typename T, int HS>
+constexpr size_t prefill_lds_bytes() {
+  return 2 * (64 * HS + HS * 64) * sizeof(T);
+}
+
 template <typename T>
 hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out, int B, int H, int Tq,
                                     int kvT, int hs, hipStream_t stream, float* lse) {
@@ -583,11 +594,14 @@ hipError_t launch_attention_prefill(const T* q, const T* k, const T* vt, T* out,
   const int n_qtiles = (Tq + 4 * QW - 1) / (4 * QW);
   dim3 grid(B * H * n_qtiles), block(256);
   if (hs == 64) {
-    hipLaunchKernelGGL((attn_prefill_kernel<T, 64, QW>), grid, block, 0, stream, q, k, vt, out, B * H, H, Tq, kvT,
+    const size_t lds = prefill_lds_bytes<T, 64>();
+    hipLaunchKernelGGL((attn_prefill_kernel<T, 64, QW>), grid, block, lds, stream, q, k, vt, out, B * H, H, Tq, kvT,
                        n_qtiles, lse);
   } else if (hs == 16 && sizeof(T) == 4) {
-    hipLaunchKernelGGL((attn_prefill_kernel<T, (sizeof(T) == 4 ? 16 : 64), QW>), grid, block, 0, stream, q, k,
-                       vt, out, B * H, H, Tq, kvT, n_qtiles, lse);
+    constexpr int HS = sizeof(T) == 4 ? 16 : 64;
+    const size_t lds = prefill_lds_bytes<T, HS>();
+    hipLaunchKernelGGL((attn_prefill_kernel<T, HS, QW>), grid, block, lds, stream, q, k, vt, out, B * H, H, Tq, kvT,
+                       n_qtiles, lse);
   } else {
     return hipErrorInvalidValue;
   }
