@@ -9,6 +9,7 @@ namespace gpt2 {
 namespace {
 
 constexpr int kColChunks = 64;  // row chunks of the first column-sum pass
+constexpr int kColBatch = 8;    // rows per thread with loads in flight together
 
 // 32x32 tile transpose through LDS; 256 threads = 32 x 8.  Tiles cover dst
 // rows c and dst columns r < ld_dst (the padding columns are written as 0).
@@ -117,31 +118,51 @@ __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __re
   float s[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s[e] = 0.f;
-  if (n < N) {
-    for (int m = m0 + ry; m < m1; m += 4) {
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + (size_t)m * N + n);
-      float v[VEC];
-      if constexpr (sizeof(Tin) == 2) {
+  if (n < N && m0 + ry < m1) {
+    // kColBatch rows per thread in flight: every load unconditional (rows past
+    // the chunk read its last row), rows past the chunk add 0 (s never holds
+    // -0, so the sums keep their bits), the additions in row order as before
+    constexpr int U = kColBatch;
+    for (int m = m0 + ry; m < m1; m += 4 * U) {
+      u32x4_t raw[U];
+      f32x4_t xr[kXhat ? U : 1];
+      float mmv[kXhat ? U : 1], rsv[kXhat ? U : 1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] = bf16_to_f32(raw[e] & 0xFFFF);
-          v[2 * e + 1] = bf16_to_f32(raw[e] >> 16);
-        }
-      } else {
-        const f32x4_t f = __builtin_bit_cast(f32x4_t, raw);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = f[e];
-      }
-      if constexpr (kXhat) {
-        const float mm = mu[m], rs = rstd[m];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          s2[e] += v[e];
-          v[e] *= (x[(size_t)m * N + n + e] - mm) * rs;
+      for (int u = 0; u < U; ++u) {
+        const int mc = min(m + 4 * u, m1 - 1);
+        raw[u] = *reinterpret_cast<const u32x4_t*>(src + (size_t)mc * N + n);
+        if constexpr (kXhat) {
+          xr[u] = *reinterpret_cast<const f32x4_t*>(x + (size_t)mc * N + n);
+          mmv[u] = mu[mc];
+          rsv[u] = rstd[mc];
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // the batch's loads before its first use
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) s[e] += v[e];
+      for (int u = 0; u < U; ++u) {
+        const bool on = m + 4 * u < m1;
+        float v[VEC];
+        if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_to_f32(raw[u][e] & 0xFFFF);
+            v[2 * e + 1] = bf16_to_f32(raw[u][e] >> 16);
+          }
+        } else {
+          const f32x4_t f = __builtin_bit_cast(f32x4_t, raw[u]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = f[e];
+        }
+        if constexpr (kXhat) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            s2[e] += on ? v[e] : 0.f;
+            v[e] *= (xr[u][e] - mmv[u]) * rsv[u];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s[e] += on ? v[e] : 0.f;
+      }
     }
   }
 #pragma unroll
@@ -785,11 +806,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reg_kernel(const bf16_t* __re
 }
 
 // out[i] = sum over s < splits of part[s * n + i], s in increasing order.
+// All MAXS loads of an element go out before the first addition (slices
+// past `splits` re-read the last one and are not added).
+template <int MAXS>
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int splits, size_t n,
                                                           float* __restrict__ out) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
-    float s = part[i];
-    for (int k = 1; k < splits; ++k) s += part[(size_t)k * n + i];
+    float v[MAXS];
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) v[k] = part[(size_t)min(k, splits - 1) * n + i];
+    float s = v[0];
+#pragma unroll
+    for (int k = 1; k < MAXS; ++k) s = k < splits ? s + v[k] : s;
     out[i] = s;
   }
 }
@@ -800,7 +828,16 @@ hipError_t launch_sum_splits(const float* part, int splits, size_t n, float* out
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, n, out);
+  if (splits < 1 || splits > 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (splits <= 2)
+    hipLaunchKernelGGL(sum_splits_kernel<2>, grid, block, 0, stream, part, splits, n, out);
+  else if (splits <= 4)
+    hipLaunchKernelGGL(sum_splits_kernel<4>, grid, block, 0, stream, part, splits, n, out);
+  else if (splits <= 8)
+    hipLaunchKernelGGL(sum_splits_kernel<8>, grid, block, 0, stream, part, splits, n, out);
+  else
+    hipLaunchKernelGGL(sum_splits_kernel<16>, grid, block, 0, stream, part, splits, n, out);
   return hipGetLastError();
 }
 
