@@ -13,7 +13,9 @@ constexpr int kMaxV4 = 8;  // float4 per lane -> D <= 2048
 
 // Ids outside [0, V) are clamped to the nearest row of wte, so the gather
 // never leaves the matrix; `bad` (optional) then receives 1.
-template <typename T>
+// NV > 0: d_model = 256 NV, all NV chunks of the row requested before the
+// first store; NV = 0: any d_model, one chunk at a time.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids, const T* __restrict__ wte,
                                                      const T* __restrict__ wpe, float* __restrict__ x, int M,
                                                      int T_seq, int pos0, int D, int V, int32_t* __restrict__ bad) {
@@ -27,10 +29,23 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const T* we = wte + (size_t)id * D;
   const T* pe = wpe + (size_t)pos * D;
   float* xr = x + (size_t)row * D;
-  for (int c = lane * 4; c < D; c += 256) {
-    float4 a = Elem<T>::load4(we + c);
-    float4 b = Elem<T>::load4(pe + c);
-    *reinterpret_cast<float4*>(xr + c) = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  if constexpr (NV > 0) {
+    float4 a[NV], b[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      a[i] = Elem<T>::load4(we + lane * 4 + i * 256);
+      b[i] = Elem<T>::load4(pe + lane * 4 + i * 256);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      *reinterpret_cast<float4*>(xr + lane * 4 + i * 256) =
+          make_float4(a[i].x + b[i].x, a[i].y + b[i].y, a[i].z + b[i].z, a[i].w + b[i].w);
+  } else {
+    for (int c = lane * 4; c < D; c += 256) {
+      float4 a = Elem<T>::load4(we + c);
+      float4 b = Elem<T>::load4(pe + c);
+      *reinterpret_cast<float4*>(xr + c) = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    }
   }
 }
 
@@ -334,8 +349,13 @@ template <typename T>
 hipError_t launch_embed(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq, int pos0, int D,
                         int V, int32_t* bad, hipStream_t stream) {
   if (V < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(embed_kernel<T>, dim3((M + 3) / 4), dim3(256), 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V,
-                     bad);
+  const dim3 grid((M + 3) / 4), block(256);
+  if (D == 768)
+    hipLaunchKernelGGL((embed_kernel<T, 3>), grid, block, 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V, bad);
+  else if (D == 1024)
+    hipLaunchKernelGGL((embed_kernel<T, 4>), grid, block, 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V, bad);
+  else
+    hipLaunchKernelGGL((embed_kernel<T, 0>), grid, block, 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V, bad);
   return hipGetLastError();
 }
 
