@@ -87,6 +87,56 @@ struct EpiQKV {
       p[3 * (size_t)kvT] = Elem<T>::from_f32(v[3]);
     }
   }
+  // The same stores with the per-column part of the index formed once per
+  // lane and tile (col_ctx: n is fixed over the rows a lane stores) and only
+  // the row part per group: destination element ((b * R + t) << hs_log2) +
+  // off, with R = H * Tq (q) or H * kvT (k).
+  struct ColCtx {
+    int which, n;
+    size_t off;
+  };
+  __device__ __forceinline__ ColCtx col_ctx(int n) const {
+    const int which = (int)D.div((uint32_t)n);
+    const int hd = n - which * (int)D.d;
+    const int head = hd >> hs_log2;
+    const int d = hd - (head << hs_log2);
+    const size_t off = which == 0 ? ((size_t)head * Tq.d << hs_log2) + d
+                                  : ((size_t)head * kvT + t0 << hs_log2) + d;
+    return ColCtx{which, n, off};
+  }
+  __device__ __forceinline__ void apply_c(int m, const ColCtx& c, const f32x4_t& v) const {
+    if (c.which == 2) {  // value columns of a wave that also holds key columns
+      apply(m, c.n, v, float4{});
+      return;
+    }
+    const uint32_t bb = Tq.div((uint32_t)m), t = (uint32_t)m - bb * Tq.d;
+    if (c.which == 0) {
+      const size_t i = ((size_t)(bb * (uint32_t)H * Tq.d + t) << hs_log2) + c.off;
+      Elem<T>::store4(q + i, v[0] * q_scale, v[1] * q_scale, v[2] * q_scale, v[3] * q_scale);
+    } else {
+      const size_t i = ((size_t)(bb * (uint32_t)H * (uint32_t)kvT + t) << hs_log2) + c.off;
+      Elem<T>::store4(k + i, v[0], v[1], v[2], v[3]);
+    }
+  }
+  // Row constants of apply_t (m is fixed over the columns a lane stores):
+  // the destination of a whole aligned vector is base + hd * kvT.
+  struct RowCtx {
+    size_t base;
+    bool vec;
+  };
+  __device__ __forceinline__ RowCtx row_ctx(int m) const {
+    const uint32_t bb = Tq.div((uint32_t)m), t = (uint32_t)m - bb * Tq.d;
+    const bool vec = m + 3 < M && t + 3 < Tq.d && ((t0 + t) & 3) == 0;
+    return RowCtx{((size_t)bb * (uint32_t)H << hs_log2) * (size_t)kvT + t0 + t, vec};
+  }
+  __device__ __forceinline__ void apply_tc(int m, const RowCtx& r, int n, const f32x4_t& v) const {
+    if (r.vec) {
+      const int hd = n - 2 * (int)D.d;
+      Elem<T>::store4(vt + r.base + (size_t)hd * kvT, v[0], v[1], v[2], v[3]);
+    } else {
+      apply_t(m, n, v);
+    }
+  }
   // v = C[m .. m+3][n] with n in the value third: positions t .. t+3 of one
   // V^T row, stored as one vector when they lie in one sequence and aligned.
   __device__ __forceinline__ void apply_t(int m, int n, const f32x4_t& v) const {

@@ -444,6 +444,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
       const int c = lane % CPR;
       const int n = nw + c * 4;
       const bool lane_on = lane < RPI * CPR;   // every lane when CPR divides 64
+      // per-lane column constants of the epilogue, formed once per round
+      const auto cctx = [&] {
+        if constexpr (requires { epi.col_ctx(0); }) return epi.col_ctx(min(n, N - 4));
+        else return 0;
+      }();
       float4 pre[NQ];
       if constexpr (Epi::kPreload) {
 #pragma unroll
@@ -467,7 +472,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
               v[g] = *reinterpret_cast<const f32x4_t*>(stg + r * RS + (slot(r, c) << 2));
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) epi.apply(mr + (q0 + g) * RPI + lane / CPR, n, v[g], pre[q0 + g]);
+            for (int g = 0; g < G; ++g) {
+              if constexpr (requires { epi.col_ctx(0); })
+                epi.apply_c(mr + (q0 + g) * RPI + lane / CPR, cctx, v[g]);
+              else
+                epi.apply(mr + (q0 + g) * RPI + lane / CPR, n, v[g], pre[q0 + g]);
+            }
           }
           continue;
         }
@@ -490,7 +500,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
           if (q0 + g >= NQ) break;
           const int r = (q0 + g) * RPI + lane / CPR;
           const int m = mr + r;
-          if (lane_on && r < R && m < M && n < N) epi.apply(m, n, v[g], pre[q0 + g]);
+          if (lane_on && r < R && m < M && n < N) {
+            if constexpr (requires { epi.col_ctx(0); })
+              epi.apply_c(m, cctx, v[g]);
+            else
+              epi.apply(m, n, v[g], pre[q0 + g]);
+          }
         }
       }
     } else {
@@ -508,6 +523,10 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
       constexpr int NQT = WTN / CPI, GT = NQT < kEpiBatch ? NQT : kEpiBatch;
       static_assert(NQT % GT == 0, "whole batches");
       const int c = lane % CPT;
+      const auto rctx = [&] {  // per-lane row constants, once per round
+        if constexpr (requires { epi.row_ctx(0); }) return epi.row_ctx(min(mr + c * 4, M - 1));
+        else return 0;
+      }();
 #pragma unroll
       for (int q0 = 0; q0 < NQT; q0 += GT) {
         f32x4_t v[GT];
@@ -520,7 +539,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
           const int m = mr + c * 4, n = nw + (q0 + g) * CPI + lane / CPT;
-          if (m < M && n < N) epi.apply_t(m, n, v[g]);
+          if (m < M && n < N) {
+            if constexpr (requires { epi.row_ctx(0); })
+              epi.apply_tc(m, rctx, n, v[g]);
+            else
+              epi.apply_t(m, n, v[g]);
+          }
         }
       }
     }
