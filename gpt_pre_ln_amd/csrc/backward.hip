@@ -749,7 +749,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reg_kernel(const bf16_t* __re
   const float lq = lse[(size_t)bh * T_seq + qc];
   const float dvq = dvec[(size_t)bh * T_seq + qc];
   fetch(0);
-  wait_vmcnt_bwd<4>();  // the wave's own rows are in; the first tile's four loads may not be
   const float l2 = lq * kLog2e;
   f32x4_t dq[4];
 #pragma unroll
