@@ -297,12 +297,20 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const int2* __restrict
   const int2* pr = part + (size_t)row * nseg;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int s = lane; s < nseg; s += 64) {
-    const int2 q = pr[s];
-    const float v = __builtin_bit_cast(float, q.x);
-    if (v > best) {
-      best = v;
-      bi = q.y;
+  // eight slices per lane requested at once (past the end: the last slice
+  // again, not compared), then compared in increasing order
+  constexpr int U = 8;
+  for (int s0 = lane; s0 < nseg; s0 += 64 * U) {
+    int2 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) q[u] = pr[min(s0 + 64 * u, nseg - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float v = __builtin_bit_cast(float, q[u].x);
+      if (s0 + 64 * u < nseg && v > best) {
+        best = v;
+        bi = q[u].y;
+      }
     }
   }
 #pragma unroll
