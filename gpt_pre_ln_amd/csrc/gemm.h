@@ -231,6 +231,20 @@ struct EpiLogits {
     }
   }
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
+  // bf16 logits only: v = C[m][n .. n+7] already packed (two per 32 bits),
+  // one 16-byte store
+  template <typename Q = O>
+    requires(sizeof(Q) == 2)
+  __device__ __forceinline__ void store8_packed(int m, int n, const u32x4_t& v) const {
+    O* p = out + (size_t)m * ldo + n;
+    if (n + 7 < n_valid) {
+      __builtin_nontemporal_store(u32x4_u2_t{v[0], v[1], v[2], v[3]}, reinterpret_cast<u32x4_u2_t*>(p));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < n_valid) p[e].bits = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
   // bf16 logits only: a = C[m][n .. n+3], b = C[m][n+4 .. n+7], one 16-byte store
   template <typename Q = O>
     requires(sizeof(Q) == 2)

@@ -391,6 +391,45 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
   const int mw = m0 + wm * WTM, nw = n0 + wn * WTN;
   const bool tr = Epi::kTransposed && epi.transposed(nw);
 
+  constexpr int CH = WTN / 8;  // 16-byte chunks per row of a bf16-staged sub-tile
+  constexpr bool kStageB16 = requires { epi.store8_packed(0, 0, u32x4_t{}); } && WTN % 8 == 0 &&
+                             (CH & (CH - 1)) == 0 && CH <= 64 && WTM % (64 / CH) == 0 &&
+                             WTM * WTN * 2 <= PER_WAVE * 4;
+  if constexpr (kStageB16) {
+    // bf16 output staged as bf16: the whole WTM x WTN sub-tile in one round
+    // (rows of WTN/8 16-byte chunks, XOR-swizzled by row), half the LDS bytes
+    // of fp32 staging; each lane then stores 8 consecutive columns
+    char* sb = reinterpret_cast<char*>(stg);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = i * 16 + lr, ch = 2 * j + (lg >> 1);
+        *reinterpret_cast<u32x2_t*>(sb + r * (WTN * 2) + ((ch ^ (r & (CH - 1))) << 4) + (lg & 1) * 8) =
+            u32x2_t{pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3])};
+      }
+    constexpr int RPW = 64 / CH, NQ8 = WTM / RPW, G = NQ8 < kEpiBatch ? NQ8 : kEpiBatch;
+    static_assert(NQ8 % G == 0, "whole batches");
+    const int cc = lane % CH;
+    const int n = nw + cc * 8;
+#pragma unroll
+    for (int q0 = 0; q0 < NQ8; q0 += G) {
+      u32x4_t v[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int r = (q0 + g) * RPW + lane / CH;
+        v[g] = *reinterpret_cast<const u32x4_t*>(sb + r * (WTN * 2) + ((cc ^ (r & (CH - 1))) << 4));
+      }
+      asm volatile("" ::: "memory");  // the batch's reads stay together
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int m = mw + (q0 + g) * RPW + lane / CH;
+        if (m < M && n < N) epi.store8_packed(m, n, v[g]);
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int rd = 0; rd < WTM / R; ++rd) {
     const int mr = mw + rd * R;  // first row of this round
