@@ -177,18 +177,21 @@ struct EpiResidual {
   __device__ __forceinline__ void apply_t(int, int, const f32x4_t&) const {}
 };
 
-template <typename T>
+// kErf picks the GELU form at compile time (false: gelu_new, the tanh form;
+// true: the erf GELU).  As a run-time flag it put both forms and a branch
+// around every four outputs of the epilogue, so the compiler could not
+// overlap the exponentials and reciprocals of a batch of staged reads.
+template <typename T, bool kErf = false>
 struct EpiGelu {
   static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false, kRowArgmax = false;
   const float* bias;  // [N]
   T* u;               // [M][ldu]
   int ldu;
-  int erf_form;       // 0: gelu_new (tanh form), 1: the erf GELU
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
-    if (erf_form)
+    if constexpr (kErf)
       Elem<T>::store4(u + (size_t)m * ldu + n, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3]));
     else
       Elem<T>::store4(u + (size_t)m * ldu + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
@@ -283,7 +286,7 @@ struct EpiStore {
 
 // c_fc of the recomputed forward: as EpiGelu, and the pre-activation (with
 // bias) kept in fp32 for the derivative.
-template <typename T>
+template <typename T, bool kErf = false>
 struct EpiGeluSave {
   static constexpr bool kPreload = false, kBias = true, kTransposed = false, kRowReduce = false,
                         kRowArgmax = false;
@@ -291,13 +294,12 @@ struct EpiGeluSave {
   T* u;               // [M][ld]
   float* g;           // [M][ld]
   int ld;
-  int erf_form;
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int, int) const { return float4{}; }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4&) const {
     *reinterpret_cast<float4*>(g + (size_t)m * ld + n) = make_float4(v[0], v[1], v[2], v[3]);
-    if (erf_form)
+    if constexpr (kErf)
       Elem<T>::store4(u + (size_t)m * ld + n, gelu_erf(v[0]), gelu_erf(v[1]), gelu_erf(v[2]), gelu_erf(v[3]));
     else
       Elem<T>::store4(u + (size_t)m * ld + n, gelu_tanh(v[0]), gelu_tanh(v[1]), gelu_tanh(v[2]), gelu_tanh(v[3]));
@@ -306,14 +308,13 @@ struct EpiGeluSave {
 };
 
 // dG = dU * act'(G): C is dU = dY W_pr^T, G the kept pre-activation.
-template <typename T>
+template <typename T, bool kErf = false>
 struct EpiGeluBwd {
   static constexpr bool kPreload = true, kBias = false, kTransposed = false, kRowReduce = false,
                         kRowArgmax = false;
   const float* g;  // [M][ld]
   T* dg;           // [M][ld]
   int ld;
-  int erf_form;
   __device__ __forceinline__ float4 bias4(int) const { return float4{}; }
   __device__ __forceinline__ float4 preload(int m, int n) const {
     return *reinterpret_cast<const float4*>(g + (size_t)m * ld + n);
@@ -321,7 +322,7 @@ struct EpiGeluBwd {
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4& x) const {
     float d0, d1, d2, d3;
-    if (erf_form) {
+    if constexpr (kErf) {
       d0 = gelu_erf_grad(x.x), d1 = gelu_erf_grad(x.y), d2 = gelu_erf_grad(x.z), d3 = gelu_erf_grad(x.w);
     } else {
       d0 = gelu_tanh_grad(x.x), d1 = gelu_tanh_grad(x.y), d2 = gelu_tanh_grad(x.z), d3 = gelu_tanh_grad(x.w);

@@ -758,20 +758,22 @@ template hipError_t launch_gemm_skinny_splitk<float>(const float*, const float*,
 template hipError_t launch_gemm_skinny_splitk<bf16_t>(const bf16_t*, const bf16_t*, int, int, int, int, int, float*,
                                                       hipStream_t);
 
-#define GPT2_INSTANTIATE_GEMM(T, EPI)                                                               \
-  template hipError_t launch_gemm<T, EPI>(GemmTile, const T*, const T*, int, int, int, int, int, \
-                                          const EPI&, hipStream_t);                                      \
-  template hipError_t launch_gemm_skinny<T, EPI>(const T*, const T*, int, int, int, int, int, const EPI&,         \
-                                                 hipStream_t);
+#define GPT2_INSTANTIATE_GEMM(T, ...)                                                                   \
+  template hipError_t launch_gemm<T, __VA_ARGS__>(GemmTile, const T*, const T*, int, int, int, int, int, \
+                                                  const __VA_ARGS__&, hipStream_t);                      \
+  template hipError_t launch_gemm_skinny<T, __VA_ARGS__>(const T*, const T*, int, int, int, int, int,    \
+                                                         const __VA_ARGS__&, hipStream_t);
 
 GPT2_INSTANTIATE_GEMM(float, EpiQKV<float>)
 GPT2_INSTANTIATE_GEMM(float, EpiResidual)
-GPT2_INSTANTIATE_GEMM(float, EpiGelu<float>)
+GPT2_INSTANTIATE_GEMM(float, EpiGelu<float, false>)
+GPT2_INSTANTIATE_GEMM(float, EpiGelu<float, true>)
 GPT2_INSTANTIATE_GEMM(float, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(float, EpiLogits<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiQKV<bf16_t>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiResidual)
-GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t>)
+GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t, false>)
+GPT2_INSTANTIATE_GEMM(bf16_t, EpiGelu<bf16_t, true>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<float>)
 GPT2_INSTANTIATE_GEMM(bf16_t, EpiLogits<bf16_t>)
 template <typename T>
@@ -813,14 +815,17 @@ template hipError_t launch_gemm<bf16_t, EpiStore<float>>(GemmTile, const bf16_t*
                                                          int, const EpiStore<float>&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiStore<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
                                                           int, int, const EpiStore<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm<float, EpiGeluSave<float>>(GemmTile, const float*, const float*, int, int, int, int,
-                                                           int, const EpiGeluSave<float>&, hipStream_t);
-template hipError_t launch_gemm<bf16_t, EpiGeluSave<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
-                                                             int, int, const EpiGeluSave<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm<float, EpiGeluBwd<float>>(GemmTile, const float*, const float*, int, int, int, int,
-                                                          int, const EpiGeluBwd<float>&, hipStream_t);
-template hipError_t launch_gemm<bf16_t, EpiGeluBwd<bf16_t>>(GemmTile, const bf16_t*, const bf16_t*, int, int, int,
-                                                            int, int, const EpiGeluBwd<bf16_t>&, hipStream_t);
+#define GPT2_INSTANTIATE_GEMM_TILED(T, ...)                                                          \
+  template hipError_t launch_gemm<T, __VA_ARGS__>(GemmTile, const T*, const T*, int, int, int, int, int, \
+                                                  const __VA_ARGS__&, hipStream_t);
+GPT2_INSTANTIATE_GEMM_TILED(float, EpiGeluSave<float, false>)
+GPT2_INSTANTIATE_GEMM_TILED(float, EpiGeluSave<float, true>)
+GPT2_INSTANTIATE_GEMM_TILED(bf16_t, EpiGeluSave<bf16_t, false>)
+GPT2_INSTANTIATE_GEMM_TILED(bf16_t, EpiGeluSave<bf16_t, true>)
+GPT2_INSTANTIATE_GEMM_TILED(float, EpiGeluBwd<float, false>)
+GPT2_INSTANTIATE_GEMM_TILED(float, EpiGeluBwd<float, true>)
+GPT2_INSTANTIATE_GEMM_TILED(bf16_t, EpiGeluBwd<bf16_t, false>)
+GPT2_INSTANTIATE_GEMM_TILED(bf16_t, EpiGeluBwd<bf16_t, true>)
 template hipError_t launch_gemm<float, EpiArgmax>(GemmTile, const float*, const float*, int, int, int, int, int,
                                                   const EpiArgmax&, hipStream_t);
 template hipError_t launch_gemm<bf16_t, EpiArgmax>(GemmTile, const bf16_t*, const bf16_t*, int, int, int, int, int,

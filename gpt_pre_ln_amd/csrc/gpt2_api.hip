@@ -10,6 +10,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/gpt2.h"
@@ -344,6 +345,15 @@ hipError_t proj_gemm(const T* A, const T* Bw, int M, int N, int K, const Epi& ep
   return launch_gemm<T>(pick_tile(M, N, K), A, Bw, M, N, K, K, K, epi, st);
 }
 
+// c_fc with its GELU epilogue, the form (0: gelu_new, 1: erf) chosen here
+// once so that each kernel carries one form only.
+template <typename T>
+hipError_t c_fc_gemm(int erf, const T* h, const T* w_fc, const float* b_fc, T* u, int M, int F, int D,
+                     hipStream_t st) {
+  if (erf) return proj_gemm<T>(h, w_fc, M, F, D, EpiGelu<T, true>{b_fc, u, F}, st);
+  return proj_gemm<T>(h, w_fc, M, F, D, EpiGelu<T, false>{b_fc, u, F}, st);
+}
+
 // Weight read-ahead.  Inside a forward a layer's weight matrices have dropped
 // out of the caches by the time they are used again (the activations stream
 // several hundred MB between two uses), and a GEMM that meets its weights cold
@@ -457,8 +467,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     }
     {
       TimedScope ts(m, kFC, st);
-      EpiGelu<T> e{pf(m, o.b_fc), u, F, c.activation};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
+      GPT2_HIP(c_fc_gemm<T>(c.activation, h, pp<T>(m, o.w_fc), pf(m, o.b_fc), u, M, F, D, st), "c_fc");
     }
     {
       TimedScope ts(m, kMLPProj, st);
@@ -578,8 +587,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
                                  pf(m, o.b_o)),
              post ? "ln_1" : "ln_2");
     {
-      EpiGelu<T> e{pf(m, o.b_fc), u, F, c.activation};
-      GPT2_HIP(proj_gemm<T>(h, pp<T>(m, o.w_fc), M, F, D, e, st), "c_fc");
+      GPT2_HIP(c_fc_gemm<T>(c.activation, h, pp<T>(m, o.w_fc), pf(m, o.b_fc), u, M, F, D, st), "c_fc");
     }
     if (split) {
       GPT2_HIP(launch_gemm_skinny_splitk<T>(u, pp<T>(m, o.w_pr), M, D, F, F, F, rpart, st), "mlp.c_proj");
@@ -800,15 +808,21 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
   }
   GPT2_HIP(launch_layernorm<T>(xh, pf(m, o.ln2_g), pf(m, o.ln2_b), h2, nullptr, M, D, c.ln_eps, st), "bwd ln_2");
   {
-    EpiGeluSave<T> e{pf(m, o.b_fc), u, gpre, F, c.activation};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, F, D), h2, pp<T>(m, o.w_fc), M, F, D, D, D, e, st), "bwd c_fc");
+    auto fc = [&](auto erf) {
+      EpiGeluSave<T, decltype(erf)::value> e{pf(m, o.b_fc), u, gpre, F};
+      return launch_gemm<T>(pick_tile(M, F, D), h2, pp<T>(m, o.w_fc), M, F, D, D, D, e, st);
+    };
+    GPT2_HIP(c.activation ? fc(std::true_type{}) : fc(std::false_type{}), "bwd c_fc");
   }
 
   // MLP
   GPT2_HIP(launch_convert<T>(dy, dyt, (size_t)M * D, (size_t)M * D, st), "bwd dy");
   {
-    EpiGeluBwd<T> e{gpre, dg, F, c.activation};
-    GPT2_HIP(launch_gemm<T>(pick_tile(M, F, D), dyt, wt_pr, M, F, D, D, D, e, st), "bwd du");
+    auto du = [&](auto erf) {
+      EpiGeluBwd<T, decltype(erf)::value> e{gpre, dg, F};
+      return launch_gemm<T>(pick_tile(M, F, D), dyt, wt_pr, M, F, D, D, D, e, st);
+    };
+    GPT2_HIP(c.activation ? du(std::true_type{}) : du(std::false_type{}), "bwd du");
   }
   // column sums: first passes into their own partial slots now (their sources
   // are overwritten later), one grouped second pass at the end
