@@ -435,7 +435,15 @@ struct EpiSample {
 // Host launchers (gemm.hip).  Shapes: A [M][lda], B [N][ldb] (K contiguous),
 // K % (128 / sizeof(T)) == 0, N % 4 == 0.  `tile` picks the tile shape
 // (see gemm.hip); returns hipSuccess or the launch error.
-enum GemmTile { kTile128x128 = 0, kTile256x256 = 1, kTile64x64 = 2, kTile32x64 = 3, kTile64x128 = 4, kTile128x96 = 5 };
+enum GemmTile {
+  kTile128x128 = 0,
+  kTile256x256 = 1,
+  kTile64x64 = 2,
+  kTile32x64 = 3,
+  kTile64x128 = 4,
+  kTile128x96 = 5,
+  kTile128x192 = 6  // 8 waves of 64x48, one block per CU
+};
 
 // Width of the column slice one wave owns in `tile` (the kRowReduce slice).
 int gemm_slice_width(GemmTile tile);

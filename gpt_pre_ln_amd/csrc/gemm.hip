@@ -559,7 +559,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_kernel(const T* __restrict
             stg[col * R + (((r >> 2) ^ (col & (CPT - 1))) << 2) + (r & 3)] = acc[rd * (R / 16) + i][j][e];
           }
       constexpr int CPI = 64 / CPT;  // columns per read instruction
-      constexpr int NQT = WTN / CPI, GT = NQT < kEpiBatch ? NQT : kEpiBatch;
+      constexpr int NQT = WTN / CPI;
+      constexpr int GT = NQT <= kEpiBatch ? NQT : NQT % kEpiBatch == 0 ? kEpiBatch : NQT % 3 == 0 ? 3 : NQT % 2 == 0 ? 2 : 1;
       static_assert(NQT % GT == 0, "whole batches");
       const int c = lane % CPT;
       const auto rctx = [&] {  // per-lane row constants, once per round
@@ -701,6 +702,7 @@ int gemm_slice_width(GemmTile tile) {
     case kTile32x64: return 64 / 2;
     case kTile64x128: return 128 / 2;
     case kTile128x96: return 96 / 2;
+    case kTile128x192: return 192 / 4;
     case kTile128x128:
     default: return 128 / 2;
   }
@@ -720,6 +722,8 @@ hipError_t launch_gemm(GemmTile tile, const T* A, const T* B, int M, int N, int 
       return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x96:
       return launch_tile<T, 128, 96, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
+    case kTile128x192:
+      return launch_tile<T, 128, 192, 2, 4, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
     case kTile128x128:
     default:
       return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K, lda, ldb, epi, stream);
@@ -792,6 +796,9 @@ hipError_t launch_gemm_splitk(GemmTile tile, const T* A, const T* B, int M, int 
       return launch_tile<T, 64, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
     case kTile128x96:
       return launch_tile<T, 128, 96, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream, splits);
+    case kTile128x192:
+      return launch_tile<T, 128, 192, 2, 4, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream,
+                                                                    splits);
     case kTile128x128:
     default:
       return launch_tile<T, 128, 128, 2, 2, 2, kPrio | kInterleave>(A, B, M, N, K_split, lda, ldb, epi, stream,

@@ -159,19 +159,31 @@ std::vector<gpt2_param_info> param_table(const gpt2_config& c) {
 }
 
 // Tile shape per GEMM: 256x256 only where there are enough tiles to fill the
-// 256 CUs many times over (the lm_head); 128x128 (2 blocks per CU) or 64x128
-// (3 blocks per CU) otherwise.
+// 256 CUs many times over (the lm_head); then 128x192 (8 waves, one block
+// per CU) or 128x96 (2 blocks per CU) where their grids fill whole rounds;
+// 128x128 (2 blocks per CU) or 64x128 (3 blocks per CU) otherwise.
 GemmTile pick_tile(int M, int N, int K) {
   if (M <= 32) return kTile32x64;
   if (M <= 64) return kTile64x64;
   const long tiles256 = (long)((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= 8 * 256) return kTile256x256;
+  // 128x192 with 8 waves of 64x48 (one block per CU, 80 KB of LDS) where
+  // its grid fills at least three whole rounds of the 256 CUs: per CU it
+  // streams 320 operand rows per k step for the same 8 wave tiles that two
+  // 128x96 blocks feed with 448.  GPT-2 small at B*T = 8192: qkv (768 tiles)
+  // and c_fc (1,024); standalone 38.4 -> 33.6 us and 47.0 -> 45.0 us.  The
+  // one-round c_proj grids measured slower on it (17.9 -> 18.8 and 42.6 ->
+  // 44.5 us) and stay below.
+  {
+    const long t192 = (long)((M + 127) / 128) * ((N + 191) / 192);
+    if (N % 192 == 0 && t192 % 256 == 0 && t192 >= 3 * 256) return kTile128x192;
+  }
   // 128x96 (2 blocks per CU) where its grid fills whole rounds of the 512
   // block slots and the 128x128 grid does not: per CU round it streams 448
   // operand rows against 512 for 128x128 and 576 for 64x128.  GPT-2 small at
-  // B*T = 8192: qkv (1,536 tiles, 3 full rounds), attn.c_proj and mlp.c_proj
-  // (512 tiles, 1 round); measured 5-7 % faster per launch than 64x128 or
-  // 128x128 on those shapes.
+  // B*T = 8192: attn.c_proj and mlp.c_proj (512 tiles, 1 round; qkv's 1,536
+  // tiles too, before the 128x192 rule); measured 5-7 % faster per launch
+  // than 64x128 or 128x128 on those shapes.
   {
     constexpr long kSlots = 2 * 256;
     const long t96 = (long)((M + 127) / 128) * ((N + 95) / 96);
@@ -650,6 +662,7 @@ int wgrad_splits(int Mr, int N, int Mp) {
     case kTile32x64: bm = 32, bn = 64; break;
     case kTile64x128: bm = 64, bn = 128; break;
     case kTile128x96: bm = 128, bn = 96; break;
+    case kTile128x192: bm = 128, bn = 192; break;
     default: break;
   }
   const long tiles = (long)((Mr + bm - 1) / bm) * ((N + bn - 1) / bn);

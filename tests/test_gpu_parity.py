@@ -329,7 +329,8 @@ def test_gpt2_small_b8t1024():
 
 def test_gpt2_small_shape_fp32():
     """The GPT-2 small shape in fp32 (fp32 MFMA operands, fp32 logits) at
-    B=8 T=1024: the 128x96 projection tiles and the 256x256 lm_head on the
+    B=8 T=1024: the 128x192 (qkv, c_fc) and 128x96 (c_proj) projection tiles
+    and the 256x256 lm_head on the
     fp32 path, checked to the fp32 tolerance and exact argmax on one sequence."""
     w = W.WORKLOADS["gpt2-small-b8t1024"]
     _announce(f"{w.name} shape in f32 B={w.batch} T={w.seq_len}")
@@ -346,8 +347,9 @@ def test_gpt2_small_shape_fp32():
 
 def test_gpt2_small_b8t1020_ragged_tiles():
     """B*T = 8160 is not a multiple of the 128-row tiles, and T = 1020 puts
-    sequence boundaries inside tiles: the 128x96 projections (qkv, both
-    c_proj) and the 256x256 lm_head with its ragged last tile-row."""
+    sequence boundaries inside tiles: the 128x192 (qkv, c_fc) and 128x96
+    (both c_proj) projections and the 256x256 lm_head with its ragged last
+    tile-row."""
     w = W.WORKLOADS["gpt2-small-b8t1024"]
     T = 1020
     _announce(f"{w.name} shape B={w.batch} T={T}")
