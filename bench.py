@@ -86,9 +86,9 @@ def class_work(shape, B, T, cls):
 # kernel of each class in the traffic summary (the tile and schedule-knob
 # fields of the GEMM template may vary)
 TRAFFIC_KERNELS = {"lm_head_gemm": r"void gemm_kernel<bf16_t, 256, 256, 2, 4, 2, \d+, EpiLogits<bf16_t> >",
-                   "fc_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, 2, 2, 2, \d+, EpiGelu<bf16_t> >",
-                   "qkv_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, 2, 2, 2, \d+, EpiQKV<bf16_t> >",
-                   "attention": r"void attn_prefill_kernel<bf16_t, 64>",
+                   "fc_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, \d+, \d+, 2, \d+, EpiGelu<bf16_t, false> >",
+                   "qkv_gemm": r"void gemm_kernel<bf16_t, \d+, \d+, \d+, \d+, 2, \d+, EpiQKV<bf16_t> >",
+                   "attention": r"void attn_prefill_kernel<bf16_t, 64, \d+>",
                    "layernorm": r"void layernorm_kernel<bf16_t, 3>"}
 
 
