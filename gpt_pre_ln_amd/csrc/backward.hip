@@ -8,7 +8,11 @@ namespace gpt2 {
 
 namespace {
 
-constexpr int kColChunks = 64;  // row chunks of the first column-sum pass
+// Row chunks of the first column-sum pass: 256 chunks of 32 rows at B*T =
+// 8192 give a 768-column fp32 sum 768 blocks (3 per CU); with 64 chunks its
+// 192 blocks kept too few loads in flight (2.9 TB/s).
+constexpr int kColChunks = 256;
+constexpr int kColFinalBatch = 32;  // partials per column a thread of the second pass has in flight
 constexpr int kColBatch = 8;    // rows per thread with loads in flight together
 
 // 32x32 tile transpose through LDS; 256 threads = 32 x 8.  Tiles cover dst
@@ -184,27 +188,47 @@ __global__ __launch_bounds__(256) void colsum_partial_vec_kernel(const Tin* __re
   }
 }
 
-// Second pass for several column sums in one launch (blockIdx.y = job):
-// out[n] = sum over row chunks rc of part[rc][n], in increasing rc.
+// Second pass: out[n] = sum over the kColChunks partials part[rc][n].  A
+// block takes 64 columns with 4 threads each: thread group g sums chunks
+// g*Q .. (g+1)*Q - 1 in increasing rc (Q = kColChunks / 4, loads in flight
+// kColFinalBatch at a time), then the four group sums are added in order g =
+// 0..3, so the result does not depend on timing.
+constexpr int kColFinalGroups = 4;
+__device__ __forceinline__ void sum_chunks_block(const float* __restrict__ part, int N, float* __restrict__ out) {
+  constexpr int Q = kColChunks / kColFinalGroups;
+  static_assert(Q % kColFinalBatch == 0, "whole batches");
+  __shared__ float red[kColFinalGroups][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + c;
+  float s = 0.f;
+  if (n < N) {
+    for (int rc0 = g * Q; rc0 < (g + 1) * Q; rc0 += kColFinalBatch) {
+      float v[kColFinalBatch];
+#pragma unroll
+      for (int u = 0; u < kColFinalBatch; ++u) v[u] = part[(size_t)(rc0 + u) * N + n];
+#pragma unroll
+      for (int u = 0; u < kColFinalBatch; ++u) s += v[u];
+    }
+  }
+  red[g][c] = s;
+  __syncthreads();
+  if (g == 0 && n < N) out[n] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+// Second pass for several column sums in one launch (blockIdx.y = job), each
+// summed as in sum_chunks_block.
 struct ColsumFinalArgs {
   ColsumJob job[kMaxColsumJobs];
 };
 __global__ __launch_bounds__(256) void colsum_final_group_kernel(ColsumFinalArgs a) {
   const ColsumJob j = a.job[blockIdx.y];
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= j.N) return;
-  float s = 0.f;
-  for (int rc = 0; rc < kColChunks; ++rc) s += j.part[(size_t)rc * j.N + n];
-  j.out[n] = s;
+  if (blockIdx.x * 64 >= j.N) return;  // block-uniform
+  sum_chunks_block(j.part, j.N, j.out);
 }
 
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int N,
                                                             float* __restrict__ out) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float s = 0.f;
-  for (int rc = 0; rc < kColChunks; ++rc) s += part[(size_t)rc * N + n];
-  out[n] = s;
+  sum_chunks_block(part, N, out);
 }
 
 // One wave per row; lane holds float4 groups c = lane*4 + i*256 (as the
@@ -873,7 +897,7 @@ hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, 
     else
       hipLaunchKernelGGL((colsum_partial_vec_kernel<Tin, false>), gridv, dim3(256), 0, stream, src, M, N, part, x,
                          mu, rstd, nullptr);
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 63) / 64), dim3(256), 0, stream, part, N, out);
     return hipGetLastError();
   }
   const dim3 grid1((N + 63) / 64, kColChunks);
@@ -882,7 +906,7 @@ hipError_t launch_colsum(const Tin* src, int M, int N, float* out, float* part, 
   else
     hipLaunchKernelGGL((colsum_partial_kernel<Tin, false>), grid1, dim3(256), 0, stream, src, M, N, part, x, mu,
                        rstd);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, N, out);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((N + 63) / 64), dim3(256), 0, stream, part, N, out);
   return hipGetLastError();
 }
 
@@ -924,7 +948,7 @@ hipError_t launch_colsum_final(const ColsumJob* jobs, int n_jobs, hipStream_t st
     n_max = std::max(n_max, jobs[i].N);
   }
   if (n_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(colsum_final_group_kernel, dim3((n_max + 255) / 256, n_jobs), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(colsum_final_group_kernel, dim3((n_max + 63) / 64, n_jobs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
