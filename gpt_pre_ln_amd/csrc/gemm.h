@@ -166,9 +166,12 @@ struct EpiResidual {
   const float* bias;  // [N]
   float* x;           // [M][ldx] fp32 residual stream, updated in place
   int ldx;
+  // When set, the residual is read from here ([M][ldx]) and x = xin + C is
+  // written: the update goes to a copy without copying first.
+  const float* xin = nullptr;
   __device__ __forceinline__ float4 bias4(int n) const { return *reinterpret_cast<const float4*>(bias + n); }
   __device__ __forceinline__ float4 preload(int m, int n) const {
-    return *reinterpret_cast<const float4*>(x + (size_t)m * ldx + n);
+    return *reinterpret_cast<const float4*>((xin ? xin : x) + (size_t)m * ldx + n);
   }
   __device__ __forceinline__ bool transposed(int) const { return false; }
   __device__ __forceinline__ void apply(int m, int n, const f32x4_t& v, const float4& r) const {

@@ -814,9 +814,8 @@ gpt2_status run_block_backward(gpt2_model* m, int l, int B, int T_seq, const flo
     GPT2_HIP(launch_gemm<T>(pick_tile(M, 3 * D, D), h1, pp<T>(m, o.w_qkv), M, 3 * D, D, D, D, e, st), "bwd c_attn");
   }
   GPT2_HIP(launch_attention_prefill<T>(q, kk, vt, a, B, H, T_seq, Tp, hs, st, lse), "bwd attention");
-  GPT2_HIP(hipMemcpyAsync(xh, x, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st), "bwd residual copy");
   {
-    EpiResidual e{pf(m, o.b_o), xh, D};
+    EpiResidual e{pf(m, o.b_o), xh, D, x};  // xh = x + attn.c_proj(a)
     GPT2_HIP(launch_gemm<T>(pick_tile(M, D, D), a, pp<T>(m, o.w_o), M, D, D, D, D, e, st), "bwd attn.c_proj");
   }
   GPT2_HIP(launch_layernorm<T>(xh, pf(m, o.ln2_g), pf(m, o.ln2_b), h2, nullptr, M, D, c.ln_eps, st), "bwd ln_2");
