@@ -428,13 +428,21 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
     return ((last + last_elems * sizeof(T)) - first) / 16 * 16;
   };
 
-  {
-    TimedScope ts(m, kEmbed, st);
-    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, V, m->id_flag, st), "embed");
-  }
   // Post-LN: the first block's attention reads the embeddings themselves (an
   // operand copy of x); later blocks read the output of the previous ln_2.
   const bool post = c.post_ln != 0;
+  if (post) {
+    TimedScope ts(m, kEmbed, st);
+    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, V, m->id_flag, st), "embed");
+  } else {
+    // Pre-LN: the embedding and the first block's ln_1 in one pass
+    const LayerOff& o0 = m->lay.layers[0];
+    TimedScope ts(m, kEmbed, st);
+    GPT2_HIP(launch_embed_layernorm<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, T_seq, 0, D, V,
+                                       m->id_flag, pf(m, o0.ln1_g), pf(m, o0.ln1_b), h, c.ln_eps, st,
+                                       pre ? m->params + o0.w_qkv : nullptr, span(o0.w_qkv, o0.w_o, (size_t)D * D)),
+             "embed + ln_1");
+  }
   if (post) GPT2_HIP(launch_convert<T>(x, h, (size_t)M * D, (size_t)M * D, st), "post-ln input");
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& o = m->lay.layers[l];
@@ -449,7 +457,7 @@ gpt2_status run_forward(gpt2_model* m, const int32_t* tokens, int B, int T_seq, 
       vtl = reinterpret_cast<T*>(m->ws + W.vt);
     }
     const float q_scale_l = c.scale_attn_by_inverse_layer_idx ? q_scale / (float)(l + 1) : q_scale;
-    if (!post) {
+    if (!post && l > 0) {  // layer 0's ln_1 ran with the embedding
       TimedScope ts(m, kLN, st);
       GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st,
                                    pre ? m->params + o.w_qkv : nullptr, span(o.w_qkv, o.w_o, (size_t)D * D)),

@@ -35,6 +35,15 @@ hipError_t launch_layernorm(float* x, const float* gamma, const float* beta, T* 
                             size_t prefetch_bytes = 0, const float* rpart = nullptr, int rks = 0,
                             const float* rbias = nullptr);
 
+// launch_embed followed by launch_layernorm(x, gamma, beta, y, nullptr, M, D,
+// eps, stream, prefetch, prefetch_bytes) in one pass where d_model is 768 or
+// 1024 (the row is normalised from the registers it was summed in: the same
+// bits, without re-reading x); two launches otherwise.
+template <typename T>
+hipError_t launch_embed_layernorm(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq,
+                                  int pos0, int D, int V, int32_t* bad, const float* gamma, const float* beta, T* y,
+                                  float eps, hipStream_t stream, const void* prefetch, size_t prefetch_bytes);
+
 // dst[n][k] = convert(src[k][n]) for a [K][N] fp32 source (Conv1D [in, out]
 // -> [out, in]); dst rows N..N_pad-1 are zero-filled.
 template <typename T>

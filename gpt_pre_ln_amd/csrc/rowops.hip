@@ -119,6 +119,49 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* x, const fl
   layernorm_row<T, NV>(v, gv, bv, lane, row, D, eps, y, y32);
 }
 
+// embed_kernel and layernorm_kernel in one pass (d_model = 256 * NV): the
+// row x = wte[id] + wpe[pos] is stored, then normalised from the registers
+// holding it, by layernorm_row as in layernorm_kernel (same bits), after the
+// same optional read-ahead of the following GEMMs' weights.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void embed_layernorm_kernel(const int32_t* __restrict__ ids,
+                                                               const T* __restrict__ wte, const T* __restrict__ wpe,
+                                                               float* __restrict__ x, int M, int T_seq, int pos0,
+                                                               int D, int V, int32_t* __restrict__ bad,
+                                                               const float* __restrict__ gamma,
+                                                               const float* __restrict__ beta, T* __restrict__ y,
+                                                               float eps, const u32x4_t* __restrict__ pf,
+                                                               size_t pf16) {
+  static_assert(NV > 0, "whole 256-column groups");
+  if (pf16) {
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < pf16; i += (size_t)gridDim.x * 256) acc ^= pf[i];
+    asm volatile("" ::"v"(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
+  }
+  const int row = xcd_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int raw = ids[row];
+  const int id = clamp_token_id(raw, V);
+  if (bad && id != raw && lane == 0) *bad = 1;
+  const int pos = pos0 + row % T_seq;
+  const T* we = wte + (size_t)id * D;
+  const T* pe = wpe + (size_t)pos * D;
+  float* xr = x + (size_t)row * D;
+  float4 v[NV], gv[NV], bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float4 a = Elem<T>::load4(we + lane * 4 + i * 256);
+    const float4 b = Elem<T>::load4(pe + lane * 4 + i * 256);
+    v[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    gv[i] = *reinterpret_cast<const float4*>(gamma + lane * 4 + i * 256);
+    bv[i] = *reinterpret_cast<const float4*>(beta + lane * 4 + i * 256);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) *reinterpret_cast<float4*>(xr + lane * 4 + i * 256) = v[i];
+  layernorm_row<T, NV>(v, gv, bv, lane, row, D, eps, y, nullptr);
+}
+
 // Residual add fused in front of the LayerNorm, for few rows: one block of
 // four waves per row.  x += (sum over s of rpart[s][row] + rbias) is written
 // back, then normalised.  Wave w sums the contiguous slices
@@ -426,11 +469,37 @@ hipError_t launch_convert(const float* src, T* dst, size_t n, size_t n_pad, hipS
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_embed_layernorm(const int32_t* ids, const T* wte, const T* wpe, float* x, int M, int T_seq,
+                                  int pos0, int D, int V, int32_t* bad, const float* gamma, const float* beta, T* y,
+                                  float eps, hipStream_t stream, const void* prefetch, size_t prefetch_bytes) {
+  if (V < 1) return hipErrorInvalidValue;
+  if (D != 768 && D != 1024) {
+    hipError_t e = launch_embed<T>(ids, wte, wpe, x, M, T_seq, pos0, D, V, bad, stream);
+    if (e != hipSuccess) return e;
+    return launch_layernorm<T>(x, gamma, beta, y, nullptr, M, D, eps, stream, prefetch, prefetch_bytes);
+  }
+  if (M == 0) return hipSuccess;
+  const dim3 grid((M + 3) / 4), block(256);
+  const u32x4_t* pf = static_cast<const u32x4_t*>(prefetch);
+  const size_t pf16 = prefetch ? prefetch_bytes / 16 : 0;
+  if (D == 768)
+    hipLaunchKernelGGL((embed_layernorm_kernel<T, 3>), grid, block, 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V,
+                       bad, gamma, beta, y, eps, pf, pf16);
+  else
+    hipLaunchKernelGGL((embed_layernorm_kernel<T, 4>), grid, block, 0, stream, ids, wte, wpe, x, M, T_seq, pos0, D, V,
+                       bad, gamma, beta, y, eps, pf, pf16);
+  return hipGetLastError();
+}
+
 #define GPT2_ROWOPS(T)                                                                                          \
   template hipError_t launch_embed<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, int, int32_t*,  \
                                       hipStream_t);                                                                 \
   template hipError_t launch_layernorm<T>(float*, const float*, const float*, T*, float*, int, int, float,          \
                                           hipStream_t, const void*, size_t, const float*, int, const float*);       \
+  template hipError_t launch_embed_layernorm<T>(const int32_t*, const T*, const T*, float*, int, int, int, int, int, \
+                                                int32_t*, const float*, const float*, T*, float, hipStream_t,     \
+                                                const void*, size_t);                                               \
   template hipError_t launch_transpose_convert<T>(const float*, T*, int, int, int, hipStream_t);                   \
   template hipError_t launch_convert<T>(const float*, T*, size_t, size_t, hipStream_t);
 
