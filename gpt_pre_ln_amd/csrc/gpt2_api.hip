@@ -574,11 +574,18 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
   const int kvT = kv_stride(kv->max_T);
   const float q_scale = 1.0f / std::sqrt((float)hs);
 
-  GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, V, m->id_flag, st), "embed");
   // Post-LN: each LayerNorm follows a residual add (ln_1 after attn.c_proj,
   // ln_2 after mlp.c_proj) and also writes the normalised row back to x; the
   // first block's attention reads an operand copy of the embeddings.
   const bool post = c.post_ln != 0;
+  if (post)
+    GPT2_HIP(launch_embed<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, V, m->id_flag, st),
+             "embed");
+  else  // Pre-LN: the embedding and the first block's ln_1 in one pass
+    GPT2_HIP(launch_embed_layernorm<T>(tokens, pp<T>(m, m->lay.wte), pp<T>(m, m->lay.wpe), x, M, 1, pos, D, V,
+                                       m->id_flag, pf(m, m->lay.layers[0].ln1_g), pf(m, m->lay.layers[0].ln1_b), h,
+                                       c.ln_eps, st, nullptr, 0),
+             "embed + ln_1");
   if (post) GPT2_HIP(launch_convert<T>(x, h, (size_t)M * D, (size_t)M * D, st), "post-ln input");
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& o = m->lay.layers[l];
@@ -586,7 +593,7 @@ gpt2_status run_decode(gpt2_model* m, gpt2_kv_view* kv, const int32_t* tokens, v
     T* kl = reinterpret_cast<T*>(base);
     T* vtl = reinterpret_cast<T*>(base + kv_layer_bytes(c, B, kv->max_T) / 2);
     const float q_scale_l = c.scale_attn_by_inverse_layer_idx ? q_scale / (float)(l + 1) : q_scale;
-    if (!post)
+    if (!post && l > 0)  // layer 0's ln_1 ran with the embedding
       GPT2_HIP(launch_layernorm<T>(x, pf(m, o.ln1_g), pf(m, o.ln1_b), h, nullptr, M, D, c.ln_eps, st, nullptr, 0,
                                    pending_bias ? rpart : nullptr, ks_p, pending_bias),
                "ln_1");
