@@ -1,13 +1,16 @@
 // Causal attention on gfx950 (see attention.h for what is computed).
 //
 // Prefill kernel (flash-style):
-//   * one block = 4 waves of QW queries (kPrefillQW = 16: 64 queries, 92
-//     registers, 5 waves per SIMD; 32 queries per wave took 156 registers and
-//     3 waves per SIMD, 1.5 % slower) of one (b, h); blocks of the longest
-//     query tiles are launched first (causal work grows with the tile index).
-//   * key tiles of 64 keys are staged in LDS (K as [key][d], V transposed as
-//     [d][key]) through a double-buffered ring; the next tile's global loads
-//     are in flight while the current one is on the matrix cores.
+//   * one block = 4 waves of QW queries (kPrefillQW = 16: 64 queries) of one
+//     (b, h); blocks of the longest query tiles are launched first (causal
+//     work grows with the tile index).
+//   * key tiles (kPrefillKeys: 32 keys for bf16, 64 for fp32) are staged in
+//     LDS (K as [key][d], V transposed as [d][key]) through a double-buffered
+//     ring; the next tile's global loads are in flight while the current one
+//     is on the matrix cores.  32-key bf16 tiles take 16 KB of LDS per block
+//     and 71 registers, so 7 waves share a SIMD (64-key tiles: 32 KB, 95
+//     registers, 5 waves); that outweighs their twice as many barriers and
+//     per-tile reductions.
 //   * each wave computes S^T = K Q^T with MFMA (lane l ends with 4 keys of one
 //     query), keeps a running max and sum per query (online softmax, fp32,
 //     the running max subtracted before exp as the llm.c notes advise), then
@@ -47,11 +50,16 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// Keys per K/V tile of the prefill kernel (fp32 keeps 64: with 32 keys its
+// head_dim-16 V^T tile would not split over the four waves' loads).
+template <typename T>
+constexpr int kPrefillKeys = sizeof(T) == 2 ? 32 : 64;
+
 template <typename T, int HS, int QW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 5 : 3))) void attn_prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? (sizeof(T) == 2 ? 6 : 5) : 3))) void attn_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt, T* __restrict__ out, int BH, int H,
     int Tq, int kvT, int n_qtiles, float* __restrict__ lse) {
-  constexpr int NW = 4, BQ = QW * NW, BKEYS = 64;
+  constexpr int NW = 4, BQ = QW * NW, BKEYS = kPrefillKeys<T>;
   constexpr int ESZ = (int)sizeof(T);
   constexpr int KROWB = HS * ESZ, KCH = KROWB / 16;     // K tile rows (keys)
   constexpr int VROWB = BKEYS * ESZ, VCH = VROWB / 16;  // V^T tile rows (d)
@@ -580,11 +588,11 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const float* __re
 
 constexpr int kPrefillQW = 16;  // queries per wave (see the kernel's notes)
 
-// Dynamic LDS of attn_prefill_kernel<T, HS, ...>: two K tiles (64 keys x HS)
-// and two V^T tiles (HS x 64 keys).
+// Dynamic LDS of attn_prefill_kernel<T, HS, ...>: two K tiles (kPrefillKeys
+// keys x HS) and two V^T tiles (HS x kPrefillKeys keys).
 template <typename T, int HS>
 constexpr size_t prefill_lds_bytes() {
-  return 2 * (64 * HS + HS * 64) * sizeof(T);
+  return 2 * (kPrefillKeys<T> * HS + HS * kPrefillKeys<T>) * sizeof(T);
 }
 
 template <typename T>
