@@ -31,7 +31,10 @@ HIP_FLAGS = [
 # (the softmax rescales them every tile; in AGPRs each rescale is a round trip
 # of v_accvgpr_read / v_accvgpr_write), and let max() skip NaN canonicalisation
 # (no NaN reaches it; masked scores are -inf, which stays allowed).
-SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+                # backward.hip: the same accumulator form, which takes the dQ kernel
+                # from 152 VGPRs + 48 AGPRs (2 waves per SIMD) to 136 VGPRs (3)
+                "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def source_files() -> list[str]:
