@@ -34,7 +34,11 @@ HIP_FLAGS = [
 SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
                 # backward.hip: the same accumulator form, which takes the dQ kernel
                 # from 152 VGPRs + 48 AGPRs (2 waves per SIMD) to 136 VGPRs (3)
-                "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                # gemm.hip: the same, so that the epilogues read the accumulators
+                # without first moving them out of AGPRs (128x96 tiles: 184-244
+                # registers in two files -> 122-132 VGPRs)
+                "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def source_files() -> list[str]:
