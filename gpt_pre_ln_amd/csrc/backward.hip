@@ -222,7 +222,7 @@ struct ColsumFinalArgs {
 };
 __global__ __launch_bounds__(256) void colsum_final_group_kernel(ColsumFinalArgs a) {
   const ColsumJob j = a.job[blockIdx.y];
-  if (blockIdx.x * 64 >= j.N) return;  // block-uniform
+  if ((int)blockIdx.x * 64 >= j.N) return;  // block-uniform
   sum_chunks_block(j.part, j.N, j.out);
 }
 

@@ -100,8 +100,8 @@ struct EpiQKV {
     const int hd = n - which * (int)D.d;
     const int head = hd >> hs_log2;
     const int d = hd - (head << hs_log2);
-    const size_t off = which == 0 ? ((size_t)head * Tq.d << hs_log2) + d
-                                  : ((size_t)head * kvT + t0 << hs_log2) + d;
+    const size_t off = which == 0 ? (((size_t)head * Tq.d) << hs_log2) + d
+                                  : (((size_t)head * kvT + t0) << hs_log2) + d;
     return ColCtx{which, n, off};
   }
   __device__ __forceinline__ void apply_c(int m, const ColCtx& c, const f32x4_t& v) const {
