@@ -84,8 +84,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QW == 16 ? 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x % BH;
-  const int qt = n_qtiles - 1 - blockIdx.x / BH;
+  // Work order: longest query tiles first, reversed within every other run
+  // of 256 blocks, so that the blocks one CU receives (one per run when all
+  // are resident) pair long tiles with short ones.
+  int widx = blockIdx.x;
+  {
+    const int run = widx >> 8, pos = widx & 255;
+    if ((run & 1) && (run << 8) + 256 <= (int)gridDim.x) widx = (run << 8) + (255 - pos);
+  }
+  const int bh = widx % BH;
+  const int qt = n_qtiles - 1 - widx / BH;
   const int b = bh / H, h = bh - b * H;
   const int D = H * HS;
 
