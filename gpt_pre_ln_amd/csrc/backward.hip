@@ -625,7 +625,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   __shared__ __attribute__((aligned(16))) char sO[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) float sL[2][kBT];
   __shared__ __attribute__((aligned(16))) float sD[2][kBT];
-  const int kt = blockIdx.x / BH, bh = blockIdx.x - kt * BH;  // key tile 0 (the longest) first
+  // Key tile 0 (the longest) first; within every other run of 256 blocks the
+  // order is reversed, so each CU's resident blocks mix long and short tiles.
+  int widx = blockIdx.x;
+  {
+    const int run = widx >> 8, pos = widx & 255;
+    if ((run & 1) && (run << 8) + 256 <= (int)gridDim.x) widx = (run << 8) + (255 - pos);
+  }
+  const int kt = widx / BH, bh = widx - kt * BH;
   const int b = bh / H, h = bh - b * H;
   const int j0 = kt * kBT;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
