@@ -97,10 +97,11 @@ CASES = [
     ("bf16", 192, 3, 1, 0, 3, 65, {}),                                  # general LayerNorm path
     ("bf16", 128, 2, 2, 1, 2, 100, dict(activation="gelu", scale_attn_by_inverse_layer_idx=True)),
     ("bf16", 128, 2, 1, 0, 1, 1, {}),                                   # a single position
+    ("bf16", 128, 2, 1, 0, 20, 1000, dict(n_positions=1024)),  # dK/dV grid of 640 blocks: a plain, a reversed and a partial run of 256
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c[:7]) + ("-var" if c[7] else ""))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c[:7]) + ("-var" if set(c[7]) - {"n_positions"} else ""))
 def test_block_backward_matches_oracle(case):
     dtype, D, H, L, layer, B, T, sw = case
     _announce(f"block backward {case}")

@@ -75,6 +75,7 @@ RAGGED = [
     ("bf16", 192, 3, 1, 777, 300, 1, 1),
     ("bf16", 192, 3, 1, 777, 300, 2, 129),
     ("bf16", 256, 4, 3, 4099, 300, 2, 300),
+    ("bf16", 128, 2, 1, 1000, 1024, 20, 1000),  # attention grid of 640 blocks: a plain, a reversed and a partial run of 256
 ]
 
 
